@@ -1,0 +1,195 @@
+/* moe_latent.h -- C ABI of the MI355X (gfx950) Stable LatentMoE layer library.
+ *
+ * One forward pass of Kimi K3's Stable LatentMoE layer with MXFP4 routed
+ * experts, split into the five calls below.  The layer is described on the
+ * kimi-k3-mlx README (PipeNetwork/kimi-k3-mlx), Architecture table (MoE,
+ * Stable LatentMoE, Activation and Source-format rows), and the tensor
+ * layouts in the K3 open-artifact audit (llm-atlas), sections 4.3 and 6.
+ *
+ * Conventions shared by every call
+ *  - Every tensor argument is a caller-owned DEVICE pointer, row-major with
+ *    the last dimension contiguous, 16-byte aligned.  bf16 values are passed
+ *    as their uint16_t bit patterns.  Weights are [out_features, in_features].
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only ENQUEUES work on `stream`: no call synchronises the host,
+ *    allocates or frees memory, or keeps state between calls.  The caller
+ *    keeps every buffer alive until the stream has passed the work.
+ *  - `ws` is a caller-owned device workspace of at least
+ *    moe_workspace_bytes(shape, fn, n) bytes; its contents are scratch.
+ *    Calls enqueued on different streams must not share a workspace.
+ *  - Arguments are validated before anything is enqueued: on any error code
+ *    nothing has been enqueued and no output has been touched.
+ *  - Preconditions on device data are documented, not checked (checking would
+ *    need a host synchronisation): expert ids in [0, E); at least top_k
+ *    finite biased scores per token.
+ *  - Asynchronous device faults surface at the caller's next synchronisation.
+ *  - Shape limits of the compiled kernels (else MOE_ENOTSUP): hidden, latent,
+ *    inter and n_shared*shared_inter multiples of 128; n_experts in
+ *    [top_k, 1024]; 1 <= top_k <= 32.
+ */
+#ifndef MOE_LATENT_H
+#define MOE_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* return codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)     /* null required pointer, bad size or enum, misaligned pointer */
+#define MOE_ENOTSUP (-2)    /* shape outside the compiled tiling, or device is not gfx950 */
+#define MOE_EWORKSPACE (-3) /* ws_bytes smaller than moe_workspace_bytes() */
+#define MOE_EHIP (-4)       /* a HIP launch or query failed */
+#define MOE_EINTERNAL (-5)  /* unexpected host-side failure caught at the boundary */
+
+/* operand modes for activations that are not exact bf16 values (the latent z,
+   the expert hidden H, the normalised latent, the shared-expert hidden) */
+#define MOE_OPND_BF16X2 0 /* a = hi + lo, two bf16 MFMAs per product (default) */
+#define MOE_OPND_BF16 1   /* a rounded once to bf16 (faster, less accurate) */
+
+/* mxfp4_grouped_gemm operations */
+#define MOE_OP_GATEUP_SITU 0
+#define MOE_OP_DOWN 1
+
+/* activation dtypes */
+#define MOE_DT_F32 0
+#define MOE_DT_BF16 1
+
+/* moe_workspace_bytes() function selectors */
+#define MOE_FN_ROUTE 0
+#define MOE_FN_PERMUTE 1
+#define MOE_FN_GROUPED_GEMM 2
+#define MOE_FN_COMBINE_NORM_UP 3
+#define MOE_FN_SHARED_FFN 4
+
+typedef struct {
+  int32_t hidden;       /* H: residual width (7168 for K3) */
+  int32_t latent;       /* L: latent width the routed experts run in (3584) */
+  int32_t n_experts;    /* E: routed experts (896) */
+  int32_t top_k;        /* k: experts per token (16) */
+  int32_t inter;        /* I: routed-expert intermediate width (3072) */
+  int32_t n_shared;     /* S: shared experts (2) */
+  int32_t shared_inter; /* Is: intermediate width of one shared expert (3072) */
+  float beta;           /* SiTU-GLU gate saturation (4) */
+  float beta_lin;       /* SiTU-GLU linear-branch saturation (25) */
+  float rms_eps;        /* RMSNorm epsilon on the combined latent (1e-6) */
+  int32_t operand_mode; /* MOE_OPND_BF16X2 or MOE_OPND_BF16 */
+} moe_shape;
+
+int moe_abi_version(void);
+const char *moe_strerror(int code);
+
+/* Workspace bytes needed by call `fn` (MOE_FN_*) for `n` rows: n = T tokens
+   for route/permute/combine/shared, n = P = T*top_k pairs for the grouped
+   GEMM.  Returns 0 for an invalid shape or selector. */
+size_t moe_workspace_bytes(const moe_shape *shape, int fn, int n);
+
+/* Router and latent down projection.
+ * Follows: kimi-k3-mlx README, Architecture table, MoE row (sigmoid router
+ * over 896 experts with the aux-loss-free e_score_correction_bias, top-16)
+ * and Stable LatentMoE row (down_proj 7168 -> 3584, shared by every expert);
+ * K3 open-artifact audit, section 6 (router weight [896, 7168] bf16, bias
+ * [896] fp32).
+ *   x         [T, H]  bf16   layer input
+ *   w_router  [E, H]  bf16
+ *   bias      [E]     fp32   correction bias (selection only)
+ *   w_down    [L, H]  bf16   latent down projection; NULL together with z to skip it
+ * Outputs:
+ *   topk_ids  [T, k]  int32  selected experts, ascending id per token
+ *   topk_w    [T, k]  fp32   sigmoid(logit) of each selected expert / their sum
+ *   z         [T, L]  fp32   x w_down^T (NULL to skip)
+ *   gap       [T]     fp32   k-th minus (k+1)-th largest biased score (NULL to skip;
+ *                            +inf when E == k)
+ * Logits accumulate in fp32; biased score = fp32 sigmoid + fp32 bias; the k
+ * largest win with ties to the lower index; NaN biased scores rank last.
+ * Errors: MOE_EINVAL for T < 1 or a null required pointer. */
+int moe_route(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *w_router,
+              const float *bias, const uint16_t *w_down, int32_t *topk_ids, float *topk_w,
+              float *z, float *gap, void *ws, size_t ws_bytes, void *stream);
+
+/* Token permutation: stable counting sort of the pairs p = t*k + j by expert.
+ * Follows: kimi-k3-mlx README, REAP section, two-bank paragraph (pairs sorted
+ * by expert index give each expert a contiguous slice).
+ *   topk_ids        [T, k]  int32 (ascending per token, each id in [0, E))
+ * Outputs:
+ *   expert_offsets  [E+1]   int32  expert e owns sorted rows offsets[e]..offsets[e+1]
+ *   sorted_pair     [T*k]   int32  pair index at each sorted row (tokens ascend in a slice)
+ *   pair_pos        [T*k]   int32  sorted row of each pair (inverse of sorted_pair)
+ *   active          [E+1]   int32  active[0] = number of experts with pairs,
+ *                                  active[1..] = their ids ascending (NULL to skip)
+ * Deterministic: no result depends on the order of concurrent updates. */
+int moe_permute(const moe_shape *shape, int T, const int32_t *topk_ids, int32_t *expert_offsets,
+                int32_t *sorted_pair, int32_t *pair_pos, int32_t *active, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* MXFP4 grouped expert GEMM over expert-sorted rows.
+ * Follows: K3 open-artifact audit, section 4.3 (w1/w3 weight_packed u8
+ * [3072, 1792] and weight_scale u8 [3072, 112]; w2 packed [3584, 1536],
+ * scale [3584, 96]); kimi-k3-mlx README, Architecture table Source-format row
+ * and Tiers section (e2m1 codes low nibble first, e8m0 scales, group 32),
+ * Activation row and Porting notes item 1 (SiTU-GLU in fp32).
+ * Weight tensors are the checkpoint bytes as-is, stacked over experts:
+ * packed [E, N, K/2] (byte b of a row holds element 2b in its low nibble),
+ * scale [E, N, K/32] (element k of row n is code * 2^(scale[n][k/32]-127)).
+ *   op = MOE_OP_GATEUP_SITU: H[p] = SiTU-GLU(A_p w1_e^T, A_p w3_e^T) for every
+ *        sorted row p of expert e; K = latent, N = inter.
+ *        w_packed/w_scale = w1 (gate), w3_packed/w3_scale = w3 (up).
+ *        A row of sorted row p: A[sorted_pair[p] / top_k] when sorted_pair is
+ *        given (A = z [T, L]), else A[p] (A already permuted, [P, L]).
+ *        C = H [P, inter] fp32.
+ *   op = MOE_OP_DOWN: Y[p] = A[p] w2_e^T; K = inter, N = latent.
+ *        A = H [P, inter] fp32 in sorted order; w3_* must be NULL.
+ *        pair_weight [T*k] fp32 (optional, needs sorted_pair): row p is
+ *        scaled by pair_weight[sorted_pair[p]].  C = Y [P, latent] fp32.
+ *   P              number of sorted rows (T*k)
+ *   expert_offsets [E+1] device int32 from moe_permute
+ *   a_dtype        MOE_DT_F32 (split or rounded per shape->operand_mode) or
+ *                  MOE_DT_BF16 (exact, single MFMA)
+ * Experts with no rows cost nothing and nothing waits on the host: the grid
+ * is sized from P and each workgroup reads its work item on the device.
+ * Errors: MOE_EINVAL for bad op/dtype, P < 1, null required pointers, or
+ * w3 given for MOE_OP_DOWN. */
+int mxfp4_grouped_gemm(const moe_shape *shape, int op, int P, const int32_t *expert_offsets,
+                       const int32_t *sorted_pair, const void *A, int a_dtype,
+                       const uint8_t *w_packed, const uint8_t *w_scale, const uint8_t *w3_packed,
+                       const uint8_t *w3_scale, const float *pair_weight, float *C, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* Weighted combine, RMSNorm on the combined latent, up projection.
+ * Follows: kimi-k3-mlx README, REAP section caveat paragraph (RMSNorm is
+ * applied to the combined expert output before up_proj) and Architecture
+ * table, Stable LatentMoE row (up_proj 3584 -> 7168).
+ *   Y        [T*k, L] fp32  expert outputs in sorted order (from MOE_OP_DOWN)
+ *   pair_pos [T*k]    int32 sorted row of each pair (from moe_permute)
+ *   topk_w   [T, k]   fp32  routing weights, or NULL when already folded into Y
+ *   gamma    [L]      bf16  RMSNorm weight
+ *   w_up     [H, L]   bf16
+ *   out      [T, H]   fp32  written (accumulate = 0) or added to (accumulate = 1)
+ * y_t = sum_j w_{t,j} Y[pair_pos[t*k+j]] in fixed j order;
+ * out_t (+)= (y_t / sqrt(mean(y_t^2) + rms_eps) * gamma) w_up^T. */
+int moe_combine_norm_up(const moe_shape *shape, int T, const float *Y, const int32_t *pair_pos,
+                        const float *topk_w, const uint16_t *gamma, const uint16_t *w_up,
+                        float *out, int accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/* Shared experts on the residual input, run as one SiTU-GLU of width
+ * S*Is (gate and up rows concatenated over experts, down columns likewise).
+ * Follows: kimi-k3-mlx README, Architecture table MoE row (2 shared experts on
+ * every token) and Porting notes item 3 (shared experts do not use the latent).
+ *   x       [T, H]      bf16
+ *   w_gate  [S*Is, H]   bf16  (expert i owns rows i*Is..(i+1)*Is)
+ *   w_up    [S*Is, H]   bf16
+ *   w_down  [H, S*Is]   bf16  (expert i owns columns i*Is..(i+1)*Is)
+ *   out     [T, H]      fp32  written (accumulate = 0) or added to (accumulate = 1) */
+int shared_expert_ffn(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *w_gate,
+                      const uint16_t *w_up, const uint16_t *w_down, float *out, int accumulate,
+                      void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LATENT_H */

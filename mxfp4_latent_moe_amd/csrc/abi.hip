@@ -1,0 +1,380 @@
+// C ABI entry points: argument validation, workspace layout, launches.
+// Nothing here allocates, frees or synchronises; every call only enqueues.
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.h"
+#include "moe_latent.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const moe_shape *s) {
+  if (s == nullptr) return MOE_EINVAL;
+  if (s->hidden <= 0 || s->latent <= 0 || s->n_experts <= 0 || s->top_k <= 0 || s->inter <= 0 ||
+      s->n_shared < 0 || s->shared_inter < 0)
+    return MOE_EINVAL;
+  if (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16) return MOE_EINVAL;
+  if (!(s->beta > 0.f) || !(s->beta_lin > 0.f) || !(s->rms_eps >= 0.f)) return MOE_EINVAL;
+  if (s->top_k > s->n_experts) return MOE_EINVAL;
+  if (s->hidden % 128 || s->latent % 128 || s->inter % 128 || (s->n_shared * s->shared_inter) % 128)
+    return MOE_ENOTSUP;
+  if (s->n_experts > 1024 || s->top_k > 32) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+// gfx950 check, cached per device
+std::mutex g_arch_mu;
+int g_arch_ok[64];  // 0 unknown, 1 ok, -1 not gfx950
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= 64) return MOE_ENOTSUP;
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_EHIP;
+    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return g_arch_ok[dev] == 1 ? MOE_OK : MOE_ENOTSUP;
+}
+
+int afmt_of(const moe_shape *s) {
+  return s->operand_mode == MOE_OPND_BF16 ? A_F32_ROUND : A_F32_SPLIT;
+}
+
+// ---- workspace layouts (offsets from ws)
+struct RouteWs {
+  size_t logits, partial, total;
+  GemmPlan pr, pd;
+};
+RouteWs route_ws(const moe_shape *s, int T) {
+  RouteWs w{};
+  w.pr = plan_dense(T, s->n_experts, s->hidden, false);
+  w.pd = plan_dense(T, s->latent, s->hidden, false);
+  w.logits = 0;
+  w.partial = align_up((size_t)T * s->n_experts * sizeof(float));
+  w.total = w.partial + align_up(std::max(w.pr.partial_bytes, w.pd.partial_bytes));
+  return w;
+}
+
+size_t permute_ws(const moe_shape *s, int T) {
+  return align_up((size_t)permute_blocks(T) * s->n_experts * sizeof(int32_t));
+}
+
+struct GroupedWs {
+  size_t chunks, count, total;
+  GemmPlan plan;
+};
+GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
+  GroupedWs w{};
+  w.plan = gateup ? plan_grouped(P, s->n_experts, s->inter, s->latent, true)
+                  : plan_grouped(P, s->n_experts, s->latent, s->inter, false);
+  w.chunks = 0;
+  w.count = align_up((size_t)w.plan.max_chunks * 16);
+  w.total = w.count + ALIGN;
+  return w;
+}
+
+struct CombineWs {
+  size_t yn, partial, total;
+  GemmPlan pu;
+};
+CombineWs combine_ws(const moe_shape *s, int T) {
+  CombineWs w{};
+  w.pu = plan_dense(T, s->hidden, s->latent, false);
+  w.yn = 0;
+  w.partial = align_up((size_t)T * s->latent * sizeof(float));
+  w.total = w.partial + align_up(w.pu.partial_bytes);
+  return w;
+}
+
+struct SharedWs {
+  size_t hs, partial, total;
+  GemmPlan pgu, pdn;
+};
+SharedWs shared_ws(const moe_shape *s, int T) {
+  SharedWs w{};
+  const int NS = s->n_shared * s->shared_inter;
+  w.pgu = plan_dense(T, NS, s->hidden, true);
+  w.pdn = plan_dense(T, s->hidden, NS, false);
+  w.hs = 0;
+  w.partial = align_up((size_t)T * NS * sizeof(float));
+  w.total = w.partial + align_up(std::max(w.pgu.partial_bytes, w.pdn.partial_bytes));
+  return w;
+}
+
+char *wsp(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+GemmArgs dense_args(const GemmPlan &pl, const void *A, long long lda, const void *W0, const void *W1,
+                    int N, int K, float *C, long long ldc, int accumulate, int rows, float *partial,
+                    const moe_shape *s) {
+  GemmArgs a{};
+  a.A = A;
+  a.lda = lda;
+  a.a_map = nullptr;
+  a.a_div = 1;
+  a.W0 = W0;
+  a.W1 = W1;
+  a.w_estride = 0;
+  a.s_estride = 0;
+  a.N = N;
+  a.K = K;
+  a.C = C;
+  a.ldc = ldc;
+  a.accumulate = accumulate;
+  a.chunks = nullptr;
+  a.chunk_count = nullptr;
+  a.dense_rows = rows;
+  a.n_blocks = pl.n_blocks;
+  a.splits = pl.splits;
+  a.grid_logical = (int)pl.grid_logical;
+  a.partial = partial;
+  a.partial_rows = rows;
+  a.beta = s->beta;
+  a.beta_lin = s->beta_lin;
+  return a;
+}
+
+// dense GEMM plus, for split K, the finalize pass
+hipError_t run_dense(const GemmPlan &pl, int afmt, bool pair, const GemmArgs &a, hipStream_t st) {
+  hipError_t e = launch_gemm(pl, W_BF16, afmt, pair, a, st);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  FinalizeArgs f{};
+  f.partial = a.partial;
+  f.splits = pl.splits;
+  f.rows = a.dense_rows;
+  f.N = a.N;
+  f.pair = pair ? 1 : 0;
+  f.C = a.C;
+  f.ldc = a.ldc;
+  f.accumulate = a.accumulate;
+  f.beta = a.beta;
+  f.beta_lin = a.beta_lin;
+  return launch_finalize(f, st);
+}
+
+template <typename F>
+int guarded(F &&f) {
+  try {
+    return f();
+  } catch (...) {
+    return MOE_EINTERNAL;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer, size, enum or alignment)";
+    case MOE_ENOTSUP: return "unsupported shape or device (needs gfx950 and the compiled tiling)";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error";
+    case MOE_EINTERNAL: return "internal error";
+    default: return "unknown error code";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape *s, int fn, int n) {
+  if (check_shape(s) != MOE_OK || n <= 0) return 0;
+  switch (fn) {
+    case MOE_FN_ROUTE: return route_ws(s, n).total;
+    case MOE_FN_PERMUTE: return permute_ws(s, n);
+    case MOE_FN_GROUPED_GEMM: {
+      const size_t a = grouped_ws(s, n, true).total, b = grouped_ws(s, n, false).total;
+      return a > b ? a : b;
+    }
+    case MOE_FN_COMBINE_NORM_UP: return combine_ws(s, n).total;
+    case MOE_FN_SHARED_FFN:
+      if (s->n_shared * s->shared_inter == 0) return ALIGN;
+      return shared_ws(s, n).total;
+    default: return 0;
+  }
+}
+
+int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_router,
+              const float *bias, const uint16_t *w_down, int32_t *topk_ids, float *topk_w, float *z,
+              float *gap, void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (T <= 0 || !x || !w_router || !bias || !topk_ids || !topk_w || !ws) return MOE_EINVAL;
+    if ((w_down == nullptr) != (z == nullptr)) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || (w_down && !aligned16(w_down)) ||
+        (z && !aligned16(z)) || !aligned16(ws))
+      return MOE_EINVAL;
+    const RouteWs w = route_ws(s, T);
+    if (ws_bytes < w.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *logits = reinterpret_cast<float *>(wsp(ws, w.logits));
+    float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
+    GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
+                            s->n_experts, 0, T, partial, s);
+    if (run_dense(w.pr, A_BF16, false, a, st) != hipSuccess) return MOE_EHIP;
+    if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) !=
+        hipSuccess)
+      return MOE_EHIP;
+    if (z) {
+      GemmArgs d = dense_args(w.pd, x, s->hidden, w_down, nullptr, s->latent, s->hidden, z,
+                              s->latent, 0, T, partial, s);
+      if (run_dense(w.pd, A_BF16, false, d, st) != hipSuccess) return MOE_EHIP;
+    }
+    return MOE_OK;
+  });
+}
+
+int moe_permute(const moe_shape *s, int T, const int32_t *topk_ids, int32_t *expert_offsets,
+                int32_t *sorted_pair, int32_t *pair_pos, int32_t *active, void *ws,
+                size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (T <= 0 || !topk_ids || !expert_offsets || !sorted_pair || !pair_pos || !ws)
+      return MOE_EINVAL;
+    if ((long long)T * s->top_k > 0x7fffffffLL) return MOE_EINVAL;
+    if (ws_bytes < permute_ws(s, T)) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (launch_permute(topk_ids, T, s->top_k, s->n_experts, static_cast<int32_t *>(ws),
+                       expert_offsets, sorted_pair, pair_pos, active, st) != hipSuccess)
+      return MOE_EHIP;
+    return MOE_OK;
+  });
+}
+
+int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_offsets,
+                       const int32_t *sorted_pair, const void *A, int a_dtype,
+                       const uint8_t *w_packed, const uint8_t *w_scale, const uint8_t *w3_packed,
+                       const uint8_t *w3_scale, const float *pair_weight, float *C, void *ws,
+                       size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (op != MOE_OP_GATEUP_SITU && op != MOE_OP_DOWN) return MOE_EINVAL;
+    if (a_dtype != MOE_DT_F32 && a_dtype != MOE_DT_BF16) return MOE_EINVAL;
+    if (P <= 0 || !expert_offsets || !A || !w_packed || !w_scale || !C || !ws) return MOE_EINVAL;
+    const bool gateup = op == MOE_OP_GATEUP_SITU;
+    if (gateup && (!w3_packed || !w3_scale)) return MOE_EINVAL;
+    if (!gateup && (w3_packed || w3_scale)) return MOE_EINVAL;
+    if (gateup && pair_weight) return MOE_EINVAL;
+    if (pair_weight && !sorted_pair) return MOE_EINVAL;
+    if (!aligned16(A) || !aligned16(w_packed) || !aligned16(C) || !aligned16(ws) ||
+        (w3_packed && !aligned16(w3_packed)) || (reinterpret_cast<uintptr_t>(w_scale) & 3u) ||
+        (w3_scale && (reinterpret_cast<uintptr_t>(w3_scale) & 3u)))
+      return MOE_EINVAL;
+    const GroupedWs w = grouped_ws(s, P, gateup);
+    if (ws_bytes < w.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t *chunks = reinterpret_cast<int32_t *>(wsp(ws, w.chunks));
+    int32_t *count = reinterpret_cast<int32_t *>(wsp(ws, w.count));
+    if (launch_plan_chunks(expert_offsets, s->n_experts, w.plan.chunk_rows, chunks, count, st) !=
+        hipSuccess)
+      return MOE_EHIP;
+    const int N = gateup ? s->inter : s->latent;
+    const int K = gateup ? s->latent : s->inter;
+    GemmArgs a{};
+    a.A = A;
+    a.lda = K;
+    a.a_map = gateup ? sorted_pair : nullptr;
+    a.a_div = s->top_k;
+    a.W0 = w_packed;
+    a.W1 = w3_packed;
+    a.S0 = w_scale;
+    a.S1 = w3_scale;
+    a.w_estride = (long long)N * (K / 2);
+    a.s_estride = (long long)N * (K / 32);
+    a.N = N;
+    a.K = K;
+    a.C = C;
+    a.ldc = N;
+    a.accumulate = 0;
+    a.rscale = pair_weight;
+    a.rscale_map = pair_weight ? sorted_pair : nullptr;
+    a.chunks = chunks;
+    a.chunk_count = count;
+    a.dense_rows = 0;
+    a.n_blocks = w.plan.n_blocks;
+    a.splits = 1;
+    a.grid_logical = (int)w.plan.grid_logical;
+    a.partial = nullptr;
+    a.partial_rows = 0;
+    a.beta = s->beta;
+    a.beta_lin = s->beta_lin;
+    const int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
+    if (launch_gemm(w.plan, W_MXFP4, afmt, gateup, a, st) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  });
+}
+
+int moe_combine_norm_up(const moe_shape *s, int T, const float *Y, const int32_t *pair_pos,
+                        const float *topk_w, const uint16_t *gamma, const uint16_t *w_up,
+                        float *out, int accumulate, void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (T <= 0 || !Y || !pair_pos || !gamma || !w_up || !out || !ws) return MOE_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
+    if (!aligned16(Y) || !aligned16(w_up) || !aligned16(out) || !aligned16(ws)) return MOE_EINVAL;
+    const CombineWs w = combine_ws(s, T);
+    if (ws_bytes < w.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *yn = reinterpret_cast<float *>(wsp(ws, w.yn));
+    if (launch_combine_norm(Y, pair_pos, topk_w, gamma, T, s->top_k, s->latent, s->rms_eps, yn,
+                            st) != hipSuccess)
+      return MOE_EHIP;
+    GemmArgs a = dense_args(w.pu, yn, s->latent, w_up, nullptr, s->hidden, s->latent, out,
+                            s->hidden, accumulate, T, reinterpret_cast<float *>(wsp(ws, w.partial)),
+                            s);
+    if (run_dense(w.pu, afmt_of(s), false, a, st) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  });
+}
+
+int shared_expert_ffn(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_gate,
+                      const uint16_t *w_up, const uint16_t *w_down, float *out, int accumulate,
+                      void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (T <= 0 || !x || !out || !ws) return MOE_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
+    const int NS = s->n_shared * s->shared_inter;
+    if (NS == 0) return MOE_EINVAL;
+    if (!w_gate || !w_up || !w_down) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned16(out) || !aligned16(ws))
+      return MOE_EINVAL;
+    const SharedWs w = shared_ws(s, T);
+    if (ws_bytes < w.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *hs = reinterpret_cast<float *>(wsp(ws, w.hs));
+    float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
+    GemmArgs g = dense_args(w.pgu, x, s->hidden, w_gate, w_up, NS, s->hidden, hs, NS, 0, T, partial,
+                            s);
+    if (run_dense(w.pgu, A_BF16, true, g, st) != hipSuccess) return MOE_EHIP;
+    GemmArgs d = dense_args(w.pdn, hs, NS, w_down, nullptr, s->hidden, NS, out, s->hidden,
+                            accumulate, T, partial, s);
+    if (run_dense(w.pdn, afmt_of(s), false, d, st) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  });
+}
+
+}  // extern "C"

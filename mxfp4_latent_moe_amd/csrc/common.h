@@ -1,0 +1,55 @@
+// Shared device helpers for the gfx950 kernels: vector types, MFMA, bf16
+// splitting, MXFP4 nibble conversion, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define MOE_DEV __device__ __forceinline__
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
+// Lane l holds A row (l % 16), B column (l % 16), each with 8 consecutive K
+// values of K-block (l / 16); D column (l % 16), rows 4*(l/16) .. +3.
+MOE_DEV f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+MOE_DEV __bf16 to_bf16(float x) { return (__bf16)x; }
+MOE_DEV float from_bf16(__bf16 x) { return (float)x; }
+
+// a = hi + lo with hi = bf16(a) and lo = bf16(a - hi); a - hi is exact in fp32.
+MOE_DEV void split_bf16(float a, __bf16 &hi, __bf16 &lo) {
+  hi = to_bf16(a);
+  lo = to_bf16(a - from_bf16(hi));
+}
+
+// Eight e2m1 codes (one dword, element 2b in the low nibble of byte b) times
+// 2^(e-127) as eight bf16 values in element order.  The scale argument is the
+// float whose bit pattern is e << 23, i.e. exactly 2^(e-127) for e in 1..254.
+MOE_DEV bf16x8_t fp4x8_to_bf16(uint32_t q, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+MOE_DEV float e8m0_to_float(uint32_t e) { return __uint_as_float(e << 23); }
+
+// SiTU-GLU in fp32: beta*tanh(g/beta)*sigmoid(g) * beta_lin*tanh(u/beta_lin).
+MOE_DEV float situ_glu(float g, float u, float beta, float beta_lin) {
+  float sg = 1.0f / (1.0f + expf(-g));
+  return beta * tanhf(g / beta) * sg * (beta_lin * tanhf(u / beta_lin));
+}
+
+MOE_DEV int lane_id() { return threadIdx.x & 63; }

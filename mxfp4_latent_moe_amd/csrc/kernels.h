@@ -1,0 +1,85 @@
+// Kernel argument blocks and host-side launch helpers shared by the HIP
+// sources and the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// weight formats, activation formats
+enum { W_BF16 = 0, W_MXFP4 = 1 };
+enum { A_BF16 = 0, A_F32_SPLIT = 1, A_F32_ROUND = 2 };
+
+// Weight-stationary GEMM: C[row, n] (+)= sum_k A[row, k] * W[n, k] over a
+// list of row chunks, optionally with two weight matrices combined by
+// SiTU-GLU.  Work item = (row chunk, block of weight rows, K split).
+struct GemmArgs {
+  const void *A;          // activations [rows, K], bf16 or fp32
+  long long lda;          // elements per activation row
+  const int32_t *a_map;   // chunk row p reads A row a_map[p] / a_div (NULL: row p)
+  int a_div;
+  const void *W0, *W1;    // weights [E][N][K] bf16 or packed [E][N][K/2]; W1 for SiTU pairs
+  const uint8_t *S0, *S1; // e8m0 scales [E][N][K/32] (MXFP4)
+  long long w_estride;    // per-expert stride of W (elements for bf16, bytes for packed)
+  long long s_estride;    // per-expert stride of S in bytes
+  int N, K;
+  float *C;
+  long long ldc;
+  int accumulate;
+  const float *rscale;    // optional row scale rscale[rscale_map[row]]
+  const int32_t *rscale_map;
+  const int32_t *chunks;  // grouped: int4 {expert, row0, nrows, 0} per chunk (NULL: dense)
+  const int32_t *chunk_count;
+  int dense_rows;         // dense: number of rows, chunked by the tile height
+  int n_blocks, splits, grid_logical;
+  float *partial;         // split-K partial sums [splits][partial_rows][ncols]
+  int partial_rows;
+  float beta, beta_lin;
+};
+
+struct FinalizeArgs {
+  const float *partial;
+  int splits, rows, N;
+  int pair;               // partial holds [G | U] (2N columns) to combine by SiTU-GLU
+  float *C;
+  long long ldc;
+  int accumulate;
+  float beta, beta_lin;
+};
+
+// kernel variant selection (host side)
+struct GemmPlan {
+  int nt;        // 16-token tiles per chunk (1 or 8)
+  int mt;        // 16-row weight tiles per wave and matrix
+  int chunk_rows;
+  int n_blocks;
+  int splits;
+  int max_chunks;
+  long long grid_logical;
+  size_t partial_bytes;
+};
+
+GemmPlan plan_dense(int rows, int N, int K, bool pair);
+GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
+
+hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
+                       hipStream_t st);
+hipError_t launch_finalize(const FinalizeArgs &f, hipStream_t st);
+hipError_t launch_plan_chunks(const int32_t *offsets, int E, int chunk_rows, int32_t *chunks,
+                              int32_t *count, hipStream_t st);
+
+hipError_t launch_topk(const float *logits, const float *bias, int T, int E, int k, int32_t *ids,
+                       float *w, float *gap, hipStream_t st);
+
+// permutation: workspace holds blk_counts [nblk][E] int32
+int permute_blocks(int T);
+hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *blk, int32_t *offsets,
+                          int32_t *sorted_pair, int32_t *pair_pos, int32_t *active,
+                          hipStream_t st);
+
+hipError_t launch_combine_norm(const float *Y, const int32_t *pair_pos, const float *w,
+                               const uint16_t *gamma, int T, int k, int L, float eps, float *yn,
+                               hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+"""Torch-facing wrappers of the five C-ABI calls, and a layer object that
+chains them on one stream.  Argument marshalling only: tensors are passed as
+device pointers, the stream as its HIP handle; all compute runs in the HIP
+library."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_DT_BF16, MOE_DT_F32, MOE_FN_COMBINE_NORM_UP, MOE_FN_GROUPED_GEMM,
+                   MOE_FN_PERMUTE, MOE_FN_ROUTE, MOE_FN_SHARED_FFN, MOE_OP_DOWN,
+                   MOE_OP_GATEUP_SITU, MoeShape, check, load)
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _s(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def shape_of(ls, operand_mode: int = _lib.MOE_OPND_BF16X2, beta=4.0, beta_lin=25.0, rms_eps=1e-6) -> MoeShape:
+    """MoeShape from any object with the LayerShape fields."""
+    return _lib.make_shape(ls.hidden, ls.latent, ls.n_experts, ls.top_k, ls.inter, ls.n_shared,
+                           ls.shared_inter, beta, beta_lin, rms_eps, operand_mode)
+
+
+def workspace_bytes(shape: MoeShape, fn: int, n: int) -> int:
+    return int(load().moe_workspace_bytes(shape, fn, n))
+
+
+def route(shape, x, w_router, bias, w_down, topk_ids, topk_w, z, gap, ws, stream=None):
+    check("moe_route", load().moe_route(shape, x.shape[0], _p(x), _p(w_router), _p(bias), _p(w_down),
+                                        _p(topk_ids), _p(topk_w), _p(z), _p(gap), _p(ws), ws.numel(),
+                                        _s(stream)))
+
+
+def permute(shape, topk_ids, offsets, sorted_pair, pair_pos, active, ws, stream=None):
+    check("moe_permute", load().moe_permute(shape, topk_ids.shape[0], _p(topk_ids), _p(offsets),
+                                            _p(sorted_pair), _p(pair_pos), _p(active), _p(ws),
+                                            ws.numel(), _s(stream)))
+
+
+def grouped_gemm(shape, op, P, offsets, sorted_pair, A, w_packed, w_scale, w3_packed, w3_scale,
+                 pair_weight, C, ws, stream=None):
+    a_dtype = MOE_DT_BF16 if A.dtype in (torch.bfloat16, torch.int16, torch.uint16) else MOE_DT_F32
+    check("mxfp4_grouped_gemm",
+          load().mxfp4_grouped_gemm(shape, op, P, _p(offsets), _p(sorted_pair), _p(A), a_dtype,
+                                    _p(w_packed), _p(w_scale), _p(w3_packed), _p(w3_scale),
+                                    _p(pair_weight), _p(C), _p(ws), ws.numel(), _s(stream)))
+
+
+def combine_norm_up(shape, T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, ws, stream=None):
+    check("moe_combine_norm_up",
+          load().moe_combine_norm_up(shape, T, _p(Y), _p(pair_pos), _p(topk_w), _p(gamma), _p(w_up),
+                                     _p(out), int(accumulate), _p(ws), ws.numel(), _s(stream)))
+
+
+def shared_ffn(shape, x, w_gate, w_up, w_down, out, accumulate, ws, stream=None):
+    check("shared_expert_ffn",
+          load().shared_expert_ffn(shape, x.shape[0], _p(x), _p(w_gate), _p(w_up), _p(w_down), _p(out),
+                                   int(accumulate), _p(ws), ws.numel(), _s(stream)))
+
+
+WEIGHT_KEYS = ("w_router", "bias", "w_down", "w_up", "gamma", "sh_gate", "sh_up", "sh_down",
+               "w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "w2_scale")
+
+
+class LatentMoE:
+    """One Stable LatentMoE layer on the GPU: weights resident, buffers per token count.
+
+    forward(x) enqueues on the current stream, in order: moe_route,
+    moe_permute, mxfp4_grouped_gemm (gate/up + SiTU-GLU), mxfp4_grouped_gemm
+    (down), moe_combine_norm_up (writes out), shared_expert_ffn (adds to out).
+    """
+
+    def __init__(self, shape: MoeShape, weights: dict, device="cuda"):
+        missing = [k for k in WEIGHT_KEYS if k not in weights]
+        if missing:
+            raise ValueError(f"missing weights: {missing}")
+        self.shape = shape
+        self.w = weights
+        self.device = torch.device(device)
+        self._bufs: dict = {}
+
+    def buffers(self, T: int) -> dict:
+        if T in self._bufs:
+            return self._bufs[T]
+        s, dev = self.shape, self.device
+        P = T * s.top_k
+        ws = max(workspace_bytes(s, fn, P if fn == MOE_FN_GROUPED_GEMM else T)
+                 for fn in (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP,
+                            MOE_FN_SHARED_FFN))
+        i32, f32 = torch.int32, torch.float32
+        b = {
+            "topk_ids": torch.empty((T, s.top_k), dtype=i32, device=dev),
+            "topk_w": torch.empty((T, s.top_k), dtype=f32, device=dev),
+            "z": torch.empty((T, s.latent), dtype=f32, device=dev),
+            "gap": torch.empty((T,), dtype=f32, device=dev),
+            "offsets": torch.empty((s.n_experts + 1,), dtype=i32, device=dev),
+            "sorted_pair": torch.empty((P,), dtype=i32, device=dev),
+            "pair_pos": torch.empty((P,), dtype=i32, device=dev),
+            "active": torch.empty((s.n_experts + 1,), dtype=i32, device=dev),
+            "H": torch.empty((P, s.inter), dtype=f32, device=dev),
+            "Y": torch.empty((P, s.latent), dtype=f32, device=dev),
+            "out": torch.empty((T, s.hidden), dtype=f32, device=dev),
+            "ws": torch.empty((ws,), dtype=torch.uint8, device=dev),
+        }
+        self._bufs[T] = b
+        return b
+
+    def forward(self, x: torch.Tensor, stream=None) -> dict:
+        s, w = self.shape, self.w
+        T = x.shape[0]
+        P = T * s.top_k
+        b = self.buffers(T)
+        ws = b["ws"]
+        route(s, x, w["w_router"], w["bias"], w["w_down"], b["topk_ids"], b["topk_w"], b["z"], b["gap"],
+              ws, stream)
+        permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"], b["active"], ws, stream)
+        grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"], w["w1_packed"],
+                     w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"], ws, stream)
+        grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
+                     w["w2_scale"], None, None, None, b["Y"], ws, stream)
+        combine_norm_up(s, T, b["Y"], b["pair_pos"], b["topk_w"], w["gamma"], w["w_up"], b["out"], 0, ws,
+                        stream)
+        if s.n_shared * s.shared_inter > 0:
+            shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 1, ws, stream)
+        return b

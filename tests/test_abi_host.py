@@ -1,0 +1,148 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls).
+
+The library loads, exports every function include/moe_latent.h declares, and
+rejects bad arguments with the documented codes before touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import synth
+from mxfp4_latent_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_latent.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails before any device work
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.load()
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for fn in ("moe_route", "moe_permute", "mxfp4_grouped_gemm", "moe_combine_norm_up",
+               "shared_expert_ffn", "moe_workspace_bytes", "moe_strerror", "moe_abi_version"):
+        assert fn in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for fn in _declared():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+    assert lib.moe_abi_version() == 1
+    assert b"workspace" in lib.moe_strerror(_lib.MOE_EWORKSPACE)
+
+
+def _shape(**kw):
+    sh = synth.K3_SHAPE
+    s = _lib.make_shape(sh.hidden, sh.latent, sh.n_experts, sh.top_k, sh.inter, sh.n_shared, sh.shared_inter)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_workspace_bytes(lib):
+    s = _shape()
+    for fn in range(5):
+        assert lib.moe_workspace_bytes(s, fn, 16) > 0
+    assert lib.moe_workspace_bytes(s, 7, 16) == 0
+    assert lib.moe_workspace_bytes(s, 0, 0) == 0
+    bad = _shape(latent=100)
+    assert lib.moe_workspace_bytes(bad, 0, 16) == 0
+    # grows with the token count
+    assert lib.moe_workspace_bytes(s, _lib.MOE_FN_ROUTE, 4096) > lib.moe_workspace_bytes(s, _lib.MOE_FN_ROUTE, 16)
+
+
+def test_route_validation(lib):
+    s = _shape()
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_ROUTE, 16)
+    args = [16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    bad_T = list(args)
+    bad_T[0] = 0
+    assert lib.moe_route(s, *bad_T) == _lib.MOE_EINVAL
+    nul = list(args)
+    nul[1] = None
+    assert lib.moe_route(s, *nul) == _lib.MOE_EINVAL
+    half = list(args)
+    half[4] = None  # w_down without z is an error (and the reverse)
+    assert lib.moe_route(s, *half) == _lib.MOE_EINVAL
+    mis = list(args)
+    mis[1] = FAKE + 2
+    assert lib.moe_route(s, *mis) == _lib.MOE_EINVAL
+    small = list(args)
+    small[10] = ws - 1
+    assert lib.moe_route(s, *small) == _lib.MOE_EWORKSPACE
+    assert lib.moe_route(None, *args) == _lib.MOE_EINVAL
+    assert lib.moe_route(_shape(operand_mode=7), *args) == _lib.MOE_EINVAL
+    assert lib.moe_route(_shape(top_k=900), *args) == _lib.MOE_EINVAL
+    assert lib.moe_route(_shape(n_experts=2048, top_k=16), *args) == _lib.MOE_ENOTSUP
+    assert lib.moe_route(_shape(hidden=7000), *args) == _lib.MOE_ENOTSUP
+    assert lib.moe_route(_shape(top_k=33), *args) == _lib.MOE_ENOTSUP
+
+
+def test_permute_validation(lib):
+    s = _shape()
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_PERMUTE, 16)
+    assert lib.moe_permute(s, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == _lib.MOE_EINVAL
+    assert lib.moe_permute(s, 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == _lib.MOE_EINVAL
+    assert lib.moe_permute(s, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == _lib.MOE_EWORKSPACE
+
+
+def test_grouped_gemm_validation(lib):
+    s = _shape()
+    P = 256
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_GROUPED_GEMM, P)
+    G, D = _lib.MOE_OP_GATEUP_SITU, _lib.MOE_OP_DOWN
+    f32 = _lib.MOE_DT_F32
+
+    def call(op=G, P_=P, off=FAKE, sp=FAKE, A=FAKE, dt=f32, wp=FAKE, wsc=FAKE, w3p=FAKE, w3s=FAKE, pw=None,
+             C=FAKE, wsb=ws):
+        return lib.mxfp4_grouped_gemm(s, op, P_, off, sp, A, dt, wp, wsc, w3p, w3s, pw, C, FAKE, wsb, None)
+
+    assert call(op=5) == _lib.MOE_EINVAL
+    assert call(dt=9) == _lib.MOE_EINVAL
+    assert call(P_=0) == _lib.MOE_EINVAL
+    assert call(w3p=None) == _lib.MOE_EINVAL           # gate/up needs w3
+    assert call(op=D) == _lib.MOE_EINVAL               # down must not get w3
+    assert call(op=D, w3p=None, w3s=None, pw=FAKE, sp=None) == _lib.MOE_EINVAL  # weights need sorted_pair
+    assert call(pw=FAKE) == _lib.MOE_EINVAL            # no pair weights on gate/up
+    assert call(A=FAKE + 4) == _lib.MOE_EINVAL
+    assert call(wsc=FAKE + 1) == _lib.MOE_EINVAL
+    assert call(wsb=ws - 1) == _lib.MOE_EWORKSPACE
+    assert call(op=D, w3p=None, w3s=None, wsb=ws - 1) == _lib.MOE_EWORKSPACE
+
+
+def test_combine_and_shared_validation(lib):
+    s = _shape()
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP, 16)
+    assert lib.moe_combine_norm_up(s, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, ws, None) == _lib.MOE_EINVAL
+    assert lib.moe_combine_norm_up(s, 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws, None) == _lib.MOE_EINVAL
+    assert lib.moe_combine_norm_up(s, 16, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, ws - 1, None) == _lib.MOE_EWORKSPACE
+    ws2 = lib.moe_workspace_bytes(s, _lib.MOE_FN_SHARED_FFN, 16)
+    assert lib.shared_expert_ffn(s, 16, FAKE, FAKE, FAKE, None, FAKE, 0, FAKE, ws2, None) == _lib.MOE_EINVAL
+    assert lib.shared_expert_ffn(s, -1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws2, None) == _lib.MOE_EINVAL
+    assert lib.shared_expert_ffn(s, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws2 - 1, None) == _lib.MOE_EWORKSPACE
+    none = _shape(n_shared=0)
+    assert lib.shared_expert_ffn(none, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws2, None) == _lib.MOE_EINVAL
+
+
+def test_no_cpu_fallback_when_library_missing(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load(str(tmp_path / "missing.so"))
