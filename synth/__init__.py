@@ -10,6 +10,7 @@ from .inputs import (  # noqa: F401
     Workload,
     WORKLOADS,
     K3_SHAPE,
+    TINY_SHAPE,
     workload,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
