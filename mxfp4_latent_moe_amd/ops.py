@@ -111,21 +111,39 @@ class LatentMoE:
         self._bufs[T] = b
         return b
 
-    def forward(self, x: torch.Tensor, stream=None) -> dict:
+    def forward(self, x: torch.Tensor, stream=None, marks: list | None = None) -> dict:
+        """Enqueue the layer on `stream` (default: current stream).  With `marks`
+        given, a timing event is recorded on the stream before the first call
+        and after each call, appended as (name, event) pairs."""
         s, w = self.shape, self.w
         T = x.shape[0]
         P = T * s.top_k
         b = self.buffers(T)
         ws = b["ws"]
+        st = torch.cuda.current_stream() if stream is None else stream
+
+        def mark(name):
+            if marks is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(st)
+                marks.append((name, ev))
+
+        mark("start")
         route(s, x, w["w_router"], w["bias"], w["w_down"], b["topk_ids"], b["topk_w"], b["z"], b["gap"],
-              ws, stream)
-        permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"], b["active"], ws, stream)
+              ws, st)
+        mark("moe_route")
+        permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"], b["active"], ws, st)
+        mark("moe_permute")
         grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"], w["w1_packed"],
-                     w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"], ws, stream)
+                     w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"], ws, st)
+        mark("grouped_gemm_gateup")
         grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
-                     w["w2_scale"], None, None, None, b["Y"], ws, stream)
+                     w["w2_scale"], None, None, None, b["Y"], ws, st)
+        mark("grouped_gemm_down")
         combine_norm_up(s, T, b["Y"], b["pair_pos"], b["topk_w"], w["gamma"], w["w_up"], b["out"], 0, ws,
-                        stream)
+                        st)
+        mark("moe_combine_norm_up")
         if s.n_shared * s.shared_inter > 0:
-            shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 1, ws, stream)
+            shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 1, ws, st)
+            mark("shared_expert_ffn")
         return b
