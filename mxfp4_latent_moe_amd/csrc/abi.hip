@@ -71,7 +71,7 @@ size_t permute_ws(const moe_shape *s, int T) {
 }
 
 struct GroupedWs {
-  size_t chunks, count, total;
+  size_t chunks, count, partial, total;
   GemmPlan plan;
 };
 GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
@@ -80,7 +80,8 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
                   : plan_grouped(P, s->n_experts, s->latent, s->inter, false);
   w.chunks = 0;
   w.count = align_up((size_t)w.plan.max_chunks * 16);
-  w.total = w.count + ALIGN;
+  w.partial = w.count + ALIGN;
+  w.total = w.partial + align_up(w.plan.partial_bytes);
   return w;
 }
 
@@ -157,6 +158,8 @@ hipError_t run_dense(const GemmPlan &pl, int afmt, bool pair, const GemmArgs &a,
   f.C = a.C;
   f.ldc = a.ldc;
   f.accumulate = a.accumulate;
+  f.rscale = nullptr;
+  f.rscale_map = nullptr;
   f.beta = a.beta;
   f.beta_lin = a.beta_lin;
   return launch_finalize(f, st);
@@ -310,14 +313,30 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     a.chunk_count = count;
     a.dense_rows = 0;
     a.n_blocks = w.plan.n_blocks;
-    a.splits = 1;
+    a.splits = w.plan.splits;
     a.grid_logical = (int)w.plan.grid_logical;
-    a.partial = nullptr;
-    a.partial_rows = 0;
+    a.partial = reinterpret_cast<float *>(wsp(ws, w.partial));
+    a.partial_rows = P;
     a.beta = s->beta;
     a.beta_lin = s->beta_lin;
     const int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
     if (launch_gemm(w.plan, W_MXFP4, afmt, gateup, a, st) != hipSuccess) return MOE_EHIP;
+    if (w.plan.splits > 1) {
+      FinalizeArgs f{};
+      f.partial = a.partial;
+      f.splits = w.plan.splits;
+      f.rows = P;
+      f.N = N;
+      f.pair = gateup ? 1 : 0;
+      f.C = C;
+      f.ldc = N;
+      f.accumulate = 0;
+      f.rscale = pair_weight;
+      f.rscale_map = pair_weight ? sorted_pair : nullptr;
+      f.beta = s->beta;
+      f.beta_lin = s->beta_lin;
+      if (launch_finalize(f, st) != hipSuccess) return MOE_EHIP;
+    }
     return MOE_OK;
   });
 }

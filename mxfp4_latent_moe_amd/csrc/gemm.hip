@@ -299,6 +299,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs f) {
     if (f.pair) u += p[f.N + col];
   }
   float v = f.pair ? situ_glu(a, u, f.beta, f.beta_lin) : a;
+  if (f.rscale != nullptr) v *= f.rscale[f.rscale_map ? f.rscale_map[row] : row];
   float *c = f.C + row * f.ldc + col;
   *c = f.accumulate ? *c + v : v;
 }
@@ -352,7 +353,7 @@ hipError_t launch_variant(const GemmArgs &a, long long grid, hipStream_t st) {
 
 template <int WF, int AF, bool PAIR>
 hipError_t launch_nt(const GemmPlan &pl, const GemmArgs &a, long long grid, hipStream_t st) {
-  if (pl.nt == 1) return launch_variant<WF, AF, PAIR, 1, 4>(a, grid, st);
+  (void)pl;
   return launch_variant<WF, AF, PAIR, 8, 2>(a, grid, st);
 }
 
@@ -378,43 +379,68 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 GemmPlan plan_dense(int rows, int N, int K, bool pair) {
   GemmPlan p{};
-  p.nt = rows <= 64 ? 1 : 8;
-  p.mt = p.nt == 1 ? 4 : 2;
-  p.chunk_rows = 16 * p.nt;
-  p.n_blocks = ceil_div(N, 64 * p.mt);
-  p.max_chunks = ceil_div(rows, p.chunk_rows);
   const int ksteps = K / KSTEP;
-  long long items = (long long)p.max_chunks * p.n_blocks;
-  int splits = 1;
-  // small row counts stream the weights once: split K until the grid fills the chip
-  while (items * splits < 2048 && splits * 2 <= ksteps && splits < 64) splits *= 2;
-  p.splits = splits;
-  p.grid_logical = items * splits;
-  p.partial_bytes = splits > 1 ? (size_t)splits * rows * (pair ? 2 : 1) * N * sizeof(float) : 0;
+  if (rows <= 64) {
+    // streaming variant: 16-row chunks, K split so each split fits in LDS and
+    // the grid fills the chip
+    p.variant = 1;
+    p.nt = 1;
+    p.chunk_rows = 16;
+    p.mt = stream_rows_per_wg(W_BF16, pair) / 64;
+    p.n_blocks = ceil_div(N, stream_rows_per_wg(W_BF16, pair));
+    p.max_chunks = ceil_div(rows, 16);
+    const long long items = (long long)p.max_chunks * p.n_blocks;
+    int splits = ceil_div(ksteps, STREAM_KSMAX);
+    while (items * splits < 2048 && ceil_div(ksteps, splits * 2) >= 2) splits *= 2;
+    p.splits = splits;
+    p.grid_logical = items * splits;
+  } else {
+    p.variant = 0;
+    p.nt = 8;
+    p.mt = 2;
+    p.chunk_rows = 128;
+    p.n_blocks = ceil_div(N, 64 * p.mt);
+    p.max_chunks = ceil_div(rows, p.chunk_rows);
+    const long long items = (long long)p.max_chunks * p.n_blocks;
+    int splits = 1;
+    while (items * splits < 1024 && splits * 2 <= ksteps && splits < 16) splits *= 2;
+    p.splits = splits;
+    p.grid_logical = items * splits;
+  }
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * rows * (pair ? 2 : 1) * N * sizeof(float) : 0;
   return p;
 }
 
 GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
-  (void)K;
-  (void)pair;
   GemmPlan p{};
-  // average rows per expert decides between the streaming (one token tile)
-  // and the tiled variant
+  const int ksteps = K / KSTEP;
+  // average rows per expert decides between the streaming and the tiled variant
   const double avg = (double)P / (double)E;
-  p.nt = avg < 2.0 ? 1 : 8;
-  p.mt = p.nt == 1 ? 4 : 2;
-  p.chunk_rows = 16 * p.nt;
-  p.n_blocks = ceil_div(N, 64 * p.mt);
+  if (avg < 2.0) {
+    p.variant = 1;
+    p.nt = 1;
+    p.chunk_rows = 16;
+    p.mt = stream_rows_per_wg(W_MXFP4, pair) / 64;
+    p.n_blocks = ceil_div(N, stream_rows_per_wg(W_MXFP4, pair));
+    p.splits = ceil_div(ksteps, STREAM_KSMAX);
+  } else {
+    p.variant = 0;
+    p.nt = 8;
+    p.mt = 2;
+    p.chunk_rows = 128;
+    p.n_blocks = ceil_div(N, 64 * p.mt);
+    p.splits = 1;
+  }
   p.max_chunks = P / p.chunk_rows + (E < P ? E : P);
-  p.splits = 1;
-  p.grid_logical = (long long)p.max_chunks * p.n_blocks;
-  p.partial_bytes = 0;
+  p.grid_logical = (long long)p.max_chunks * p.n_blocks * p.splits;
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * P * (pair ? 2 : 1) * N * sizeof(float) : 0;
   return p;
 }
 
 hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
                        hipStream_t st) {
   const long long grid = (pl.grid_logical + 7) / 8 * 8;
+  if (pl.variant == 1) return launch_stream_gemm(wfmt, afmt, pair, a, grid, st);
   if (wfmt == W_MXFP4) return launch_af<W_MXFP4>(pl, afmt, pair, a, grid, st);
   return launch_af<W_BF16>(pl, afmt, pair, a, grid, st);
 }

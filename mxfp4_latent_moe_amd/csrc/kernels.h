@@ -45,11 +45,18 @@ struct FinalizeArgs {
   float *C;
   long long ldc;
   int accumulate;
+  const float *rscale;    // optional row scale rscale[rscale_map[row]]
+  const int32_t *rscale_map;
   float beta, beta_lin;
 };
 
+// K steps (of 128) one streaming workgroup keeps in LDS; K is split so that
+// no split exceeds it.
+constexpr int STREAM_KSMAX = 8;
+
 // kernel variant selection (host side)
 struct GemmPlan {
+  int variant;   // 0: tiled (LDS-staged K steps), 1: streaming (<= 16-row chunks)
   int nt;        // 16-token tiles per chunk (1 or 8)
   int mt;        // 16-row weight tiles per wave and matrix
   int chunk_rows;
@@ -62,6 +69,10 @@ struct GemmPlan {
 
 GemmPlan plan_dense(int rows, int N, int K, bool pair);
 GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
+
+int stream_rows_per_wg(int wfmt, bool pair);
+hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
+                              hipStream_t st);
 
 hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
                        hipStream_t st);

@@ -126,7 +126,7 @@ def test_grouped_gemm_validation(lib):
     assert call(A=FAKE + 4) == _lib.MOE_EINVAL
     assert call(wsc=FAKE + 1) == _lib.MOE_EINVAL
     assert call(wsb=ws - 1) == _lib.MOE_EWORKSPACE
-    assert call(op=D, w3p=None, w3s=None, wsb=ws - 1) == _lib.MOE_EWORKSPACE
+    assert call(op=D, w3p=None, w3s=None, wsb=16) == _lib.MOE_EWORKSPACE
 
 
 def test_combine_and_shared_validation(lib):
