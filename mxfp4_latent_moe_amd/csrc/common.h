@@ -53,3 +53,29 @@ MOE_DEV float situ_glu(float g, float u, float beta, float beta_lin) {
 }
 
 MOE_DEV int lane_id() { return threadIdx.x & 63; }
+
+// Raw buffer resource over [base, base + bytes): loads outside it return 0.
+// Word 3 is the gfx9-family raw-buffer format (32-bit data format, no swizzle).
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+MOE_DEV u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+MOE_DEV uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+// Work-item decode shared by the GEMM kernels.  The grid is sized for the
+// worst case; the real items are the first `total` logical ids.  Blocks are
+// handed to the 8 XCDs round-robin, so block b gets logical id
+// (b % 8) * (T8 / 8) + b / 8 with T8 = total rounded up to 8: every XCD gets an
+// equal share of the real items and consecutive logical ids (the weight
+// blocks of one row chunk) run on the same XCD.  Returns -1 for no work.
+MOE_DEV int xcd_logical(int total) {
+  const int t8 = (total + 7) & ~7;
+  const int b = blockIdx.x;
+  if (b >= t8) return -1;
+  const int logical = (b & 7) * (t8 >> 3) + (b >> 3);
+  return logical < total ? logical : -1;
+}

@@ -40,13 +40,11 @@ __global__ __launch_bounds__(256) void ws_gemm_kernel(GemmArgs g) {
   const int kg = lane >> 4;
   const int r16 = lane & 15;
 
-  // XCD-aware remap: blocks b, b+8, b+16, ... run on one XCD; give them
-  // consecutive logical ids so one chunk's weight blocks share an L2.
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
-  const int logical = (b & 7) * (G >> 3) + (b >> 3);
-  if (logical >= g.grid_logical) return;
+  // XCD-aware remap over the real work items (one chunk's weight blocks share an L2)
   const int per_chunk = g.n_blocks * g.splits;
+  const int total = g.chunks ? min(*g.chunk_count * per_chunk, g.grid_logical) : g.grid_logical;
+  const int logical = xcd_logical(total);
+  if (logical < 0) return;
   const int chunk = logical / per_chunk;
   const int rem = logical - chunk * per_chunk;
   const int nb = rem / g.splits;
@@ -54,7 +52,6 @@ __global__ __launch_bounds__(256) void ws_gemm_kernel(GemmArgs g) {
 
   int expert, row0, nrows;
   if (g.chunks != nullptr) {
-    if (chunk >= *g.chunk_count) return;
     const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
     expert = c.x;
     row0 = c.y;
@@ -419,10 +416,10 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
   if (avg < 2.0) {
     p.variant = 1;
     p.nt = 1;
-    p.chunk_rows = 16;
+    p.chunk_rows = STREAM_GROUPED_ROWS;
     p.mt = stream_rows_per_wg(W_MXFP4, pair) / 64;
     p.n_blocks = ceil_div(N, stream_rows_per_wg(W_MXFP4, pair));
-    p.splits = ceil_div(ksteps, STREAM_KSMAX);
+    p.splits = ceil_div(ksteps, STREAM_GROUPED_KSMAX);
   } else {
     p.variant = 0;
     p.nt = 8;

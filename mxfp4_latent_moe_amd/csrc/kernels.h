@@ -53,6 +53,10 @@ struct FinalizeArgs {
 // K steps (of 128) one streaming workgroup keeps in LDS; K is split so that
 // no split exceeds it.
 constexpr int STREAM_KSMAX = 8;
+// Streaming expert GEMMs: rows per chunk and the K steps one workgroup holds
+// (the whole K of the K3 expert matrices: 3584 / 128 = 28).
+constexpr int STREAM_GROUPED_ROWS = 2;
+constexpr int STREAM_GROUPED_KSMAX = 32;
 
 // kernel variant selection (host side)
 struct GemmPlan {

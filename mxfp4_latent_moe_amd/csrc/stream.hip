@@ -2,9 +2,10 @@
 // token rows (decode-sized work): the weights are the whole cost, so the
 // kernel is built to keep many weight bytes in flight.
 //
-//  * K is split across workgroups so that one workgroup's slice of the token
-//    rows (<= 16 rows x KSMAX*128 K values, bf16 or bf16 hi+lo) sits in LDS
+//  * A workgroup's token rows (R rows per chunk) for its K slice sit in LDS
 //    for the whole main loop: one barrier per workgroup, none per K step.
+//    Expert GEMMs use R = 2 rows and the whole K range; dense products use
+//    R = 16 and split K so the slice fits.
 //  * Each wave streams its own weight rows through a D-deep ring of
 //    registers: the load for K step q+D is issued right after step q is
 //    consumed, with every load unconditional (indices clamped) so the
@@ -21,14 +22,15 @@ namespace {
 
 constexpr int KSTEP = 128;
 
-template <int WF, int AF, bool PAIR, int MT, int D, int KSMAX>
+template <int WF, int AF, bool PAIR, int MT, int D, int R, int KSMAX>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
   constexpr int ROWS_WG = 64 * MT;
   constexpr int WREG = (WF == W_MXFP4) ? 1 : 4;
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
-  constexpr int STEP = 16 * KSTEP;  // bf16 elements per K step per plane: [octet][token][8]
+  constexpr int STEP = 16 * R * 8;  // bf16 elements per K step per plane: [octet 16][row R][8]
+  constexpr int NGRP = (R * KSMAX * 16 + 255) / 256;  // 8-element groups staged per thread
   __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
 
   const int tid = threadIdx.x;
@@ -37,11 +39,10 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
   const int kg = lane >> 4;
   const int r16 = lane & 15;
 
-  const int G = gridDim.x;
-  const int b = blockIdx.x;
-  const int logical = (b & 7) * (G >> 3) + (b >> 3);
-  if (logical >= g.grid_logical) return;
   const int per_chunk = g.n_blocks * g.splits;
+  const int total = g.chunks ? min(*g.chunk_count * per_chunk, g.grid_logical) : g.grid_logical;
+  const int logical = xcd_logical(total);
+  if (logical < 0) return;
   const int chunk = logical / per_chunk;
   const int rem = logical - chunk * per_chunk;
   const int nb = rem / g.splits;
@@ -49,15 +50,14 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
 
   int expert, row0, nrows;
   if (g.chunks != nullptr) {
-    if (chunk >= *g.chunk_count) return;
     const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
     expert = c.x;
     row0 = c.y;
     nrows = c.z;
   } else {
     expert = 0;
-    row0 = chunk * 16;
-    nrows = min(16, g.dense_rows - row0);
+    row0 = chunk * R;
+    nrows = min(R, g.dense_rows - row0);
     if (nrows <= 0) return;
   }
   const int N = g.N, K = g.K;
@@ -65,135 +65,161 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
   const int ks0 = (split * ksteps) / g.splits;
   const int nks = ((split + 1) * ksteps) / g.splits - ks0;  // <= KSMAX (host guarantees)
 
-  // ---- activation rows of the chunk for this K slice: thread = (token tid/16, octet tid%16)
-  {
-    const int r = tid >> 4;
-    const int oct = tid & 15;
-    const int esz = (AF == A_BF16) ? 2 : 4;
-    const char *src = nullptr;
-    if (r < nrows) {
-      const int p = row0 + r;
-      const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
-      src = static_cast<const char *>(g.A) + (arow * g.lda + (long long)ks0 * KSTEP + oct * 8) * esz;
-    }
-    u32x4_t araw[KSMAX][(AF == A_BF16) ? 1 : 2];
+  // ---- weight rows of this wave, read through buffer resources (base in
+  // SGPRs, one 32-bit row offset per tile); the first D K steps are requested
+  // before anything else
+  const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
+  constexpr uint32_t STEP_BYTES = (WF == W_MXFP4) ? KSTEP / 2 : KSTEP * 2;
+  const uint32_t row_bytes = (WF == W_MXFP4) ? K / 2 : K * 2;
+  __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
-    for (int q = 0; q < KSMAX; ++q) {
-      if (q < nks && src != nullptr) {
-        if constexpr (AF == A_BF16) {
-          araw[q][0] = *reinterpret_cast<const u32x4_t *>(src + (long long)q * KSTEP * 2);
-        } else {
-          const u32x4_t *p4 = reinterpret_cast<const u32x4_t *>(src + (long long)q * KSTEP * 4);
-          araw[q][0] = p4[0];
-          araw[q][1] = p4[1];
-        }
-      } else {
-        araw[q][0] = u32x4_t{0, 0, 0, 0};
-        if constexpr (AF != A_BF16) araw[q][1] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < KSMAX; ++q) {
-      if (q < nks) {
-        const int off = q * STEP + (oct * 16 + r) * 8;
-        if constexpr (AF == A_BF16) {
-          *reinterpret_cast<u32x4_t *>(&lds[0][off]) = araw[q][0];
-        } else {
-          bf16x8_t hi, lo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f = __uint_as_float(e < 4 ? araw[q][0][e] : araw[q][1][e - 4]);
-            if constexpr (AF == A_F32_SPLIT) {
-              __bf16 h, l;
-              split_bf16(f, h, l);
-              hi[e] = h;
-              lo[e] = l;
-            } else {
-              hi[e] = to_bf16(f);
-            }
-          }
-          *reinterpret_cast<bf16x8_t *>(&lds[0][off]) = hi;
-          if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[NPL - 1][off]) = lo;
-        }
-      }
+  for (int mat = 0; mat < NMAT; ++mat) {
+    const char *W = static_cast<const char *>(mat ? g.W1 : g.W0) +
+                    expert * g.w_estride * ((WF == W_MXFP4) ? 1 : 2);
+    wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
+    if constexpr (WF == W_MXFP4) {
+      const uint8_t *S = (mat ? g.S1 : g.S0) + expert * g.s_estride;
+      sr[mat] = make_rsrc(S, (uint32_t)N * (K / 32));
     }
   }
-
-  // ---- weight rows of this wave
-  const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
-  const uint8_t *wptr8[NTILE];
-  const uint8_t *sptr[NTILE];
-  const __bf16 *wptr16[NTILE];
+  uint32_t woff[NTILE], soff[NTILE];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
-    const int m = t % MT;
-    const int mat = t / MT;
-    const int n = min(wrow_base + m * 16 + r16, N - 1);
-    if constexpr (WF == W_MXFP4) {
-      const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0);
-      const uint8_t *S = mat ? g.S1 : g.S0;
-      wptr8[t] = W + expert * g.w_estride + (long long)n * (K / 2) + (long long)ks0 * 64 + kg * 16;
-      sptr[t] = S + expert * g.s_estride + (long long)n * (K / 32) + ks0 * 4;
-      wptr16[t] = nullptr;
-    } else {
-      const __bf16 *W = static_cast<const __bf16 *>(mat ? g.W1 : g.W0);
-      wptr16[t] = W + expert * g.w_estride + (long long)n * K + (long long)ks0 * KSTEP + kg * 32;
-      wptr8[t] = nullptr;
-      sptr[t] = nullptr;
-    }
+    const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
+    woff[t] = (uint32_t)n * row_bytes + (uint32_t)ks0 * STEP_BYTES + kg * ((WF == W_MXFP4) ? 16 : 64);
+    soff[t] = (uint32_t)n * (K / 32) + ks0 * 4;
   }
-
   u32x4_t wq[D][NTILE][WREG];
   uint32_t wsc[D][NTILE];
   auto load_w = [&](int d, int q) {
-    q = min(q, nks - 1);  // clamped: tail loads re-read the last step, always in bounds
+    q = min(q, nks - 1);  // clamped: tail requests re-read the last step, always in bounds
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-      if constexpr (WF == W_MXFP4) {
-        wq[d][t][0] = *reinterpret_cast<const u32x4_t *>(wptr8[t] + (long long)q * 64);
-        wsc[d][t] = *reinterpret_cast<const uint32_t *>(sptr[t] + q * 4);
-      } else {
+      const int mat = t / MT;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          wq[d][t][j] = *reinterpret_cast<const u32x4_t *>(wptr16[t] + (long long)q * KSTEP + 8 * j);
-      }
+      for (int j = 0; j < WREG; ++j) wq[d][t][j] = buf_load16(wr[mat], woff[t] + 16 * j, q * STEP_BYTES);
+      if constexpr (WF == W_MXFP4) wsc[d][t] = buf_load4(sr[mat], soff[t], q * 4);
     }
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) load_w(d, d);
 
-  __syncthreads();
-
-  f32x4_t acc[NTILE];
+  // ---- the chunk's token rows for this K slice -> LDS (bf16, or bf16 hi + lo)
+  {
+    const int esz = (AF == A_BF16) ? 2 : 4;
+    const int ngrp = R * nks * 16;
+    u32x4_t araw[NGRP][(AF == A_BF16) ? 1 : 2];
+    int aoff[NGRP];
 #pragma unroll
-  for (int t = 0; t < NTILE; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int q0 = 0; q0 < nks; q0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int q = q0 + d;
-      if (q < nks) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int off = q * STEP + ((4 * kg + j) * 16 + r16) * 8;
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
-          bf16x8_t bl;
-          if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
-#pragma unroll
-          for (int t = 0; t < NTILE; ++t) {
-            bf16x8_t wa;
-            if constexpr (WF == W_MXFP4) {
-              wa = fp4x8_to_bf16(wq[d][t][0][j], e8m0_to_float((wsc[d][t] >> (8 * kg)) & 0xFFu));
-            } else {
-              wa = __builtin_bit_cast(bf16x8_t, wq[d][t][j]);
-            }
-            acc[t] = mfma_16x16x32(wa, bh, acc[t]);
-            if constexpr (NPL == 2) acc[t] = mfma_16x16x32(wa, bl, acc[t]);
-          }
+    for (int i = 0; i < NGRP; ++i) {
+      const int gi = tid + 256 * i;  // group -> (K step q, octet, row r)
+      const int r = gi % R;
+      const int oct = (gi / R) & 15;
+      const int q = gi / (16 * R);
+      aoff[i] = (gi < ngrp) ? q * STEP + (oct * R + r) * 8 : -1;
+      araw[i][0] = u32x4_t{0, 0, 0, 0};
+      if constexpr (AF != A_BF16) araw[i][1] = u32x4_t{0, 0, 0, 0};
+      if (gi < ngrp && r < nrows) {
+        const int p = row0 + r;
+        const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
+        const char *src = static_cast<const char *>(g.A) +
+                          (arow * g.lda + (long long)(ks0 + q) * KSTEP + oct * 8) * esz;
+        if constexpr (AF == A_BF16) {
+          araw[i][0] = *reinterpret_cast<const u32x4_t *>(src);
+        } else {
+          araw[i][0] = reinterpret_cast<const u32x4_t *>(src)[0];
+          araw[i][1] = reinterpret_cast<const u32x4_t *>(src)[1];
         }
-        load_w(d, q + D);
       }
     }
+#pragma unroll
+    for (int i = 0; i < NGRP; ++i) {
+      if (aoff[i] < 0) continue;
+      if constexpr (AF == A_BF16) {
+        *reinterpret_cast<u32x4_t *>(&lds[0][aoff[i]]) = araw[i][0];
+      } else {
+        bf16x8_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = __uint_as_float(e < 4 ? araw[i][0][e] : araw[i][1][e - 4]);
+          if constexpr (AF == A_F32_SPLIT) {
+            __bf16 h, l;
+            split_bf16(f, h, l);
+            hi[e] = h;
+            lo[e] = l;
+          } else {
+            hi[e] = to_bf16(f);
+          }
+        }
+        *reinterpret_cast<bf16x8_t *>(&lds[0][aoff[i]]) = hi;
+        if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[NPL - 1][aoff[i]]) = lo;
+      }
+    }
+  }
+  __syncthreads();
+
+  // hi and lo products accumulate separately so consecutive MFMAs never wait
+  // on each other's result; they are added once at the end
+  f32x4_t acc[NTILE], accl[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accl[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Lanes whose token column is >= R read row (r16 % R): those MFMA output
+  // columns are never stored, so their B values need no zeroing.
+  const int brow = r16 % R;
+  auto compute = [&](int d, int q) {
+    bf16x8_t bh[4], bl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
+      bh[j] = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+      if constexpr (NPL == 2) bl[j] = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
+    }
+    float sc[NTILE];
+    if constexpr (WF == W_MXFP4) {
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) sc[t] = e8m0_to_float((wsc[d][t] >> (8 * kg)) & 0xFFu);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t wa[NTILE];
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        if constexpr (WF == W_MXFP4) {
+          wa[t] = fp4x8_to_bf16(wq[d][t][0][j], sc[t]);
+        } else {
+          wa[t] = __builtin_bit_cast(bf16x8_t, wq[d][t][j]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh[j], acc[t]);
+      if constexpr (NPL == 2) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl[j], accl[t]);
+      }
+    }
+  };
+
+  // main loop: whole rings of D steps, every load unconditional
+  const int nfull = nks - nks % D;
+  for (int q0 = 0; q0 < nfull; q0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(d, q0 + d);
+      load_w(d, q0 + d + D);
+    }
+  }
+  // remaining nks % D steps: their weights are already in the ring
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (nfull + d < nks) compute(d, nfull + d);
+
+  if constexpr (NPL == 2) {
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) acc[t] += accl[t];
   }
 
   // ---- epilogue: lane holds token r16, weight rows 4*kg + 0..3 of each tile
@@ -250,10 +276,11 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
 template <int WF, int AF, bool PAIR>
 hipError_t launch_cfg(const GemmArgs &a, long long grid, hipStream_t st) {
   if constexpr (WF == W_MXFP4) {
-    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, PAIR ? 2 : 4, 4, STREAM_KSMAX>),
+    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, PAIR ? 2 : 4, 4, STREAM_GROUPED_ROWS,
+                                           STREAM_GROUPED_KSMAX>),
                        dim3((unsigned)grid), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, PAIR ? 1 : 2, 2, STREAM_KSMAX>),
+    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, PAIR ? 1 : 2, 2, 16, STREAM_KSMAX>),
                        dim3((unsigned)grid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
