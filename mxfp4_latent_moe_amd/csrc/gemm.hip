@@ -413,7 +413,14 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
   const int ksteps = K / KSTEP;
   // average rows per expert decides between the streaming and the tiled variant
   const double avg = (double)P / (double)E;
-  if (avg < 2.0) {
+  if (avg < 2.0 && grouped_stream_fits(K)) {
+    p.variant = 2;
+    p.nt = 1;
+    p.chunk_rows = STREAM_GROUPED_ROWS;
+    p.mt = 1;
+    p.n_blocks = ceil_div(N, grouped_stream_rows_per_wg());
+    p.splits = 1;
+  } else if (avg < 2.0) {
     p.variant = 1;
     p.nt = 1;
     p.chunk_rows = STREAM_GROUPED_ROWS;
@@ -437,6 +444,7 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
 hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
                        hipStream_t st) {
   const long long grid = (pl.grid_logical + 7) / 8 * 8;
+  if (pl.variant == 2) return launch_grouped_stream(afmt, pair, a, st);
   if (pl.variant == 1) return launch_stream_gemm(wfmt, afmt, pair, a, grid, st);
   if (wfmt == W_MXFP4) return launch_af<W_MXFP4>(pl, afmt, pair, a, grid, st);
   return launch_af<W_BF16>(pl, afmt, pair, a, grid, st);

@@ -1,0 +1,338 @@
+// Persistent streaming MXFP4 grouped GEMM for decode-sized expert segments.
+//
+// Work item = (row chunk of <= R sorted rows of one expert, block of weight
+// rows).  The grid holds one resident wave of work-groups; work-group w takes
+// the contiguous item range [w*n/G, (w+1)*n/G) of the n items that exist on
+// the device (n is read from the chunk list, so nothing waits on the host).
+// Within a work-group the weight stream never stops: every wave walks the K
+// steps of its rows item after item, with a D-deep register ring whose loads
+// run D steps ahead of the MFMAs and cross item boundaries freely.  The
+// token rows of the current chunk (bf16, or bf16 hi + lo) sit in LDS; they
+// are restaged only when the chunk changes.
+//
+// Per K step (128 K values) a lane holds one 16-byte slice of one weight row
+// (32 e2m1 codes = one scale group), converted in registers with the scaled
+// fp4 -> bf16 instruction and fed to MFMA 16x16x32 bf16 as the M side; the
+// tokens are the N side.  Scales are read 16 bytes at a time (four K steps of
+// one row); the kernel takes rows whose K steps come in groups of four.
+#include <atomic>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int KSTEP = 128;
+constexpr int R = STREAM_GROUPED_ROWS;
+constexpr int KSMAX = STREAM_GROUPED_KSMAX;
+
+template <int AF, bool PAIR, int MT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
+  static_assert(D == 4, "16-byte scale reads cover four K steps: a 4-deep ring");
+  constexpr int NMAT = PAIR ? 2 : 1;
+  constexpr int NTILE = NMAT * MT;
+  constexpr int NTHR = 64 * NW;
+  constexpr int ROWS_WG = 16 * NW * MT;
+  constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
+  constexpr int STEP = 16 * R * 8;  // bf16 elements per K step per plane: [octet][row][8]
+  __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kg = lane >> 4;
+  const int r16 = lane & 15;
+  const int N = g.N, K = g.K;
+  const int nks = K / KSTEP;
+  const uint32_t row_bytes = K / 2;
+  const uint32_t srow_bytes = K / 32;
+
+  const int n_items = *g.chunk_count * g.n_blocks;
+  const int G = gridDim.x;
+  const int i_begin = (int)((long long)blockIdx.x * n_items / G);
+  const int i_end = (int)((long long)(blockIdx.x + 1) * n_items / G);
+  if (i_begin >= i_end) return;
+  // the chunk list is read-only here: reading it through the constant address
+  // space with wave-uniform indices keeps those reads on the scalar unit, off
+  // the vector memory counter that paces the weight ring
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const_i32 *chunks = (const_i32 *)(g.chunks);  // {expert, row0, nrows, 0} per chunk
+
+  // ---- load cursor: item and K step of the next weight load
+  int l_item = i_begin, l_q = 0;
+  __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
+  uint32_t woff[NTILE], soff[NTILE];
+  auto set_load_item = [&](int it) {
+    const int c = __builtin_amdgcn_readfirstlane(it / g.n_blocks);
+    const int nb = it - c * g.n_blocks;
+    const int expert = chunks[4 * c];
+#pragma unroll
+    for (int mat = 0; mat < NMAT; ++mat) {
+      const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0) + expert * g.w_estride;
+      const uint8_t *S = (mat ? g.S1 : g.S0) + expert * g.s_estride;
+      wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
+      sr[mat] = make_rsrc(S, (uint32_t)N * srow_bytes);
+    }
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int n = min(nb * ROWS_WG + wave * 16 * MT + (t % MT) * 16 + r16, N - 1);
+      woff[t] = (uint32_t)n * row_bytes + kg * 16;
+      soff[t] = (uint32_t)n * srow_bytes;
+    }
+  };
+  set_load_item(i_begin);
+
+  u32x4_t wq[D][NTILE];
+  // 16 scale bytes = the scale dwords of 4 consecutive K steps: the group being
+  // computed and the one being loaded (copied over at each group boundary, so
+  // every register index stays static)
+  u32x4_t sc_cur[NTILE], sc_nxt[NTILE];
+  // Issue the loads of the load cursor's step into ring slot d and advance the
+  // cursor.  Past the last item the loads are kept (so the memory counter
+  // pattern stays fixed) but all lanes read one 16-byte line.
+  auto load_step = [&](int d) {
+    const bool live = l_item < i_end;
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int mat = t / MT;
+      wq[d][t] = buf_load16(wr[mat], live ? woff[t] : 0u, live ? (uint32_t)l_q * 64u : 0u);
+      if (d == 0) sc_nxt[t] = buf_load16(sr[mat], live ? soff[t] : 0u, live ? (uint32_t)l_q * 4u : 0u);
+    }
+    if (++l_q == nks) {
+      l_q = 0;
+      if (++l_item < i_end) set_load_item(l_item);
+    }
+  };
+
+  // ---- compute cursor
+  int c_item = i_begin, c_q = 0;
+  int staged_chunk = -1;
+  int row0 = 0, nrows = 0, c_nb = 0;
+
+  auto stage = [&](int c) {
+    c = __builtin_amdgcn_readfirstlane(c);
+    row0 = chunks[4 * c + 1];
+    nrows = chunks[4 * c + 2];
+    if (c == staged_chunk) return;
+    __syncthreads();  // every wave is done with the previous chunk's rows
+    constexpr int SG = 2;
+    const int esz = (AF == A_BF16) ? 2 : 4;
+    const int ngrp = R * nks * 16;
+    for (int i0 = tid; i0 < ngrp; i0 += NTHR * SG) {
+      u32x4_t araw[SG][(AF == A_BF16) ? 1 : 2];
+      int aoff[SG];
+#pragma unroll
+      for (int ii = 0; ii < SG; ++ii) {
+        const int gi = i0 + NTHR * ii;
+        const int r = gi % R;
+        const int oct = (gi / R) & 15;
+        const int q = gi / (16 * R);
+        aoff[ii] = (gi < ngrp) ? q * STEP + (oct * R + r) * 8 : -1;
+        araw[ii][0] = u32x4_t{0, 0, 0, 0};
+        if constexpr (AF != A_BF16) araw[ii][1] = u32x4_t{0, 0, 0, 0};
+        if (gi < ngrp && r < nrows) {
+          const int p = row0 + r;
+          const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
+          const char *src = static_cast<const char *>(g.A) + (arow * g.lda + (long long)q * KSTEP + oct * 8) * esz;
+          if constexpr (AF == A_BF16) {
+            araw[ii][0] = *reinterpret_cast<const u32x4_t *>(src);
+          } else {
+            araw[ii][0] = reinterpret_cast<const u32x4_t *>(src)[0];
+            araw[ii][1] = reinterpret_cast<const u32x4_t *>(src)[1];
+          }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < SG; ++ii) {
+        if (aoff[ii] < 0) continue;
+        if constexpr (AF == A_BF16) {
+          *reinterpret_cast<u32x4_t *>(&lds[0][aoff[ii]]) = araw[ii][0];
+        } else {
+          bf16x8_t hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = __uint_as_float(e < 4 ? araw[ii][0][e] : araw[ii][1][e - 4]);
+            if constexpr (AF == A_F32_SPLIT) {
+              __bf16 h, l;
+              split_bf16(f, h, l);
+              hi[e] = h;
+              lo[e] = l;
+            } else {
+              hi[e] = to_bf16(f);
+            }
+          }
+          *reinterpret_cast<bf16x8_t *>(&lds[0][aoff[ii]]) = hi;
+          if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[NPL - 1][aoff[ii]]) = lo;
+        }
+      }
+    }
+    __syncthreads();
+    staged_chunk = c;
+  };
+
+  f32x4_t acc[NTILE], accl[NTILE];
+  auto reset_acc = [&]() {
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accl[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  auto begin_item = [&]() {
+    const int c = c_item / g.n_blocks;
+    c_nb = c_item - c * g.n_blocks;
+    stage(c);
+    reset_acc();
+  };
+
+  auto finish_item = [&]() {
+    const int tok = r16;
+    if (tok < nrows) {
+      const long long orow = row0 + tok;
+      const int wrow_base = c_nb * ROWS_WG + wave * 16 * MT;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int col0 = wrow_base + m * 16 + 4 * kg;
+        f32x4_t a = acc[m];
+        if constexpr (NPL == 2) a += accl[m];
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (PAIR) {
+            f32x4_t u = acc[m + MT];
+            if constexpr (NPL == 2) u += accl[m + MT];
+            v[r] = situ_glu(a[r], u[r], g.beta, g.beta_lin);
+          } else {
+            v[r] = a[r];
+          }
+        }
+        if (g.rscale != nullptr) {
+          const float rs = g.rscale[g.rscale_map ? g.rscale_map[orow] : orow];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] *= rs;
+        }
+        float *cp = g.C + orow * g.ldc + col0;
+        if (col0 + 3 < N) {
+          *reinterpret_cast<f32x4_t *>(cp) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col0 + r < N) cp[r] = v[r];
+        }
+      }
+    }
+  };
+
+  // Lanes whose token column is >= R read row (r16 % R): those MFMA output
+  // columns are never stored.
+  const int brow = r16 % R;
+  auto compute = [&](int d, int q) {
+    bf16x8_t bh[4], bl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
+      bh[j] = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+      if constexpr (NPL == 2) bl[j] = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
+    }
+    float scl[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const uint32_t sw = sc_cur[t][d];  // the dword of K step q (= group start + d)
+      scl[t] = e8m0_to_float((sw >> (8 * kg)) & 0xFFu);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t wa[NTILE];
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[d][t][j], scl[t]);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh[j], acc[t]);
+      if constexpr (NPL == 2) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl[j], accl[t]);
+      }
+    }
+  };
+
+  // ---- prologue: the first D steps are requested before the first staging
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_step(d);
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) sc_cur[t] = sc_nxt[t];
+
+  // nks is a multiple of D (host guarantee), so every item starts at ring
+  // slot 0 with a fresh scale group
+  for (; c_item < i_end; ++c_item) {
+    begin_item();
+    for (c_q = 0; c_q < nks; c_q += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        compute(d, c_q + d);
+        load_step(d);  // refill slot d with the step D ahead
+      }
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) sc_cur[t] = sc_nxt[t];
+    }
+    finish_item();
+  }
+}
+
+template <int AF, bool PAIR>
+void *kernel_ptr() {
+  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, 1, 4, 4>);
+}
+
+void *select_kernel(int afmt, bool pair) {
+  switch (afmt) {
+    case A_BF16: return pair ? kernel_ptr<A_BF16, true>() : kernel_ptr<A_BF16, false>();
+    case A_F32_SPLIT: return pair ? kernel_ptr<A_F32_SPLIT, true>() : kernel_ptr<A_F32_SPLIT, false>();
+    default: return pair ? kernel_ptr<A_F32_ROUND, true>() : kernel_ptr<A_F32_ROUND, false>();
+  }
+}
+
+}  // namespace
+
+int grouped_stream_rows_per_wg() { return 16 * 4 * 1; }
+
+bool grouped_stream_fits(int K) {
+  const int nks = K / KSTEP;
+  return nks % 4 == 0 && nks <= KSMAX;
+}
+
+hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st) {
+  void *fn = select_kernel(afmt, pair);
+  // one resident wave of work-groups (occupancy queried once per kernel and device)
+  static std::atomic<int> cache[64][6];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const int slot = afmt * 2 + (pair ? 1 : 0);
+  int per_cu = cache[dev][slot].load();
+  if (per_cu == 0) {
+    int blocks = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 256, 0);
+    if (e != hipSuccess) return e;
+    per_cu = blocks > 0 ? blocks : 1;
+    cache[dev][slot].store(per_cu);
+  }
+  static std::atomic<int> cus[64];
+  int ncu = cus[dev].load();
+  if (ncu == 0) {
+    hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus[dev].store(ncu);
+  }
+  const long long max_items = (long long)a.grid_logical;  // chunks bound x weight blocks
+  long long grid = (long long)ncu * per_cu;
+  if (grid > max_items) grid = max_items;
+  if (grid < 1) grid = 1;
+  GemmArgs args = a;
+  void *params[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), params, 0, st);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -60,7 +60,8 @@ constexpr int STREAM_GROUPED_KSMAX = 32;
 
 // kernel variant selection (host side)
 struct GemmPlan {
-  int variant;   // 0: tiled (LDS-staged K steps), 1: streaming (<= 16-row chunks)
+  int variant;   // 0: tiled (LDS-staged K steps), 1: streaming (<= 16-row chunks),
+                 // 2: persistent streaming over expert row chunks
   int nt;        // 16-token tiles per chunk (1 or 8)
   int mt;        // 16-row weight tiles per wave and matrix
   int chunk_rows;
@@ -75,6 +76,9 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair);
 GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
 
 int stream_rows_per_wg(int wfmt, bool pair);
+int grouped_stream_rows_per_wg();
+bool grouped_stream_fits(int K);
+hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                               hipStream_t st);
 

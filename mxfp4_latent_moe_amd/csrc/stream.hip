@@ -22,15 +22,16 @@ namespace {
 
 constexpr int KSTEP = 128;
 
-template <int WF, int AF, bool PAIR, int MT, int D, int R, int KSMAX>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
+template <int WF, int AF, bool PAIR, int MT, int D, int R, int KSMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(GemmArgs g) {
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
-  constexpr int ROWS_WG = 64 * MT;
+  constexpr int NTHR = 64 * NW;
+  constexpr int ROWS_WG = 16 * NW * MT;
   constexpr int WREG = (WF == W_MXFP4) ? 1 : 4;
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
   constexpr int STEP = 16 * R * 8;  // bf16 elements per K step per plane: [octet 16][row R][8]
-  constexpr int NGRP = (R * KSMAX * 16 + 255) / 256;  // 8-element groups staged per thread
+  constexpr int NGRP = (R * KSMAX * 16 + NTHR - 1) / NTHR;  // 8-element groups staged per thread
   __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
 
   const int tid = threadIdx.x;
@@ -104,59 +105,69 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int d = 0; d < D; ++d) load_w(d, d);
 
-  // ---- the chunk's token rows for this K slice -> LDS (bf16, or bf16 hi + lo)
+  // ---- the chunk's token rows for this K slice -> LDS (bf16, or bf16 hi + lo),
+  // in passes of SG groups per thread to keep few registers live
   {
+    constexpr int SG = 2;
     const int esz = (AF == A_BF16) ? 2 : 4;
     const int ngrp = R * nks * 16;
-    u32x4_t araw[NGRP][(AF == A_BF16) ? 1 : 2];
-    int aoff[NGRP];
+#pragma unroll 1
+    for (int i0 = 0; i0 < NGRP; i0 += SG) {
+      u32x4_t araw[SG][(AF == A_BF16) ? 1 : 2];
+      int aoff[SG];
 #pragma unroll
-    for (int i = 0; i < NGRP; ++i) {
-      const int gi = tid + 256 * i;  // group -> (K step q, octet, row r)
-      const int r = gi % R;
-      const int oct = (gi / R) & 15;
-      const int q = gi / (16 * R);
-      aoff[i] = (gi < ngrp) ? q * STEP + (oct * R + r) * 8 : -1;
-      araw[i][0] = u32x4_t{0, 0, 0, 0};
-      if constexpr (AF != A_BF16) araw[i][1] = u32x4_t{0, 0, 0, 0};
-      if (gi < ngrp && r < nrows) {
-        const int p = row0 + r;
-        const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
-        const char *src = static_cast<const char *>(g.A) +
-                          (arow * g.lda + (long long)(ks0 + q) * KSTEP + oct * 8) * esz;
-        if constexpr (AF == A_BF16) {
-          araw[i][0] = *reinterpret_cast<const u32x4_t *>(src);
-        } else {
-          araw[i][0] = reinterpret_cast<const u32x4_t *>(src)[0];
-          araw[i][1] = reinterpret_cast<const u32x4_t *>(src)[1];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NGRP; ++i) {
-      if (aoff[i] < 0) continue;
-      if constexpr (AF == A_BF16) {
-        *reinterpret_cast<u32x4_t *>(&lds[0][aoff[i]]) = araw[i][0];
-      } else {
-        bf16x8_t hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = __uint_as_float(e < 4 ? araw[i][0][e] : araw[i][1][e - 4]);
-          if constexpr (AF == A_F32_SPLIT) {
-            __bf16 h, l;
-            split_bf16(f, h, l);
-            hi[e] = h;
-            lo[e] = l;
+      for (int ii = 0; ii < SG; ++ii) {
+        const int gi = tid + NTHR * (i0 + ii);  // group -> (K step q, octet, row r)
+        const int r = gi % R;
+        const int oct = (gi / R) & 15;
+        const int q = gi / (16 * R);
+        aoff[ii] = (gi < ngrp) ? q * STEP + (oct * R + r) * 8 : -1;
+        araw[ii][0] = u32x4_t{0, 0, 0, 0};
+        if constexpr (AF != A_BF16) araw[ii][1] = u32x4_t{0, 0, 0, 0};
+        if (gi < ngrp && r < nrows) {
+          const int p = row0 + r;
+          const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
+          const char *src = static_cast<const char *>(g.A) +
+                            (arow * g.lda + (long long)(ks0 + q) * KSTEP + oct * 8) * esz;
+          if constexpr (AF == A_BF16) {
+            araw[ii][0] = *reinterpret_cast<const u32x4_t *>(src);
           } else {
-            hi[e] = to_bf16(f);
+            araw[ii][0] = reinterpret_cast<const u32x4_t *>(src)[0];
+            araw[ii][1] = reinterpret_cast<const u32x4_t *>(src)[1];
           }
         }
-        *reinterpret_cast<bf16x8_t *>(&lds[0][aoff[i]]) = hi;
-        if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[NPL - 1][aoff[i]]) = lo;
+      }
+#pragma unroll
+      for (int ii = 0; ii < SG; ++ii) {
+        if (aoff[ii] < 0) continue;
+        if constexpr (AF == A_BF16) {
+          *reinterpret_cast<u32x4_t *>(&lds[0][aoff[ii]]) = araw[ii][0];
+        } else {
+          bf16x8_t hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = __uint_as_float(e < 4 ? araw[ii][0][e] : araw[ii][1][e - 4]);
+            if constexpr (AF == A_F32_SPLIT) {
+              __bf16 h, l;
+              split_bf16(f, h, l);
+              hi[e] = h;
+              lo[e] = l;
+            } else {
+              hi[e] = to_bf16(f);
+            }
+          }
+          *reinterpret_cast<bf16x8_t *>(&lds[0][aoff[ii]]) = hi;
+          if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[NPL - 1][aoff[ii]]) = lo;
+        }
       }
     }
   }
   __syncthreads();
+  // The staging above already waited for every load it issued (the newest
+  // ones); saying so explicitly lets the waitcnt pass enter the main loop with
+  // no pending writes, instead of merging them into a full wait at the loop
+  // head on every iteration.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // hi and lo products accumulate separately so consecutive MFMAs never wait
   // on each other's result; they are added once at the end
@@ -276,11 +287,11 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs g) {
 template <int WF, int AF, bool PAIR>
 hipError_t launch_cfg(const GemmArgs &a, long long grid, hipStream_t st) {
   if constexpr (WF == W_MXFP4) {
-    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, PAIR ? 2 : 4, 4, STREAM_GROUPED_ROWS,
-                                           STREAM_GROUPED_KSMAX>),
+    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, 2, 4, STREAM_GROUPED_ROWS,
+                                           STREAM_GROUPED_KSMAX, 4>),
                        dim3((unsigned)grid), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, PAIR ? 1 : 2, 2, 16, STREAM_KSMAX>),
+    hipLaunchKernelGGL((stream_gemm_kernel<WF, AF, PAIR, 1, 3, 16, STREAM_KSMAX, 4>),
                        dim3((unsigned)grid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
@@ -303,7 +314,8 @@ hipError_t launch_af(int afmt, bool pair, const GemmArgs &a, long long grid, hip
 }  // namespace
 
 int stream_rows_per_wg(int wfmt, bool pair) {
-  const int mt = (wfmt == W_MXFP4) ? (pair ? 2 : 4) : (pair ? 1 : 2);
+  (void)pair;
+  const int mt = (wfmt == W_MXFP4) ? 2 : 1;
   return 64 * mt;
 }
 
