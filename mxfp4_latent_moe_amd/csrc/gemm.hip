@@ -418,7 +418,7 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
     p.nt = 1;
     p.chunk_rows = STREAM_GROUPED_ROWS;
     p.mt = 1;
-    p.n_blocks = ceil_div(N, grouped_stream_rows_per_wg());
+    p.n_blocks = ceil_div(N, grouped_stream_rows_per_wg(pair));
     p.splits = 1;
   } else if (avg < 2.0) {
     p.variant = 1;

@@ -5,8 +5,9 @@
 // the contiguous item range [w*n/G, (w+1)*n/G) of the n items that exist on
 // the device (n is read from the chunk list, so nothing waits on the host).
 // Within a work-group the weight stream never stops: every wave walks the K
-// steps of its rows item after item, with a D-deep register ring whose loads
-// run D steps ahead of the MFMAs and cross item boundaries freely.  The
+// steps of its rows item after item.  Weights are requested a group of four
+// K steps at a time (256 contiguous bytes per row in one burst, which keeps
+// DRAM pages open), two groups ahead of the MFMAs, across item boundaries.  The
 // token rows of the current chunk (bf16, or bf16 hi + lo) sit in LDS; they
 // are restaged only when the chunk changes.
 //
@@ -27,9 +28,9 @@ constexpr int KSTEP = 128;
 constexpr int R = STREAM_GROUPED_ROWS;
 constexpr int KSMAX = STREAM_GROUPED_KSMAX;
 
-template <int AF, bool PAIR, int MT, int D, int NW>
+template <int AF, bool PAIR, int MT, int AHEAD, int NW>
 __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
-  static_assert(D == 4, "16-byte scale reads cover four K steps: a 4-deep ring");
+  constexpr int D = 4;  // K steps per group: one 16-byte read of scales covers four steps
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
   constexpr int NTHR = 64 * NW;
@@ -83,23 +84,26 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   };
   set_load_item(i_begin);
 
-  u32x4_t wq[D][NTILE];
-  // 16 scale bytes = the scale dwords of 4 consecutive K steps: the group being
-  // computed and the one being loaded (copied over at each group boundary, so
-  // every register index stays static)
-  u32x4_t sc_cur[NTILE], sc_nxt[NTILE];
-  // Issue the loads of the load cursor's step into ring slot d and advance the
-  // cursor.  Past the last item the loads are kept (so the memory counter
-  // pattern stays fixed) but all lanes read one 16-byte line.
-  auto load_step = [&](int d) {
+  // wq[0] / scg[0]: the group being computed; [1..AHEAD]: groups requested ahead
+  u32x4_t wq[AHEAD + 1][D][NTILE];
+  u32x4_t scg[AHEAD + 1][NTILE];
+  // Request one whole group -- D consecutive K steps of every tile, one burst
+  // of 4 x 64 contiguous bytes per weight row, then its 16 scale bytes -- into
+  // slot `bi` and advance the cursor.  Past the last item the requests are
+  // kept (so the memory counter pattern stays fixed) but all lanes read one
+  // 16-byte line.
+  auto load_group = [&](int bi) {
     const bool live = l_item < i_end;
 #pragma unroll
-    for (int t = 0; t < NTILE; ++t) {
-      const int mat = t / MT;
-      wq[d][t] = buf_load16(wr[mat], live ? woff[t] : 0u, live ? (uint32_t)l_q * 64u : 0u);
-      if (d == 0) sc_nxt[t] = buf_load16(sr[mat], live ? soff[t] : 0u, live ? (uint32_t)l_q * 4u : 0u);
-    }
-    if (++l_q == nks) {
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t)
+        wq[bi][d][t] = buf_load16(wr[t / MT], live ? woff[t] : 0u, live ? (uint32_t)(l_q + d) * 64u : 0u);
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t)
+      scg[bi][t] = buf_load16(sr[t / MT], live ? soff[t] : 0u, live ? (uint32_t)l_q * 4u : 0u);
+    l_q += D;
+    if (l_q == nks) {
       l_q = 0;
       if (++l_item < i_end) set_load_item(l_item);
     }
@@ -228,61 +232,63 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   // Lanes whose token column is >= R read row (r16 % R): those MFMA output
   // columns are never stored.
   const int brow = r16 % R;
+  // one K step from group slot 0
   auto compute = [&](int d, int q) {
-    bf16x8_t bh[4], bl[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
-      bh[j] = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
-      if constexpr (NPL == 2) bl[j] = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
-    }
     float scl[NTILE];
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-      const uint32_t sw = sc_cur[t][d];  // the dword of K step q (= group start + d)
+      const uint32_t sw = scg[0][t][d];  // the scale dword of K step q
       scl[t] = e8m0_to_float((sw >> (8 * kg)) & 0xFFu);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+      bf16x8_t bl;
+      if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
       bf16x8_t wa[NTILE];
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[d][t][j], scl[t]);
+      for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[0][d][t][j], scl[t]);
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh[j], acc[t]);
+      for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh, acc[t]);
       if constexpr (NPL == 2) {
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl[j], accl[t]);
+        for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl, accl[t]);
       }
     }
   };
 
-  // ---- prologue: the first D steps are requested before the first staging
+  // ---- prologue: groups 1..AHEAD are requested before the first staging
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_step(d);
+  for (int i = 1; i <= AHEAD; ++i) load_group(i);
   __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-  for (int t = 0; t < NTILE; ++t) sc_cur[t] = sc_nxt[t];
 
-  // nks is a multiple of D (host guarantee), so every item starts at ring
-  // slot 0 with a fresh scale group
+  // nks is a multiple of D (host guarantee): items are whole groups
   for (; c_item < i_end; ++c_item) {
     begin_item();
     for (c_q = 0; c_q < nks; c_q += D) {
+      // the oldest requested group becomes the computed one (static indices)
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        compute(d, c_q + d);
-        load_step(d);  // refill slot d with the step D ahead
+      for (int i = 0; i < AHEAD; ++i) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+          for (int t = 0; t < NTILE; ++t) wq[i][d][t] = wq[i + 1][d][t];
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) scg[i][t] = scg[i + 1][t];
       }
+      load_group(AHEAD);  // one burst for the group AHEAD groups ahead
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) sc_cur[t] = sc_nxt[t];
+      for (int d = 0; d < D; ++d) compute(d, c_q + d);
     }
     finish_item();
   }
 }
 
+// gate/up: one tile of w1 and one of w3 per wave; down: two tiles of w2 per wave
 template <int AF, bool PAIR>
 void *kernel_ptr() {
-  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, 1, 4, 4>);
+  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, PAIR ? 1 : 2, 2, 4>);
 }
 
 void *select_kernel(int afmt, bool pair) {
@@ -295,7 +301,7 @@ void *select_kernel(int afmt, bool pair) {
 
 }  // namespace
 
-int grouped_stream_rows_per_wg() { return 16 * 4 * 1; }
+int grouped_stream_rows_per_wg(bool pair) { return 16 * 4 * (pair ? 1 : 2); }
 
 bool grouped_stream_fits(int K) {
   const int nks = K / KSTEP;

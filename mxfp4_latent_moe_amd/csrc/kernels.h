@@ -76,7 +76,7 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair);
 GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
 
 int stream_rows_per_wg(int wfmt, bool pair);
-int grouped_stream_rows_per_wg();
+int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
 hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
