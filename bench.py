@@ -1,21 +1,37 @@
 """Benchmark: one forward pass of the Stable LatentMoE layer per step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload decode|prefill] [--no-cpu-baseline]
+    python bench.py --summarize-trace DIR            # rocprofv3 --kernel-trace --stats csv -> text
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR  # two --pmc runs -> traffic summary
 
 A step is one pass of the whole layer (moe_route, moe_permute, gate/up and
 down grouped MXFP4 GEMMs, combine + RMSNorm + up_proj, shared experts) over
 one batch of seeded synthetic tokens at full Kimi K3 shapes; inputs and
-weights are resident in HBM before timing starts.  Prints one JSON line.
+weights are resident in HBM before timing starts.  The steps rotate through
+--layers device copies of the weights (default 4, 64 GB), like consecutive
+layers of the model.  Prints one JSON line.
 
 Fields beyond the headline: `roofline` for the dominant kernel (the gate/up
 grouped GEMM: HBM-bound at decode, MFMA-bound at prefill), its duration taken
 from HIP events recorded on the launch stream around that call in every timed
 step; `cpu_baseline` = the CPU oracle timed on a bounded sample of the same
-workload on this host; `secondary` = the prefill (T=4096) line.
+workload on this host; `secondary` = the prefill (T=4096) line; `cold_cache`
+= the same layer timed with a 512 MiB write before every step, so that no
+weight is served from the 256 MB last-level cache.
+
+`roofline.traffic` is the HBM traffic of one launch of the dominant kernel as
+read by the FETCH_SIZE and WRITE_SIZE counters (two rocprofv3 --pmc runs of
+this script with --calibrate-copy), each scaled by what the same counter reads
+for a plain copy of known size in the same run.  It is taken from the text
+summary under profiles/ and reported only while the kernel's sources still
+hash to the value recorded there.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +44,43 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FLUSH_BYTES = 512 << 20         # > the 256 MB last-level (MALL) cache
+COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
+
+# Sources of the decode gate/up kernel: the traffic figure is valid only for them.
+DECODE_GATEUP_SOURCES = ["mxfp4_latent_moe_amd/csrc/grouped_stream.hip", "mxfp4_latent_moe_amd/csrc/common.h",
+                         "mxfp4_latent_moe_amd/csrc/kernels.h"]
+DECODE_GATEUP_KERNEL = "grouped_stream_kernel<1, true"
+PMC_SUMMARY = "profiles/grouped_gemm_gateup_decode_T16_traffic.txt"
+
+
+def sources_sha256(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_summary(path) -> dict:
+    out = {}
+    full = os.path.join(ROOT, path)
+    if not os.path.exists(full):
+        return out
+    for line in open(full):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode gate/up kernel from the committed
+    counter summary, or None when the kernel changed since it was taken."""
+    d = read_summary(PMC_SUMMARY)
+    if not d or d.get("source_sha256") != sources_sha256(DECODE_GATEUP_SOURCES):
+        return None
+    return int(float(d["traffic_bytes_per_launch"]))
 
 
 def _expert_gateup_bytes(sh) -> int:
@@ -39,32 +92,143 @@ def _expert_bytes(sh) -> int:
     return _expert_gateup_bytes(sh) + sh.latent * sh.inter // 2 + sh.latent * sh.inter // 32
 
 
-def run_workload(mx, torch, synth, w, wl, steps, warmup):
+def _pct(v, q):
+    return round(float(np.percentile(np.asarray(v), q)), 4)
+
+
+def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0):
+    """Step i runs layer i % len(layers): consecutive steps read different
+    weight copies, as consecutive layers of the model do, so no step finds the
+    previous step's weights in the last-level cache."""
     from synth.device import upload_tokens
     dev = torch.device("cuda:0")
     sh = wl.shape
-    moe = mx.LatentMoE(mx.shape_of(sh), w, dev)
+    moes = [mx.LatentMoE(mx.shape_of(sh), w, dev) for w in layers]
     x = upload_tokens(wl, dev)
-    for _ in range(warmup):
-        moe.forward(x)
+    for i in range(warmup):
+        moes[i % len(moes)].forward(x)
     torch.cuda.synchronize()
     marks_all = []
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         marks = []
-        moe.forward(x, marks=marks)
+        moes[i % len(moes)].forward(x, marks=marks)
         marks_all.append(marks)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-call durations from the events recorded on the launch stream
     names = [n for n, _ in marks_all[0][1:]]
     per_call = {n: 0.0 for n in names}
+    spans = []
     for marks in marks_all:
         for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
             per_call[n1] += e0.elapsed_time(e1) / steps
-    b = moe.buffers(wl.tokens)
+        spans.append(marks[0][1].elapsed_time(marks[-1][1]))
+    b = moes[0].buffers(wl.tokens)
     e_act = int(b["active"][0].item())
-    return {"wall_s": wall, "per_call_ms": per_call, "e_act": e_act, "T": wl.tokens}
+    r = {"wall_s": wall, "per_call_ms": per_call, "e_act": e_act, "T": wl.tokens,
+         "step_ms": {"median": _pct(spans, 50), "p10": _pct(spans, 10), "p90": _pct(spans, 90)}}
+    if cold_steps > 0:
+        # every step after a write of FLUSH_BYTES: nothing is left in the last-level cache
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        cold = []
+        for i in range(cold_steps):
+            scratch.fill_(float(i))
+            marks = []
+            moes[0].forward(x, marks=marks)
+            cold.append(marks)
+        torch.cuda.synchronize()
+        cspans = [m[0][1].elapsed_time(m[-1][1]) for m in cold]
+        r["cold_cache"] = {"flush_bytes": FLUSH_BYTES, "steps": cold_steps, "median_ms": _pct(cspans, 50),
+                           "p10_ms": _pct(cspans, 10), "p90_ms": _pct(cspans, 90),
+                           "tokens_per_s": round(wl.tokens / (float(np.median(cspans)) * 1e-3), 1)}
+        del scratch
+    return r
+
+
+def calibration_copy(torch):
+    """A plain elementwise copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES),
+    run three times so the counters of a known-size transfer sit beside the
+    layer's kernels in the same profile."""
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _short(name: str) -> str:
+    return name.replace("moe::(anonymous namespace)::", "").replace("(moe::GemmArgs)", "").replace("void ", "")
+
+
+def summarize_trace(d):
+    """Kernel-trace --stats csv of one rocprofv3 run -> short text table."""
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        sys.exit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    print(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in rows:
+        print(f"{_short(r['Name'])[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+              f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+
+
+def _pmc_per_kernel(d, counter):
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not f:
+        sys.exit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for r in csv.DictReader(open(f[0])):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) -> traffic summary.
+    The scale of each counter is the copy's known byte count over what the
+    counter read for it."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(acc, key):
+        ks = [k for k in acc if key in k]
+        if not ks:
+            sys.exit(f"no dispatch of {key!r}")
+        v = [x for k in ks for x in acc[k]]
+        return sum(v) / len(v), len(v)
+
+    copy_key = "elementwise"  # torch's mul kernel (the calibration copy)
+    cf = [v for k in fetch if copy_key in k for v in fetch[k] if v * 1024 > COPY_BYTES / 4]
+    cw = [v for k in write if copy_key in k for v in write[k] if v * 1024 > COPY_BYTES / 4]
+    if not cf or not cw:
+        sys.exit("calibration copy not found (run bench.py with --calibrate-copy)")
+    f_scale = COPY_BYTES / (1024.0 * sum(cf) / len(cf))
+    w_scale = COPY_BYTES / (1024.0 * sum(cw) / len(cw))
+    kf, nf = pick(fetch, DECODE_GATEUP_KERNEL)
+    kw, nw = pick(write, DECODE_GATEUP_KERNEL)
+    traffic = kf * 1024 * f_scale + kw * 1024 * w_scale
+    print("# HBM traffic of the decode gate/up grouped GEMM kernel (T=16, full K3 shapes)")
+    print("# made by:")
+    print("#   cd /tmp && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -o run -- "
+          "python3 <repo>/bench.py --steps 3 --warmup 1 --no-secondary --no-cpu-baseline --calibrate-copy")
+    print("#   cd /tmp && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -o run -- "
+          "python3 <repo>/bench.py --steps 3 --warmup 1 --no-secondary --no-cpu-baseline --calibrate-copy")
+    print("#   python3 bench.py --summarize-pmc <F> <W>")
+    print(f"kernel: {DECODE_GATEUP_KERNEL}, 1, 2, 4>")
+    print(f"source_sha256: {sources_sha256(DECODE_GATEUP_SOURCES)}")
+    print(f"copy_bytes: {COPY_BYTES}")
+    print(f"copy_fetch_kib_per_dispatch: {sum(cf) / len(cf):.1f}")
+    print(f"copy_write_kib_per_dispatch: {sum(cw) / len(cw):.1f}")
+    print(f"fetch_scale: {f_scale:.4f}")
+    print(f"write_scale: {w_scale:.4f}")
+    print(f"kernel_fetch_kib_per_dispatch: {kf:.1f}  (n={nf})")
+    print(f"kernel_write_kib_per_dispatch: {kw:.1f}  (n={nw})")
+    print(f"traffic_bytes_per_launch: {traffic:.0f}")
 
 
 def cpu_baseline(synth, wl, n_tokens):
@@ -103,7 +267,20 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="weight copies the steps rotate through (16 GB each at full shape)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps of one layer timed after a cache flush (0: none)")
+    ap.add_argument("--calibrate-copy", action="store_true", help="run a known-size copy for counter scaling")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU expert parallelism "
               "is not part of this build", file=sys.stderr)
@@ -119,9 +296,10 @@ def main():
     wl = synth.workload(args.workload)
     sh = wl.shape
     w = upload_weights(wl, torch.device("cuda:0"))
+    layers = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(max(1, args.layers) - 1)]
     torch.cuda.synchronize()
     print("bench: timing", wl.name, file=sys.stderr, flush=True)
-    r = run_workload(mx, torch, synth, w, wl, args.steps, args.warmup)
+    r = run_workload(mx, torch, synth, layers, wl, args.steps, args.warmup, args.cold_steps)
     ms = 1e3 * r["wall_s"] / args.steps
     value = wl.tokens * args.steps / r["wall_s"]
 
@@ -133,7 +311,7 @@ def main():
         traffic = r["e_act"] * _expert_gateup_bytes(sh) + wl.tokens * sh.latent * 4 + P * sh.inter * 4
         achieved = traffic / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "mxfp4_grouped_gemm gate/up (+SiTU-GLU)", "algorithmic_bytes": int(traffic),
                 "avg_ms": round(gu_ms, 4), "active_experts": r["e_act"]}
     else:
@@ -165,10 +343,14 @@ def main():
             "operands": "MXFP4 expert weights (checkpoint bytes), bf16 dense weights, "
                         "bf16 hi+lo split activations, fp32 accumulate, fp32 output",
             "parallelism": "single GPU",
+            "layers_rotated": len(layers),
         },
         "per_call_ms": {k: round(v, 4) for k, v in r["per_call_ms"].items()},
+        "step_ms": r["step_ms"],
         "roofline": roof,
     }
+    if "cold_cache" in r:
+        line["cold_cache"] = r["cold_cache"]
     if args.workload == "decode":
         line["expert_weight_bytes_per_step"] = r["e_act"] * _expert_bytes(sh)
         line["expert_hbm_frac_layer"] = round(
@@ -177,7 +359,7 @@ def main():
     if not args.no_secondary and args.workload == "decode":
         pf = synth.workload("prefill")
         print("bench: timing prefill", file=sys.stderr, flush=True)
-        rp = run_workload(mx, torch, synth, w, pf, max(2, args.steps // 5), 2)
+        rp = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2)
         pms = 1e3 * rp["wall_s"] / max(2, args.steps // 5)
         layer_flops = 2.0 * pf.tokens * (sh.top_k * 3 * sh.latent * sh.inter + sh.n_experts * sh.hidden
                                          + 2 * sh.latent * sh.hidden
@@ -194,6 +376,8 @@ def main():
             "per_call_ms": {k: round(v, 4) for k, v in rp["per_call_ms"].items()},
         }
 
+    if args.calibrate_copy:
+        calibration_copy(torch)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(synth, wl, 8 if args.workload == "decode" else 4)

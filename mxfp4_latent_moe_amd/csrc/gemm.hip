@@ -416,7 +416,7 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
   if (avg < 2.0 && grouped_stream_fits(K)) {
     p.variant = 2;
     p.nt = 1;
-    p.chunk_rows = STREAM_GROUPED_ROWS;
+    p.chunk_rows = PERSIST_ROWS;
     p.mt = 1;
     p.n_blocks = ceil_div(N, grouped_stream_rows_per_wg(pair));
     p.splits = 1;

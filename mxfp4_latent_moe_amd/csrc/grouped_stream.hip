@@ -1,15 +1,15 @@
 // Persistent streaming MXFP4 grouped GEMM for decode-sized expert segments.
 //
-// Work item = (row chunk of <= R sorted rows of one expert, block of weight
-// rows).  The grid holds one resident wave of work-groups; work-group w takes
-// the contiguous item range [w*n/G, (w+1)*n/G) of the n items that exist on
-// the device (n is read from the chunk list, so nothing waits on the host).
-// Within a work-group the weight stream never stops: every wave walks the K
-// steps of its rows item after item.  Weights are requested a group of four
-// K steps at a time (256 contiguous bytes per row in one burst, which keeps
-// DRAM pages open), two groups ahead of the MFMAs, across item boundaries.  The
-// token rows of the current chunk (bf16, or bf16 hi + lo) sit in LDS; they
-// are restaged only when the chunk changes.
+// Work item = (row chunk of <= R = 4 sorted rows of one expert, block of
+// weight rows).  The grid holds one resident wave of work-groups; work-group
+// w takes the contiguous item range [w*n/G, (w+1)*n/G) of the n items that
+// exist on the device (n is read from the chunk list, so nothing waits on the
+// host).  Within a work-group the weight stream never stops: every wave walks
+// the K steps of its rows item after item.  Weights are requested a group of
+// four K steps at a time (256 contiguous bytes per row in one burst, which
+// keeps DRAM pages open), two groups ahead of the MFMAs, across item
+// boundaries.  The token rows of the current chunk (bf16, or bf16 hi + lo) sit
+// in LDS; they are restaged only when the chunk changes.
 //
 // Per K step (128 K values) a lane holds one 16-byte slice of one weight row
 // (32 e2m1 codes = one scale group), converted in registers with the scaled
@@ -25,7 +25,7 @@ namespace moe {
 namespace {
 
 constexpr int KSTEP = 128;
-constexpr int R = STREAM_GROUPED_ROWS;
+constexpr int R = PERSIST_ROWS;
 constexpr int KSMAX = STREAM_GROUPED_KSMAX;
 
 template <int AF, bool PAIR, int MT, int AHEAD, int NW>

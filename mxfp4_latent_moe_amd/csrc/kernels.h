@@ -57,6 +57,8 @@ constexpr int STREAM_KSMAX = 8;
 // (the whole K of the K3 expert matrices: 3584 / 128 = 28).
 constexpr int STREAM_GROUPED_ROWS = 2;
 constexpr int STREAM_GROUPED_KSMAX = 32;
+// persistent grouped kernel: rows per chunk (decode segments rarely exceed 4)
+constexpr int PERSIST_ROWS = 4;
 
 // kernel variant selection (host side)
 struct GemmPlan {
