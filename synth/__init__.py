@@ -15,6 +15,7 @@ from .inputs import (  # noqa: F401
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     gen_dense,
+    gen_gamma_random,
     gen_expert,
     gen_expert_stack,
     gen_tokens,

@@ -33,6 +33,7 @@ T_X, T_ROUTER, T_BIAS, T_DOWN, T_UP = 1, 2, 3, 4, 5
 T_SH_GATE, T_SH_UP, T_SH_DOWN = 6, 7, 8
 T_W1P, T_W1S, T_W3P, T_W3S, T_W2P, T_W2S = 10, 11, 12, 13, 14, 15
 T_ZIPF_PERM, T_MB_COUNTS, T_MB_A = 20, 21, 22
+T_GAMMA = 23
 _WSET_DOMAIN = 1000
 
 
@@ -174,6 +175,13 @@ def gen_dense(wl: Workload) -> dict:
         down[:, i * Is:(i + 1) * Is] = _normal_bf16(_stream(d, T_SH_DOWN, i), (H, Is), Is ** -0.5, chunk_rows=512)
     out["sh_gate"], out["sh_up"], out["sh_down"] = gate, up, down
     return out
+
+
+def gen_gamma_random(wl: Workload, std: float = 0.1) -> np.ndarray:
+    """A non-trivial RMSNorm weight for diagnostics: bf16 bits of 1 + N(0, std), [L]."""
+    ss = _stream(_WSET_DOMAIN + wl.wset, T_GAMMA)
+    v = 1.0 + std * _rng(ss).standard_normal(wl.shape.latent)
+    return f32_to_bf16_bits(v.astype(np.float32))
 
 
 def gen_bias(wl: Workload, zipf_bias_path: str | None = None) -> np.ndarray:

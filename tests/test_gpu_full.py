@@ -135,3 +135,38 @@ def test_microbench_grouped_gemm(mx, k3):
         errs.append(rel_max_err(Yg, Yr))
     say(f"microbench: max|gpu-oracle|/rms on Y over sampled rows = {max(errs):.3e}")
     assert max(errs) <= TOL
+
+
+def test_expert_slice_partition_invariance(mx, k3):
+    """One GPU's share under expert parallelism: the grouped GEMMs run over a
+    contiguous 112-expert slice (weights, offsets and rows of that slice only)
+    give bit-identical H and Y rows to the full 896-expert call."""
+    from mxfp4_latent_moe_amd import ops
+    wl = synth.workload("decode")
+    sh = wl.shape
+    say("case: decode layer, then each of the 8 expert slices of 112 experts")
+    g = _run_layer(mx, k3, wl)
+    w = k3["w"]
+    offsets = g["offsets"]
+    n_slice = sh.n_experts // 8
+    for e0 in range(0, sh.n_experts, n_slice):
+        r0, r1 = int(offsets[e0]), int(offsets[e0 + n_slice])
+        if r1 == r0:
+            continue
+        sub = synth.LayerShape(sh.hidden, sh.latent, n_slice, sh.top_k, sh.inter, sh.n_shared, sh.shared_inter)
+        s = mx.shape_of(sub)
+        P = r1 - r0
+        off = to_dev((offsets[e0:e0 + n_slice + 1] - r0).astype(np.int32), DEV)
+        sp = to_dev(g["sorted_pair"][r0:r1].astype(np.int32), DEV)
+        z = to_dev(g["z"], DEV)
+        ws = torch.empty(ops.workspace_bytes(s, ops.MOE_FN_GROUPED_GEMM, P), dtype=torch.uint8, device=DEV)
+        H = torch.empty((P, sh.inter), dtype=torch.float32, device=DEV)
+        Y = torch.empty((P, sh.latent), dtype=torch.float32, device=DEV)
+        sl = slice(e0, e0 + n_slice)
+        ops.grouped_gemm(s, ops.MOE_OP_GATEUP_SITU, P, off, sp, z, w["w1_packed"][sl], w["w1_scale"][sl],
+                         w["w3_packed"][sl], w["w3_scale"][sl], None, H, ws)
+        ops.grouped_gemm(s, ops.MOE_OP_DOWN, P, off, sp, H, w["w2_packed"][sl], w["w2_scale"][sl], None, None,
+                         None, Y, ws)
+        torch.cuda.synchronize()
+        assert (H.cpu().numpy() == g["H"][r0:r1]).all(), e0
+        assert (Y.cpu().numpy() == g["Y"][r0:r1]).all(), e0

@@ -158,3 +158,49 @@ def test_tiny_ragged_tokens_and_ties(mx):
     ids = got["topk_ids"].cpu().numpy()
     assert (ids == np.array([3, 7, 9, 20])).all()
     np.testing.assert_allclose(got["topk_w"].cpu().numpy(), 0.25, rtol=1e-6)
+
+
+def test_tiny_random_gamma(mx):
+    """A non-trivial RMSNorm weight (1 + N(0, 0.1)) reaches the output through the combine."""
+    wl, x_bits, d, b, st = _tiny_setup()
+    say("case: tiny layer with gamma = 1 + N(0, 0.1)")
+    d = dict(d)
+    d["gamma"] = synth.gen_gamma_random(wl)
+    w = upload_weights(wl, DEV)
+    w["gamma"] = to_dev_bf16(d["gamma"], DEV)
+    layer_ = mx.LatentMoE(mx.shape_of(wl.shape), w, DEV)
+    out = layer_.forward(to_dev_bf16(x_bits, DEV))["out"].cpu().numpy()
+    ref = _oracle(wl, x_bits, d, b, st)
+    unit = _oracle(wl, x_bits, _tiny_setup()[2], b, st)
+    assert rel_max_err(ref["out"], unit["out"]) > 1e-3  # gamma matters
+    assert rel_max_err(out, ref["out"]) < 1e-4
+
+
+def test_tiny_graph_capture_replays(mx):
+    """The six calls enqueue only kernels (no allocation, memset or host wait), so the
+    layer can be captured in a HIP graph; every replay must equal the eager result."""
+    wl, x_bits, d, b, st = _tiny_setup()
+    say("case: tiny layer captured in a HIP graph, 3 replays")
+    w = upload_weights(wl, DEV)
+    x = to_dev_bf16(x_bits, DEV)
+    layer_ = mx.LatentMoE(mx.shape_of(wl.shape), w, DEV)
+    eager = {k: v.clone() for k, v in layer_.forward(x).items() if k != "ws"}
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer_.forward(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        bufs = layer_.forward(x)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for k in ("out", "H", "Y", "topk_ids"):
+            bufs[k].zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("topk_ids", "topk_w", "z", "H", "Y", "out"):
+            assert torch.equal(bufs[k], eager[k]), (i, k)
