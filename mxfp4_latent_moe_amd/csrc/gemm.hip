@@ -427,6 +427,14 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
     p.mt = stream_rows_per_wg(W_MXFP4, pair) / 64;
     p.n_blocks = ceil_div(N, stream_rows_per_wg(W_MXFP4, pair));
     p.splits = ceil_div(ksteps, STREAM_GROUPED_KSMAX);
+  } else if ((long long)P * K * 4 < (1LL << 31)) {
+    // activation offsets fit the 32-bit buffer addressing of the prefill kernel
+    p.variant = 3;
+    p.nt = PREFILL_NT;
+    p.chunk_rows = 16 * PREFILL_NT;
+    p.mt = prefill_rows_per_wg(pair) / 64;
+    p.n_blocks = ceil_div(N, prefill_rows_per_wg(pair));
+    p.splits = 1;
   } else {
     p.variant = 0;
     p.nt = 8;
@@ -445,6 +453,7 @@ hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const 
                        hipStream_t st) {
   const long long grid = (pl.grid_logical + 7) / 8 * 8;
   if (pl.variant == 2) return launch_grouped_stream(afmt, pair, a, st);
+  if (pl.variant == 3) return launch_prefill_gemm(afmt, pair, a, grid, st);
   if (pl.variant == 1) return launch_stream_gemm(wfmt, afmt, pair, a, grid, st);
   if (wfmt == W_MXFP4) return launch_af<W_MXFP4>(pl, afmt, pair, a, grid, st);
   return launch_af<W_BF16>(pl, afmt, pair, a, grid, st);

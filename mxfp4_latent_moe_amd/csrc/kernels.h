@@ -59,11 +59,15 @@ constexpr int STREAM_GROUPED_ROWS = 2;
 constexpr int STREAM_GROUPED_KSMAX = 32;
 // persistent grouped kernel: rows per chunk (decode segments rarely exceed 4)
 constexpr int PERSIST_ROWS = 4;
+// tiled prefill kernel: 16-token tiles per chunk, 16-row weight tiles per wave
+constexpr int PREFILL_NT = 6;
+constexpr int PREFILL_MT_PAIR = 4;
+constexpr int PREFILL_MT_SINGLE = 8;
 
 // kernel variant selection (host side)
 struct GemmPlan {
   int variant;   // 0: tiled (LDS-staged K steps), 1: streaming (<= 16-row chunks),
-                 // 2: persistent streaming over expert row chunks
+                 // 2: persistent streaming over expert row chunks, 3: tiled prefill
   int nt;        // 16-token tiles per chunk (1 or 8)
   int mt;        // 16-row weight tiles per wave and matrix
   int chunk_rows;
@@ -81,6 +85,8 @@ int stream_rows_per_wg(int wfmt, bool pair);
 int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
 hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st);
+int prefill_rows_per_wg(bool pair);
+hipError_t launch_prefill_gemm(int afmt, bool pair, const GemmArgs &a, long long grid, hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                               hipStream_t st);
 
