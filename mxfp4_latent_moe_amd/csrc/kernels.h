@@ -60,9 +60,11 @@ constexpr int STREAM_GROUPED_KSMAX = 32;
 // persistent grouped kernel: rows per chunk (decode segments rarely exceed 4)
 constexpr int PERSIST_ROWS = 4;
 // tiled prefill kernel: 16-token tiles per chunk, 16-row weight tiles per wave
+// and matrix, waves per work-group
 constexpr int PREFILL_NT = 6;
-constexpr int PREFILL_MT_PAIR = 4;
-constexpr int PREFILL_MT_SINGLE = 8;
+constexpr int PREFILL_MT_PAIR = 2;
+constexpr int PREFILL_MT_SINGLE = 4;
+constexpr int PREFILL_NW = 8;
 
 // kernel variant selection (host side)
 struct GemmPlan {

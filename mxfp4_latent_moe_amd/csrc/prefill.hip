@@ -15,7 +15,9 @@
 //    octet-wise writes and the token-wise fragment reads free of bank
 //    conflicts;
 //  * one barrier per step.
-// Token tiles past the chunk's last row are skipped (wave-uniform branch).
+// The item body is specialised on the number of active 16-token tiles, so the
+// K loop is straight-line code and token tiles past the chunk's last row cost
+// nothing.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,32 +26,26 @@ namespace {
 
 constexpr int KSTEP = 128;
 
-template <int AF, bool PAIR, int NT, int MT>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
+// One work item with NTA active 16-token tiles (the K loop has no branches).
+template <int AF, bool PAIR, int NTA, int MT, int NW>
+__device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int expert, int row0,
+                                        int nrows, int nb) {
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;  // LDS planes (hi, lo)
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;                  // 16-row weight tiles per wave
-  constexpr int CT = 16 * NT;                       // tokens per chunk
-  constexpr int ROWS_WG = 64 * MT;                  // weight rows per matrix per work-group
+  constexpr int CT = 16 * NTA;                      // staged tokens
+  constexpr int ROWS_WG = 16 * NW * MT;             // weight rows per matrix per work-group
   constexpr int PLANE = CT * KSTEP;                 // bf16 elements per plane per stage
   constexpr int AW = (AF == A_BF16) ? 1 : 2;        // 16-byte loads per staged octet
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][NPL][PLANE];
+  constexpr int RPP = 4 * NW;                       // token rows staged per pass (16 threads a row)
+  constexpr int NPASS = (CT + RPP - 1) / RPP;       // staging passes per K step
+  auto lds = [&](int b, int p) { return lds_base + (b * NPL + p) * PLANE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int kg = lane >> 4;
   const int r16 = lane & 15;
-
-  // ---- work item (XCD-aware over the items that exist on the device)
-  const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
-  const int logical = xcd_logical(total);
-  if (logical < 0) return;
-  const int chunk = logical / g.n_blocks;
-  const int nb = logical - chunk * g.n_blocks;
-  const int4 cinfo = reinterpret_cast<const int4 *>(g.chunks)[chunk];
-  const int expert = cinfo.x, row0 = cinfo.y, nrows = cinfo.z;
-  const int nta = (nrows + 15) >> 4;  // active token tiles
   const int N = g.N, K = g.K;
   const int nks = K / KSTEP;
 
@@ -72,15 +68,15 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
     soff[t] = (uint32_t)n * srow_bytes;
   }
 
-  // ---- activation rows this thread stages: token (tid >> 4) + 16 i, octet tid & 15
+  // ---- activation rows this thread stages: token (tid >> 4) + RPP i, octet tid & 15
   const int a_oct = tid & 15;
   const int esz = (AF == A_BF16) ? 2 : 4;
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.A, 0x7FFFFFF0u);
-  uint32_t aoff[NT];
-  bool alive[NT];
+  uint32_t aoff[NPASS];
+  bool alive[NPASS];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int r = (tid >> 4) + 16 * i;
+  for (int i = 0; i < NPASS; ++i) {
+    const int r = (tid >> 4) + RPP * i;
     alive[i] = r < nrows;
     const int p = row0 + min(r, nrows - 1);
     const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
@@ -89,9 +85,11 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
 
   u32x4_t wq[2][NTILE];
   uint32_t wsc[2][NTILE];
-  u32x4_t aq[NT][AW];
+  u32x4_t aq[NPASS][AW];
 
+  // loads past the last K step re-read the last one (never past the rows)
   auto load_w = [&](int b, int s) {
+    s = min(s, nks - 1);
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
@@ -99,9 +97,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
     }
   };
   auto load_a = [&](int s) {
+    s = min(s, nks - 1);
     const uint32_t so = (uint32_t)s * KSTEP * esz;
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
+    for (int i = 0; i < NPASS; ++i) {
 #pragma unroll
       for (int h = 0; h < AW; ++h) aq[i][h] = buf_load16(ar, aoff[i] + 16 * h, so);
     }
@@ -110,12 +109,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
   auto slot = [](int oct, int tok) { return (oct * CT + (tok ^ oct)) * 8; };
   auto store_a = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int r = (tid >> 4) + 16 * i;
+    for (int i = 0; i < NPASS; ++i) {
+      const int r = (tid >> 4) + RPP * i;
+      if (CT % RPP != 0 && r >= CT) continue;
       const int off = slot(a_oct, r);
       if constexpr (AF == A_BF16) {
         const u32x4_t v = alive[i] ? aq[i][0] : u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t *>(&lds[b][0][off]) = v;
+        *reinterpret_cast<u32x4_t *>(lds(b, 0) + off) = v;
       } else {
         bf16x8_t hi, lo;
 #pragma unroll
@@ -130,69 +130,79 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
             hi[e] = to_bf16(f);
           }
         }
-        *reinterpret_cast<bf16x8_t *>(&lds[b][0][off]) = hi;
-        if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[b][NPL - 1][off]) = lo;
+        *reinterpret_cast<bf16x8_t *>(lds(b, 0) + off) = hi;
+        if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(lds(b, NPL - 1) + off) = lo;
       }
     }
   };
 
-  f32x4_t acc[NTILE][NT];
+  f32x4_t acc[NTILE][NTA];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NTA; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Fragments f = (sub-step j, plane p, token tile n) in order; each B fragment
+  // is read from LDS two fragments ahead of its MFMAs, and the weights of
+  // sub-step j+1 are converted while sub-step j's MFMAs run.
   auto compute = [&](int b) {
     float scl[NTILE];
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[b][t] >> (8 * kg)) & 0xFFu);
+    constexpr int FJ = NPL * NTA;  // fragments per sub-step
+    constexpr int F = 4 * FJ;      // fragments per K step
+    constexpr int D = 2;           // read-ahead distance
+    auto rd = [&](int f) {
+      const int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
+      return *reinterpret_cast<const bf16x8_t *>(lds(b, p) + slot(4 * kg + j, 16 * n + r16));
+    };
+    bf16x8_t bq[D + 1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int oct = 4 * kg + j;
-      bf16x8_t wa[NTILE];
+    for (int f = 0; f < D; ++f) bq[f] = rd(f);
+    bf16x8_t wa[2][NTILE];
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[b][t][j], scl[t]);
+    for (int t = 0; t < NTILE; ++t) wa[0][t] = fp4x8_to_bf16(wq[b][t][0], scl[t]);
 #pragma unroll
-      for (int p = 0; p < NPL; ++p) {
+    for (int f = 0; f < F; ++f) {
+      const int j = f / FJ, n = f % NTA;
+      if (f + D < F) bq[(f + D) % (D + 1)] = rd(f + D);
+      if (f % FJ == 0 && j + 1 < 4) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (n < nta) {
-            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(&lds[b][p][slot(oct, 16 * n + r16)]);
-#pragma unroll
-            for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[t], bv, acc[t][n]);
-          }
-        }
+        for (int t = 0; t < NTILE; ++t) wa[(j + 1) & 1][t] = fp4x8_to_bf16(wq[b][t][j + 1], scl[t]);
       }
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bq[f % (D + 1)], acc[t][n]);
     }
+    // let the scheduler interleave the LDS reads with the MFMAs of this region
+    __builtin_amdgcn_iglp_opt(0);
+  };
+  // one K step: activations of s+1 and weights of s+2 are requested while s computes
+  auto step = [&](int h, int s) {
+    load_a(s + 1);
+    compute(h);
+    load_w(h, s + 2);
+    store_a(h ^ 1);
+    __syncthreads();
   };
 
-  // ---- pipeline: step s computes from LDS stage s&1 and weight buffer s&1;
-  // activations of step s+1 and weights of step s+2 are in flight meanwhile.
   load_w(0, 0);
   load_a(0);
-  if (nks > 1) load_w(1, 1);
+  load_w(1, 1);
   store_a(0);
   __syncthreads();
-  for (int s = 0; s < nks; s += 2) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ss = s + h;
-      if (ss < nks) {
-        if (ss + 1 < nks) load_a(ss + 1);
-        compute(h);
-        if (ss + 2 < nks) load_w(h, ss + 2);
-        if (ss + 1 < nks) store_a(h ^ 1);
-        __syncthreads();
-      }
-    }
+  int s = 0;
+  for (; s + 1 < nks; s += 2) {
+    step(0, s);
+    step(1, s + 1);
   }
+  if (s < nks) step(0, s);
 
   // ---- epilogue: SiTU-GLU of the gate/up pair (or the plain product), row scale, store
   const int col_base = wrow_base + 4 * kg;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  for (int n = 0; n < NTA; ++n) {
     const int tok = 16 * n + r16;
-    if (n < nta && tok < nrows) {
+    if (tok < nrows) {
       const long long orow = row0 + tok;
       float rs = 1.f;
       if (g.rscale != nullptr) rs = g.rscale[g.rscale_map ? g.rscale_map[orow] : orow];
@@ -218,16 +228,44 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(GemmArgs g) {
   }
 }
 
+template <int AF, bool PAIR, int NT, int MT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(GemmArgs g) {
+  constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * NPL * 16 * NT * KSTEP];
+  static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
+
+  // ---- work item (XCD-aware over the items that exist on the device)
+  const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
+  const int logical = xcd_logical(total);
+  if (logical < 0) return;
+  const int chunk = logical / g.n_blocks;
+  const int nb = logical - chunk * g.n_blocks;
+  const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
+  const int nta = min((c.z + 15) >> 4, NT);  // active 16-token tiles (chunks hold <= 16*NT rows)
+  if (nta == NT) {
+    pf_item<AF, PAIR, NT, MT, NW>(g, lds, c.x, c.y, c.z, nb);
+    return;
+  }
+  switch (nta) {
+    case 1: if constexpr (NT > 1) pf_item<AF, PAIR, 1, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+    case 2: if constexpr (NT > 2) pf_item<AF, PAIR, 2, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+    case 3: if constexpr (NT > 3) pf_item<AF, PAIR, 3, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+    case 4: if constexpr (NT > 4) pf_item<AF, PAIR, 4, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+    default: if constexpr (NT > 5) pf_item<AF, PAIR, 5, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+  }
+}
+
 template <int AF, bool PAIR>
 hipError_t launch_pf(const GemmArgs &a, long long grid, hipStream_t st) {
   constexpr int MT = PAIR ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE;
-  hipLaunchKernelGGL((prefill_kernel<AF, PAIR, PREFILL_NT, MT>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<AF, PAIR, PREFILL_NT, MT, PREFILL_NW>), dim3((unsigned)grid),
+                     dim3(64 * PREFILL_NW), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_rows_per_wg(bool pair) { return 64 * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
+int prefill_rows_per_wg(bool pair) { return 16 * PREFILL_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
 
 hipError_t launch_prefill_gemm(int afmt, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
   switch (afmt) {
