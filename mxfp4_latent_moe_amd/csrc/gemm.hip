@@ -391,6 +391,16 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair) {
     while (items * splits < 2048 && ceil_div(ksteps, splits * 2) >= 2) splits *= 2;
     p.splits = splits;
     p.grid_logical = items * splits;
+  } else if (rows >= 1024 && (long long)rows * K * 4 < (1LL << 31)) {
+    // enough row chunks to fill the chip without splitting K
+    p.variant = 3;
+    p.nt = PREFILL_NT;
+    p.chunk_rows = 16 * PREFILL_NT;
+    p.mt = prefill_rows_per_wg(pair) / 64;
+    p.n_blocks = ceil_div(N, prefill_rows_per_wg(pair));
+    p.max_chunks = ceil_div(rows, p.chunk_rows);
+    p.splits = 1;
+    p.grid_logical = (long long)p.max_chunks * p.n_blocks;
   } else {
     p.variant = 0;
     p.nt = 8;
@@ -453,7 +463,7 @@ hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const 
                        hipStream_t st) {
   const long long grid = (pl.grid_logical + 7) / 8 * 8;
   if (pl.variant == 2) return launch_grouped_stream(afmt, pair, a, st);
-  if (pl.variant == 3) return launch_prefill_gemm(afmt, pair, a, grid, st);
+  if (pl.variant == 3) return launch_prefill_gemm(wfmt, afmt, pair, a, grid, st);
   if (pl.variant == 1) return launch_stream_gemm(wfmt, afmt, pair, a, grid, st);
   if (wfmt == W_MXFP4) return launch_af<W_MXFP4>(pl, afmt, pair, a, grid, st);
   return launch_af<W_BF16>(pl, afmt, pair, a, grid, st);

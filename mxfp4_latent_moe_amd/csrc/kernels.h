@@ -88,7 +88,8 @@ int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
 hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st);
 int prefill_rows_per_wg(bool pair);
-hipError_t launch_prefill_gemm(int afmt, bool pair, const GemmArgs &a, long long grid, hipStream_t st);
+hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
+                               hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                               hipStream_t st);
 

@@ -1,4 +1,5 @@
-// Tiled MXFP4 grouped GEMM for prefill-sized expert segments.
+// Tiled GEMM for prefill-sized work: MXFP4 expert segments (grouped) and the
+// bf16 dense products of the layer.
 //
 // Work item = (chunk of <= 16*NT expert-sorted token rows of one expert,
 // block of 64*MT weight rows).  Weight rows are the MFMA's M side, tokens its
@@ -27,7 +28,7 @@ namespace {
 constexpr int KSTEP = 128;
 
 // One work item with NTA active 16-token tiles (the K loop has no branches).
-template <int AF, bool PAIR, int NTA, int MT, int NW>
+template <int WF, int AF, bool PAIR, int NTA, int MT, int NW>
 __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int expert, int row0,
                                         int nrows, int nb) {
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;  // LDS planes (hi, lo)
@@ -49,22 +50,24 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   const int N = g.N, K = g.K;
   const int nks = K / KSTEP;
 
-  // ---- weight rows of this wave: buffer resources per matrix, offsets per tile
-  const uint32_t row_bytes = K / 2, srow_bytes = K / 32;
+  // ---- weight rows of this wave: buffer resources per matrix, offsets per tile.
+  // MXFP4: lane group kg's 16 bytes of a 128-wide K step are its 32 codes (one
+  // scale group); bf16: its 64 bytes (32 values), one 16-byte load per sub-step.
+  constexpr bool FP4 = WF == W_MXFP4;
+  const uint32_t row_bytes = FP4 ? K / 2 : K * 2, srow_bytes = FP4 ? K / 32 : 0;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) {
     const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0) + expert * g.w_estride;
-    const uint8_t *S = (mat ? g.S1 : g.S0) + expert * g.s_estride;
     wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
-    sr[mat] = make_rsrc(S, (uint32_t)N * srow_bytes);
+    if constexpr (FP4) sr[mat] = make_rsrc((mat ? g.S1 : g.S0) + expert * g.s_estride, (uint32_t)N * srow_bytes);
   }
   const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
   uint32_t woff[NTILE], soff[NTILE];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
     const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
-    woff[t] = (uint32_t)n * row_bytes + kg * 16;
+    woff[t] = (uint32_t)n * row_bytes + kg * (FP4 ? 16 : 64);
     soff[t] = (uint32_t)n * srow_bytes;
   }
 
@@ -83,18 +86,27 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     aoff[i] = (uint32_t)((arow * g.lda + a_oct * 8) * esz);
   }
 
-  u32x4_t wq[2][NTILE];
+  u32x4_t wq[2][NTILE];    // MXFP4: codes of one K step per stage
   uint32_t wsc[2][NTILE];
+  u32x4_t wb[4][NTILE];    // bf16: ring of sub-steps, two ahead of use
   u32x4_t aq[NPASS][AW];
 
   // loads past the last K step re-read the last one (never past the rows)
   auto load_w = [&](int b, int s) {
+    if constexpr (!FP4) return;
     s = min(s, nks - 1);
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
       wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
     }
+  };
+  // bf16 sub-step j of step s into ring slot j (sub-steps past the last step re-read it)
+  auto load_wj = [&](int s, int j) {
+    if constexpr (FP4) return;
+    s = min(s, nks - 1);
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) wb[j][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 256u + 16u * j);
   };
   auto load_a = [&](int s) {
     s = min(s, nks - 1);
@@ -145,10 +157,12 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   // Fragments f = (sub-step j, plane p, token tile n) in order; each B fragment
   // is read from LDS two fragments ahead of its MFMAs, and the weights of
   // sub-step j+1 are converted while sub-step j's MFMAs run.
-  auto compute = [&](int b) {
+  auto compute = [&](int b, int s) {
     float scl[NTILE];
+    if constexpr (FP4) {
 #pragma unroll
-    for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[b][t] >> (8 * kg)) & 0xFFu);
+      for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[b][t] >> (8 * kg)) & 0xFFu);
+    }
     constexpr int FJ = NPL * NTA;  // fragments per sub-step
     constexpr int F = 4 * FJ;      // fragments per K step
     constexpr int D = 2;           // read-ahead distance
@@ -156,19 +170,28 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
       const int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
       return *reinterpret_cast<const bf16x8_t *>(lds(b, p) + slot(4 * kg + j, 16 * n + r16));
     };
+    auto wfrag = [&](int j, int t) {
+      if constexpr (FP4) return fp4x8_to_bf16(wq[b][t][j], scl[t]);
+      else return __builtin_bit_cast(bf16x8_t, wb[j][t]);
+    };
     bf16x8_t bq[D + 1];
 #pragma unroll
     for (int f = 0; f < D; ++f) bq[f] = rd(f);
     bf16x8_t wa[2][NTILE];
 #pragma unroll
-    for (int t = 0; t < NTILE; ++t) wa[0][t] = fp4x8_to_bf16(wq[b][t][0], scl[t]);
+    for (int t = 0; t < NTILE; ++t) wa[0][t] = wfrag(0, t);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int j = f / FJ, n = f % NTA;
       if (f + D < F) bq[(f + D) % (D + 1)] = rd(f + D);
-      if (f % FJ == 0 && j + 1 < 4) {
+      if (f % FJ == 0) {
+        if (j + 1 < 4) {
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) wa[(j + 1) & 1][t] = fp4x8_to_bf16(wq[b][t][j + 1], scl[t]);
+          for (int t = 0; t < NTILE; ++t) wa[(j + 1) & 1][t] = wfrag(j + 1, t);
+        }
+        // bf16: sub-step j+2 (of this step or the next) into its ring slot,
+        // whose previous sub-step was converted before sub-step j began
+        load_wj(j + 2 < 4 ? s : s + 1, (j + 2) & 3);
       }
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bq[f % (D + 1)], acc[t][n]);
@@ -179,13 +202,15 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   // one K step: activations of s+1 and weights of s+2 are requested while s computes
   auto step = [&](int h, int s) {
     load_a(s + 1);
-    compute(h);
+    compute(h, s);
     load_w(h, s + 2);
     store_a(h ^ 1);
     __syncthreads();
   };
 
   load_w(0, 0);
+  load_wj(0, 0);
+  load_wj(0, 1);
   load_a(0);
   load_w(1, 1);
   store_a(0);
@@ -217,64 +242,90 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
         }
         float *cp = g.C + orow * g.ldc + col0;
         if (col0 + 3 < N) {
-          *reinterpret_cast<f32x4_t *>(cp) = f32x4_t{v[0], v[1], v[2], v[3]};
+          f32x4_t o = f32x4_t{v[0], v[1], v[2], v[3]};
+          if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
+          *reinterpret_cast<f32x4_t *>(cp) = o;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (col0 + r < N) cp[r] = v[r];
+            if (col0 + r < N) cp[r] = g.accumulate ? cp[r] + v[r] : v[r];
         }
       }
     }
   }
 }
 
-template <int AF, bool PAIR, int NT, int MT, int NW>
+template <int WF, int AF, bool PAIR, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(GemmArgs g) {
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * NPL * 16 * NT * KSTEP];
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
 
-  // ---- work item (XCD-aware over the items that exist on the device)
-  const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
-  const int logical = xcd_logical(total);
-  if (logical < 0) return;
-  const int chunk = logical / g.n_blocks;
-  const int nb = logical - chunk * g.n_blocks;
-  const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
-  const int nta = min((c.z + 15) >> 4, NT);  // active 16-token tiles (chunks hold <= 16*NT rows)
+  // ---- work item (XCD-aware over the items that exist on the device).
+  // Expert chunks come from the chunk list, chunk-major (the weight blocks of
+  // one chunk share its activations); dense rows are cut into chunks of 16*NT
+  // here, block-major (the chunks of one weight block share its weights).
+  int expert, row0, nrows, nb;
+  if (g.chunks != nullptr) {
+    const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
+    const int logical = xcd_logical(total);
+    if (logical < 0) return;
+    const int chunk = logical / g.n_blocks;
+    nb = logical - chunk * g.n_blocks;
+    const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
+    expert = c.x;
+    row0 = c.y;
+    nrows = c.z;
+  } else {
+    const int nch = (g.dense_rows + 16 * NT - 1) / (16 * NT);
+    const int logical = xcd_logical(min(nch * g.n_blocks, g.grid_logical));
+    if (logical < 0) return;
+    nb = logical / nch;
+    const int chunk = logical - nb * nch;
+    expert = 0;
+    row0 = chunk * 16 * NT;
+    nrows = min(16 * NT, g.dense_rows - row0);
+  }
+  const int nta = min((nrows + 15) >> 4, NT);  // active 16-token tiles
   if (nta == NT) {
-    pf_item<AF, PAIR, NT, MT, NW>(g, lds, c.x, c.y, c.z, nb);
+    pf_item<WF, AF, PAIR, NT, MT, NW>(g, lds, expert, row0, nrows, nb);
     return;
   }
   switch (nta) {
-    case 1: if constexpr (NT > 1) pf_item<AF, PAIR, 1, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    case 2: if constexpr (NT > 2) pf_item<AF, PAIR, 2, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    case 3: if constexpr (NT > 3) pf_item<AF, PAIR, 3, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    case 4: if constexpr (NT > 4) pf_item<AF, PAIR, 4, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    default: if constexpr (NT > 5) pf_item<AF, PAIR, 5, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+    case 1: if constexpr (NT > 1) pf_item<WF, AF, PAIR, 1, MT, NW>(g, lds, expert, row0, nrows, nb); break;
+    case 2: if constexpr (NT > 2) pf_item<WF, AF, PAIR, 2, MT, NW>(g, lds, expert, row0, nrows, nb); break;
+    case 3: if constexpr (NT > 3) pf_item<WF, AF, PAIR, 3, MT, NW>(g, lds, expert, row0, nrows, nb); break;
+    case 4: if constexpr (NT > 4) pf_item<WF, AF, PAIR, 4, MT, NW>(g, lds, expert, row0, nrows, nb); break;
+    default: if constexpr (NT > 5) pf_item<WF, AF, PAIR, 5, MT, NW>(g, lds, expert, row0, nrows, nb); break;
   }
 }
 
-template <int AF, bool PAIR>
+template <int WF, int AF, bool PAIR>
 hipError_t launch_pf(const GemmArgs &a, long long grid, hipStream_t st) {
   constexpr int MT = PAIR ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE;
-  hipLaunchKernelGGL((prefill_kernel<AF, PAIR, PREFILL_NT, MT, PREFILL_NW>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_kernel<WF, AF, PAIR, PREFILL_NT, MT, PREFILL_NW>), dim3((unsigned)grid),
                      dim3(64 * PREFILL_NW), 0, st, a);
   return hipGetLastError();
+}
+
+template <int WF>
+hipError_t launch_wf(int afmt, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
+  switch (afmt) {
+    case A_BF16: return pair ? launch_pf<WF, A_BF16, true>(a, grid, st) : launch_pf<WF, A_BF16, false>(a, grid, st);
+    case A_F32_SPLIT:
+      return pair ? launch_pf<WF, A_F32_SPLIT, true>(a, grid, st) : launch_pf<WF, A_F32_SPLIT, false>(a, grid, st);
+    default:
+      return pair ? launch_pf<WF, A_F32_ROUND, true>(a, grid, st) : launch_pf<WF, A_F32_ROUND, false>(a, grid, st);
+  }
 }
 
 }  // namespace
 
 int prefill_rows_per_wg(bool pair) { return 16 * PREFILL_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
 
-hipError_t launch_prefill_gemm(int afmt, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
-  switch (afmt) {
-    case A_BF16: return pair ? launch_pf<A_BF16, true>(a, grid, st) : launch_pf<A_BF16, false>(a, grid, st);
-    case A_F32_SPLIT:
-      return pair ? launch_pf<A_F32_SPLIT, true>(a, grid, st) : launch_pf<A_F32_SPLIT, false>(a, grid, st);
-    default:
-      return pair ? launch_pf<A_F32_ROUND, true>(a, grid, st) : launch_pf<A_F32_ROUND, false>(a, grid, st);
-  }
+hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
+                               hipStream_t st) {
+  return wfmt == W_MXFP4 ? launch_wf<W_MXFP4>(afmt, pair, a, grid, st) : launch_wf<W_BF16>(afmt, pair, a, grid, st);
 }
 
 }  // namespace moe
