@@ -14,7 +14,8 @@ layers of the model.  Prints one JSON line.
 Fields beyond the headline: `roofline` for the dominant kernel (the gate/up
 grouped GEMM: HBM-bound at decode, MFMA-bound at prefill), its duration taken
 from HIP events recorded on the launch stream around that call in every timed
-step; `cpu_baseline` = the CPU oracle timed on a bounded sample of the same
+step (the only events in the timed loop); `per_call_ms` from a separate loop
+with events around every call; `cpu_baseline` = the CPU oracle timed on a bounded sample of the same
 workload on this host; `secondary` = the prefill (T=4096) line; `cold_cache`
 = the same layer timed with a 512 MiB write before every step, so that no
 weight is served from the 256 MB last-level cache.
@@ -92,14 +93,27 @@ def _expert_bytes(sh) -> int:
     return _expert_gateup_bytes(sh) + sh.latent * sh.inter // 2 + sh.latent * sh.inter // 32
 
 
+def _span(marks):
+    """Milliseconds from the first call's start to the last call's end."""
+    first = marks[0][1]
+    return max(first.elapsed_time(e1) for _, _, e1 in marks)
+
+
 def _pct(v, q):
     return round(float(np.percentile(np.asarray(v), q)), 4)
 
 
-def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0):
+DOMINANT = "grouped_gemm_gateup"
+
+
+def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, breakdown_steps=10):
     """Step i runs layer i % len(layers): consecutive steps read different
     weight copies, as consecutive layers of the model do, so no step finds the
-    previous step's weights in the last-level cache."""
+    previous step's weights in the last-level cache.
+
+    The timed loop records HIP events only around the dominant call (on its
+    stream), so timing adds almost nothing to the step; the per-call
+    breakdown comes from a separate loop with events around every call."""
     from synth.device import upload_tokens
     dev = torch.device("cuda:0")
     sh = wl.shape
@@ -108,25 +122,31 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0):
     for i in range(warmup):
         moes[i % len(moes)].forward(x)
     torch.cuda.synchronize()
-    marks_all = []
+    dom = []
     t0 = time.perf_counter()
     for i in range(steps):
+        moes[i % len(moes)].forward(x, marks=dom, mark_names=(DOMINANT,))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms = [e0.elapsed_time(e1) for _, e0, e1 in dom]
+
+    # per-call breakdown (events around every call; a little slower than the timed loop)
+    marks_all = []
+    for i in range(breakdown_steps):
         marks = []
         moes[i % len(moes)].forward(x, marks=marks)
         marks_all.append(marks)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # per-call durations from the events recorded on the launch stream
-    names = [n for n, _ in marks_all[0][1:]]
-    per_call = {n: 0.0 for n in names}
+    per_call = {n: 0.0 for n, _, _ in marks_all[0]}
     spans = []
     for marks in marks_all:
-        for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
-            per_call[n1] += e0.elapsed_time(e1) / steps
-        spans.append(marks[0][1].elapsed_time(marks[-1][1]))
+        for n, e0, e1 in marks:
+            per_call[n] += e0.elapsed_time(e1) / len(marks_all)
+        spans.append(_span(marks))
     b = moes[0].buffers(wl.tokens)
     e_act = int(b["active"][0].item())
     r = {"wall_s": wall, "per_call_ms": per_call, "e_act": e_act, "T": wl.tokens,
+         "dominant_ms": float(np.mean(dom_ms)),
          "step_ms": {"median": _pct(spans, 50), "p10": _pct(spans, 10), "p90": _pct(spans, 90)}}
     if cold_steps > 0:
         # every step after a write of FLUSH_BYTES: nothing is left in the last-level cache
@@ -138,7 +158,7 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0):
             moes[0].forward(x, marks=marks)
             cold.append(marks)
         torch.cuda.synchronize()
-        cspans = [m[0][1].elapsed_time(m[-1][1]) for m in cold]
+        cspans = [_span(m) for m in cold]
         r["cold_cache"] = {"flush_bytes": FLUSH_BYTES, "steps": cold_steps, "median_ms": _pct(cspans, 50),
                            "p10_ms": _pct(cspans, 10), "p90_ms": _pct(cspans, 90),
                            "tokens_per_s": round(wl.tokens / (float(np.median(cspans)) * 1e-3), 1)}
@@ -303,7 +323,7 @@ def main():
     ms = 1e3 * r["wall_s"] / args.steps
     value = wl.tokens * args.steps / r["wall_s"]
 
-    gu_ms = r["per_call_ms"]["grouped_gemm_gateup"]
+    gu_ms = r["dominant_ms"]  # events around the gate/up call in every timed step
     P = wl.tokens * sh.top_k
     if args.workload == "decode":
         # algorithmic bytes of the gate/up grouped GEMM: w1+w3 of every active
@@ -346,7 +366,7 @@ def main():
             "layers_rotated": len(layers),
         },
         "per_call_ms": {k: round(v, 4) for k, v in r["per_call_ms"].items()},
-        "step_ms": r["step_ms"],
+        "step_ms_with_call_events": r["step_ms"],
         "roofline": roof,
     }
     if "cold_cache" in r:
@@ -359,12 +379,12 @@ def main():
     if not args.no_secondary and args.workload == "decode":
         pf = synth.workload("prefill")
         print("bench: timing prefill", file=sys.stderr, flush=True)
-        rp = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2)
+        rp = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2, breakdown_steps=2)
         pms = 1e3 * rp["wall_s"] / max(2, args.steps // 5)
         layer_flops = 2.0 * pf.tokens * (sh.top_k * 3 * sh.latent * sh.inter + sh.n_experts * sh.hidden
                                          + 2 * sh.latent * sh.hidden
                                          + 3 * sh.n_shared * sh.shared_inter * sh.hidden)
-        gu = rp["per_call_ms"]["grouped_gemm_gateup"]
+        gu = rp["dominant_ms"]
         gu_flops = 2.0 * pf.tokens * sh.top_k * sh.latent * sh.inter * 2
         line["secondary"] = {
             "workload": "prefill T=4096, same shapes and weights",

@@ -71,12 +71,16 @@ WEIGHT_KEYS = ("w_router", "bias", "w_down", "w_up", "gamma", "sh_gate", "sh_up"
 class LatentMoE:
     """One Stable LatentMoE layer on the GPU: weights resident, buffers per token count.
 
-    forward(x) enqueues on the current stream, in order: moe_route,
-    moe_permute, mxfp4_grouped_gemm (gate/up + SiTU-GLU), mxfp4_grouped_gemm
-    (down), moe_combine_norm_up (writes out), shared_expert_ffn (adds to out).
+    forward(x) enqueues the shared experts (shared_expert_ffn, writes out) on a
+    side stream, and on the caller's stream: moe_route, moe_permute,
+    mxfp4_grouped_gemm (gate/up + SiTU-GLU), mxfp4_grouped_gemm (down), then,
+    after the side stream, moe_combine_norm_up (adds the routed part to out).
+    The shared experts depend only on x, so they overlap the latency-bound
+    routing steps; the two parts are added once, so the result is the same as
+    running the calls in sequence.
     """
 
-    def __init__(self, shape: MoeShape, weights: dict, device="cuda"):
+    def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True):
         missing = [k for k in WEIGHT_KEYS if k not in weights]
         if missing:
             raise ValueError(f"missing weights: {missing}")
@@ -84,6 +88,8 @@ class LatentMoE:
         self.w = weights
         self.device = torch.device(device)
         self._bufs: dict = {}
+        self.overlap_shared = overlap_shared
+        self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None  # default priority
 
     def buffers(self, T: int) -> dict:
         if T in self._bufs:
@@ -91,8 +97,8 @@ class LatentMoE:
         s, dev = self.shape, self.device
         P = T * s.top_k
         ws = max(workspace_bytes(s, fn, P if fn == MOE_FN_GROUPED_GEMM else T)
-                 for fn in (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP,
-                            MOE_FN_SHARED_FFN))
+                 for fn in (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP))
+        ws_sh = max(16, workspace_bytes(s, MOE_FN_SHARED_FFN, T))
         i32, f32 = torch.int32, torch.float32
         b = {
             "topk_ids": torch.empty((T, s.top_k), dtype=i32, device=dev),
@@ -107,43 +113,58 @@ class LatentMoE:
             "Y": torch.empty((P, s.latent), dtype=f32, device=dev),
             "out": torch.empty((T, s.hidden), dtype=f32, device=dev),
             "ws": torch.empty((ws,), dtype=torch.uint8, device=dev),
+            "ws_shared": torch.empty((ws_sh,), dtype=torch.uint8, device=dev),
         }
         self._bufs[T] = b
         return b
 
-    def forward(self, x: torch.Tensor, stream=None, marks: list | None = None) -> dict:
-        """Enqueue the layer on `stream` (default: current stream).  With `marks`
-        given, a timing event is recorded on the stream before the first call
-        and after each call, appended as (name, event) pairs."""
+    def forward(self, x: torch.Tensor, stream=None, marks: list | None = None, mark_names=None) -> dict:
+        """Enqueue the layer.  With `marks` given, timing events are recorded
+        around every call (or the calls named in `mark_names`) on the stream
+        it runs on, appended as (name, start_event, end_event)."""
         s, w = self.shape, self.w
         T = x.shape[0]
         P = T * s.top_k
         b = self.buffers(T)
         ws = b["ws"]
         st = torch.cuda.current_stream() if stream is None else stream
+        side = self.side if self.overlap_shared else st
 
-        def mark(name):
-            if marks is not None:
-                ev = torch.cuda.Event(enable_timing=True)
-                ev.record(st)
-                marks.append((name, ev))
+        def call(name, strm, fn):
+            if marks is None or (mark_names is not None and name not in mark_names):
+                fn()
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(strm)
+            fn()
+            e1.record(strm)
+            marks.append((name, e0, e1))
 
-        mark("start")
-        route(s, x, w["w_router"], w["bias"], w["w_down"], b["topk_ids"], b["topk_w"], b["z"], b["gap"],
-              ws, st)
-        mark("moe_route")
-        permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"], b["active"], ws, st)
-        mark("moe_permute")
-        grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"], w["w1_packed"],
-                     w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"], ws, st)
-        mark("grouped_gemm_gateup")
-        grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
-                     w["w2_scale"], None, None, None, b["Y"], ws, st)
-        mark("grouped_gemm_down")
-        combine_norm_up(s, T, b["Y"], b["pair_pos"], b["topk_w"], w["gamma"], w["w_up"], b["out"], 0, ws,
-                        st)
-        mark("moe_combine_norm_up")
-        if s.n_shared * s.shared_inter > 0:
-            shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 1, ws, st)
-            mark("shared_expert_ffn")
+        shared = s.n_shared * s.shared_inter > 0
+        if shared:
+            if side is not st:
+                side.wait_stream(st)
+                x.record_stream(side)
+            call("shared_expert_ffn", side,
+                 lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, b["ws_shared"],
+                                    side))
+            shared_done = torch.cuda.Event()
+            shared_done.record(side)
+        call("moe_route", st, lambda: route(s, x, w["w_router"], w["bias"], w["w_down"], b["topk_ids"],
+                                            b["topk_w"], b["z"], b["gap"], ws, st))
+        call("moe_permute", st, lambda: permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"],
+                                                b["active"], ws, st))
+        call("grouped_gemm_gateup", st,
+             lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"],
+                                  w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"],
+                                  ws, st))
+        call("grouped_gemm_down", st,
+             lambda: grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
+                                  w["w2_scale"], None, None, None, b["Y"], ws, st))
+        if shared and side is not st:
+            st.wait_event(shared_done)
+        call("moe_combine_norm_up", st,
+             lambda: combine_norm_up(s, T, b["Y"], b["pair_pos"], b["topk_w"], w["gamma"], w["w_up"], b["out"],
+                                     1 if shared else 0, ws, st))
         return b
