@@ -96,7 +96,7 @@ size_t moe_workspace_bytes(const moe_shape *shape, int fn, int n);
  * K3 open-artifact audit, section 6 (router weight [896, 7168] bf16, bias
  * [896] fp32).
  *   x         [T, H]  bf16   layer input
- *   w_router  [E, H]  bf16
+ *   w_router  [E, H]  bf16   (NULL: z only)
  *   bias      [E]     fp32   correction bias (selection only)
  *   w_down    [L, H]  bf16   latent down projection; NULL together with z to skip it
  * Outputs:
@@ -107,7 +107,11 @@ size_t moe_workspace_bytes(const moe_shape *shape, int fn, int n);
  *                            +inf when E == k)
  * Logits accumulate in fp32; biased score = fp32 sigmoid + fp32 bias; the k
  * largest win with ties to the lower index; NaN biased scores rank last.
- * Errors: MOE_EINVAL for T < 1 or a null required pointer. */
+ * With w_router NULL (and bias, topk_ids, topk_w, gap NULL) only z is
+ * computed, so that the latent projection can run on another stream than the
+ * routing.
+ * Errors: MOE_EINVAL for T < 1, a null required pointer, or a routing call
+ * missing one of w_router, bias, topk_ids, topk_w. */
 int moe_route(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *w_router,
               const float *bias, const uint16_t *w_down, int32_t *topk_ids, float *topk_w,
               float *z, float *gap, void *ws, size_t ws_bytes, void *stream);

@@ -215,9 +215,13 @@ int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_ro
   return guarded([&]() -> int {
     int rc = check_shape(s);
     if (rc) return rc;
-    if (T <= 0 || !x || !w_router || !bias || !topk_ids || !topk_w || !ws) return MOE_EINVAL;
+    if (T <= 0 || !x || !ws) return MOE_EINVAL;
     if ((w_down == nullptr) != (z == nullptr)) return MOE_EINVAL;
-    if (!aligned16(x) || !aligned16(w_router) || (w_down && !aligned16(w_down)) ||
+    // routing needs the router, bias and both outputs; without a router only z is computed
+    const bool routing = w_router != nullptr;
+    if (routing && (!bias || !topk_ids || !topk_w)) return MOE_EINVAL;
+    if (!routing && (bias || topk_ids || topk_w || gap || !z)) return MOE_EINVAL;
+    if ((routing && !aligned16(w_router)) || (w_down && !aligned16(w_down)) || !aligned16(x) ||
         (z && !aligned16(z)) || !aligned16(ws))
       return MOE_EINVAL;
     const RouteWs w = route_ws(s, T);
@@ -226,12 +230,13 @@ int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_ro
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *logits = reinterpret_cast<float *>(wsp(ws, w.logits));
     float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
-    GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
-                            s->n_experts, 0, T, partial, s);
-    if (run_dense(w.pr, A_BF16, false, a, st) != hipSuccess) return MOE_EHIP;
-    if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) !=
-        hipSuccess)
-      return MOE_EHIP;
+    if (routing) {
+      GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
+                              s->n_experts, 0, T, partial, s);
+      if (run_dense(w.pr, A_BF16, false, a, st) != hipSuccess) return MOE_EHIP;
+      if (launch_topk(logits, 1, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) != hipSuccess)
+        return MOE_EHIP;
+    }
     if (z) {
       GemmArgs d = dense_args(w.pd, x, s->hidden, w_down, nullptr, s->latent, s->hidden, z,
                               s->latent, 0, T, partial, s);

@@ -72,12 +72,13 @@ class LatentMoE:
     """One Stable LatentMoE layer on the GPU: weights resident, buffers per token count.
 
     forward(x) enqueues the shared experts (shared_expert_ffn, writes out) on a
-    side stream, and on the caller's stream: moe_route, moe_permute,
-    mxfp4_grouped_gemm (gate/up + SiTU-GLU), mxfp4_grouped_gemm (down), then,
-    after the side stream, moe_combine_norm_up (adds the routed part to out).
-    The shared experts depend only on x, so they overlap the latency-bound
-    routing steps; the two parts are added once, so the result is the same as
-    running the calls in sequence.
+    side stream, and on the caller's stream: moe_route, moe_permute, then,
+    after the side stream, mxfp4_grouped_gemm (gate/up + SiTU-GLU),
+    mxfp4_grouped_gemm (down) and moe_combine_norm_up (adds the routed part to
+    out).  The shared experts depend only on x, so they overlap the
+    latency-bound routing steps, and the expert GEMMs then stream alone; the
+    two output parts are added once, so the result is the same as running the
+    calls in sequence.
     """
 
     def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True):
@@ -89,7 +90,8 @@ class LatentMoE:
         self.device = torch.device(device)
         self._bufs: dict = {}
         self.overlap_shared = overlap_shared
-        self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None  # default priority
+        # default-priority side stream for the shared experts
+        self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None
 
     def buffers(self, T: int) -> dict:
         if T in self._bufs:
@@ -142,19 +144,25 @@ class LatentMoE:
             marks.append((name, e0, e1))
 
         shared = s.n_shared * s.shared_inter > 0
-        if shared:
-            if side is not st:
-                side.wait_stream(st)
-                x.record_stream(side)
+        if shared and side is not st:
+            # side stream: the shared experts, during the latency-bound routing steps
+            side.wait_stream(st)
+            x.record_stream(side)
             call("shared_expert_ffn", side,
                  lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, b["ws_shared"],
                                     side))
-            shared_done = torch.cuda.Event()
-            shared_done.record(side)
+            side_done = torch.cuda.Event()
+            side_done.record(side)
+        elif shared:
+            call("shared_expert_ffn", st,
+                 lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, ws, st))
         call("moe_route", st, lambda: route(s, x, w["w_router"], w["bias"], w["w_down"], b["topk_ids"],
                                             b["topk_w"], b["z"], b["gap"], ws, st))
         call("moe_permute", st, lambda: permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"],
                                                 b["active"], ws, st))
+        if shared and side is not st:
+            # the expert GEMMs stream weights at full bandwidth on their own
+            st.wait_event(side_done)
         call("grouped_gemm_gateup", st,
              lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"],
                                   w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"],
@@ -162,8 +170,6 @@ class LatentMoE:
         call("grouped_gemm_down", st,
              lambda: grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
                                   w["w2_scale"], None, None, None, b["Y"], ws, st))
-        if shared and side is not st:
-            st.wait_event(shared_done)
         call("moe_combine_norm_up", st,
              lambda: combine_norm_up(s, T, b["Y"], b["pair_pos"], b["topk_w"], w["gamma"], w["w_up"], b["out"],
                                      1 if shared else 0, ws, st))

@@ -89,6 +89,15 @@ def test_route_validation(lib):
     small = list(args)
     small[10] = ws - 1
     assert lib.moe_route(s, *small) == _lib.MOE_EWORKSPACE
+    no_router = list(args)
+    no_router[2] = None  # z only: bias, ids, weights and gap must be NULL too
+    assert lib.moe_route(s, *no_router) == _lib.MOE_EINVAL
+    z_only = [16, FAKE, None, None, FAKE, None, None, FAKE, None, FAKE, ws, None]
+    bad_z_only = list(z_only)
+    bad_z_only[4] = None
+    bad_z_only[7] = None
+    assert lib.moe_route(s, *bad_z_only) == _lib.MOE_EINVAL  # neither routing nor z
+    assert lib.moe_route(s, *z_only[:10], ws - 1, None) == _lib.MOE_EWORKSPACE
     assert lib.moe_route(None, *args) == _lib.MOE_EINVAL
     assert lib.moe_route(_shape(operand_mode=7), *args) == _lib.MOE_EINVAL
     assert lib.moe_route(_shape(top_k=900), *args) == _lib.MOE_EINVAL
