@@ -106,7 +106,7 @@ def _pct(v, q):
 DOMINANT = "grouped_gemm_gateup"
 
 
-def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, breakdown_steps=10):
+def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, breakdown_steps=10, operand_mode=0):
     """Step i runs layer i % len(layers): consecutive steps read different
     weight copies, as consecutive layers of the model do, so no step finds the
     previous step's weights in the last-level cache.
@@ -117,7 +117,7 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, brea
     from synth.device import upload_tokens
     dev = torch.device("cuda:0")
     sh = wl.shape
-    moes = [mx.LatentMoE(mx.shape_of(sh), w, dev) for w in layers]
+    moes = [mx.LatentMoE(mx.shape_of(sh, operand_mode), w, dev) for w in layers]
     x = upload_tokens(wl, dev)
     for i in range(warmup):
         moes[i % len(moes)].forward(x)
@@ -394,6 +394,20 @@ def main():
             "layer_mfma_frac_algorithmic": round(layer_flops / (pms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "gateup_tflops": round(gu_flops / (gu * 1e-3) / 1e12, 1),
             "per_call_ms": {k: round(v, 4) for k, v in rp["per_call_ms"].items()},
+        }
+        # the same prefill with the MX-scaled expert GEMMs (three fp8 activation terms)
+        print("bench: timing prefill, MX fp8 operand mode", file=sys.stderr, flush=True)
+        rm = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2, breakdown_steps=2,
+                          operand_mode=mx.MOE_OPND_MX8X3)
+        mms = 1e3 * rm["wall_s"] / max(2, args.steps // 5)
+        line["secondary_mx8x3"] = {
+            "workload": "prefill T=4096, expert GEMM activations as three e4m3 terms (operand mode MX8X3)",
+            "tokens_per_s": round(pf.tokens / (mms * 1e-3), 1),
+            "ms_per_step": round(mms, 3),
+            "layer_tflops_algorithmic": round(layer_flops / (mms * 1e-3) / 1e12, 1),
+            "layer_mfma_frac_algorithmic": round(layer_flops / (mms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "gateup_tflops": round(gu_flops / (rm["dominant_ms"] * 1e-3) / 1e12, 1),
+            "per_call_ms": {k: round(v, 4) for k, v in rm["per_call_ms"].items()},
         }
 
     if args.calibrate_copy:

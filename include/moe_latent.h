@@ -51,6 +51,13 @@ extern "C" {
    the expert hidden H, the normalised latent, the shared-expert hidden) */
 #define MOE_OPND_BF16X2 0 /* a = hi + lo, two bf16 MFMAs per product (default) */
 #define MOE_OPND_BF16 1   /* a rounded once to bf16 (faster, less accurate) */
+/* MXFP4 expert GEMMs over prefill-sized segments take fp32 activations as
+   three e4m3 terms with power-of-two scales per block of 32 (residual near
+   2^-12 of the block maximum) and feed them with the raw e2m1 weights and
+   their e8m0 scales to the MX-scaled MFMA; every other product is BF16X2.
+   A faster mode that departs from dequantise-to-bf16 arithmetic; its error
+   against the exact layer is about 1e-4 of the output rms. */
+#define MOE_OPND_MX8X3 2
 
 /* mxfp4_grouped_gemm operations */
 #define MOE_OP_GATEUP_SITU 0
@@ -78,7 +85,7 @@ typedef struct {
   float beta;           /* SiTU-GLU gate saturation (4) */
   float beta_lin;       /* SiTU-GLU linear-branch saturation (25) */
   float rms_eps;        /* RMSNorm epsilon on the combined latent (1e-6) */
-  int32_t operand_mode; /* MOE_OPND_BF16X2 or MOE_OPND_BF16 */
+  int32_t operand_mode; /* MOE_OPND_BF16X2, MOE_OPND_BF16 or MOE_OPND_MX8X3 */
 } moe_shape;
 
 int moe_abi_version(void);

@@ -21,7 +21,9 @@ int check_shape(const moe_shape *s) {
   if (s->hidden <= 0 || s->latent <= 0 || s->n_experts <= 0 || s->top_k <= 0 || s->inter <= 0 ||
       s->n_shared < 0 || s->shared_inter < 0)
     return MOE_EINVAL;
-  if (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16) return MOE_EINVAL;
+  if (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16 &&
+      s->operand_mode != MOE_OPND_MX8X3)
+    return MOE_EINVAL;
   if (!(s->beta > 0.f) || !(s->beta_lin > 0.f) || !(s->rms_eps >= 0.f)) return MOE_EINVAL;
   if (s->top_k > s->n_experts) return MOE_EINVAL;
   if (s->hidden % 128 || s->latent % 128 || s->inter % 128 || (s->n_shared * s->shared_inter) % 128)
@@ -70,18 +72,27 @@ size_t permute_ws(const moe_shape *s, int T) {
   return align_up((size_t)permute_blocks(T) * s->n_experts * sizeof(int32_t));
 }
 
+// MX fp8 activation terms are used for fp32 activations on the tiled path,
+// while 3 term planes of P rows stay addressable with 32-bit offsets
+bool use_mx8(const moe_shape *s, const GemmPlan &pl, int P, int K) {
+  return s->operand_mode == MOE_OPND_MX8X3 && pl.variant == 3 && 3LL * P * K < (1LL << 32) - 256;
+}
+
 struct GroupedWs {
-  size_t chunks, count, partial, total;
+  size_t chunks, count, partial, mx, total;
   GemmPlan plan;
 };
 GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
   GroupedWs w{};
+  const int K = gateup ? s->latent : s->inter;
   w.plan = gateup ? plan_grouped(P, s->n_experts, s->inter, s->latent, true)
                   : plan_grouped(P, s->n_experts, s->latent, s->inter, false);
   w.chunks = 0;
   w.count = align_up((size_t)w.plan.max_chunks * 16);
   w.partial = w.count + ALIGN;
-  w.total = w.partial + align_up(w.plan.partial_bytes);
+  w.mx = w.partial + align_up(w.plan.partial_bytes);
+  // activation rows are at most P (T = P / k rows when they are gathered by sorted_pair)
+  w.total = w.mx + (use_mx8(s, w.plan, P, K) ? align_up(mx8_split_bytes(P, K)) : 0);
   return w;
 }
 
@@ -324,7 +335,19 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     a.partial_rows = P;
     a.beta = s->beta;
     a.beta_lin = s->beta_lin;
-    const int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
+    int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
+    if (a_dtype == MOE_DT_F32 && use_mx8(s, w.plan, P, K)) {
+      // split the fp32 activation rows into three MX fp8 terms, then the MX-scaled GEMM
+      // gate/up gathers rows of z [P / k, K] through sorted_pair; down reads H [P, K] in order
+      const long long rows = (gateup && sorted_pair) ? (long long)(P / s->top_k) : (long long)P;
+      uint8_t *mx = reinterpret_cast<uint8_t *>(wsp(ws, w.mx));
+      if (launch_mx8_split(static_cast<const float *>(A), K, (int)rows, K, mx, st) != hipSuccess)
+        return MOE_EHIP;
+      a.mxq = mx;
+      a.mxs = mx + (size_t)rows * K * 3;
+      a.mx_rows = rows;
+      afmt = A_MX8X3;
+    }
     if (launch_gemm(w.plan, W_MXFP4, afmt, gateup, a, st) != hipSuccess) return MOE_EHIP;
     if (w.plan.splits > 1) {
       FinalizeArgs f{};

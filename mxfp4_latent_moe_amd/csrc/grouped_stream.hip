@@ -285,10 +285,13 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   }
 }
 
-// gate/up: one tile of w1 and one of w3 per wave; down: two tiles of w2 per wave
+// One 16-row tile per wave and matrix, two groups in flight; gate/up (two
+// matrices per wave) runs eight waves per work-group, down four.
+constexpr int gs_waves(bool pair) { return pair ? 8 : 4; }
+
 template <int AF, bool PAIR>
 void *kernel_ptr() {
-  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, PAIR ? 1 : 2, 2, 4>);
+  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, 1, 2, gs_waves(PAIR)>);
 }
 
 void *select_kernel(int afmt, bool pair) {
@@ -301,7 +304,7 @@ void *select_kernel(int afmt, bool pair) {
 
 }  // namespace
 
-int grouped_stream_rows_per_wg(bool pair) { return 16 * 4 * (pair ? 1 : 2); }
+int grouped_stream_rows_per_wg(bool pair) { return 16 * gs_waves(pair); }
 
 bool grouped_stream_fits(int K) {
   const int nks = K / KSTEP;
@@ -318,7 +321,7 @@ hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStre
   int per_cu = cache[dev][slot].load();
   if (per_cu == 0) {
     int blocks = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 256, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * gs_waves(pair), 0);
     if (e != hipSuccess) return e;
     per_cu = blocks > 0 ? blocks : 1;
     cache[dev][slot].store(per_cu);
@@ -336,7 +339,7 @@ hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStre
   if (grid < 1) grid = 1;
   GemmArgs args = a;
   void *params[] = {&args};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), params, 0, st);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * gs_waves(pair)), params, 0, st);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

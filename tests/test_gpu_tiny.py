@@ -204,3 +204,25 @@ def test_tiny_graph_capture_replays(mx):
         torch.cuda.synchronize()
         for k in ("topk_ids", "topk_w", "z", "H", "Y", "out"):
             assert torch.equal(bufs[k], eager[k]), (i, k)
+
+
+def test_tiny_mx8x3_operand_mode(mx):
+    """Prefill-sized segments (T=37: 4.6 rows per expert) through the MX-scaled
+    expert GEMMs: activations as three fp8 terms, weights as raw e2m1 codes."""
+    from mxfp4_latent_moe_amd import _lib
+    wl = synth.workload("tiny")
+    x_bits = synth.gen_tokens(synth.Workload("tiny37", 11, wl.shape, 37, wl.wset, wl.router_std, wl.bias_std,
+                                             "normal", wl.exp_lo, wl.exp_hi))
+    d = synth.gen_dense(wl)
+    b = synth.gen_bias(wl)
+    st = synth.gen_expert_stack(wl)
+    say("case: tiny T=37, operand mode mx8x3")
+    g = _run(mx, wl, x_bits, operand_mode=_lib.MOE_OPND_MX8X3)
+    ref = _oracle(wl, x_bits, d, b, st)
+    excl = check_routing(g["topk_ids"], g["topk_w"], ref)
+    check_permutation(g, ref["ids"], wl.shape.n_experts, excl)
+    errH = rel_max_err(g["H"], ref["H_sorted"])
+    err = rel_max_err(g["out"], ref["out"])
+    say(f"tiny mx8x3: H {errH:.3e}, out {err:.3e}")
+    assert err <= TOL
+    assert err < 2e-3 and errH < 2e-3
