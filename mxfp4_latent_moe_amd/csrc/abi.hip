@@ -245,7 +245,7 @@ int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_ro
       GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
                               s->n_experts, 0, T, partial, s);
       if (run_dense(w.pr, A_BF16, false, a, st) != hipSuccess) return MOE_EHIP;
-      if (launch_topk(logits, 1, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) != hipSuccess)
+      if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) != hipSuccess)
         return MOE_EHIP;
     }
     if (z) {
