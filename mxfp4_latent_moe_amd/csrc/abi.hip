@@ -348,7 +348,15 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
       a.mx_rows = rows;
       afmt = A_MX8X3;
     }
-    if (launch_gemm(w.plan, W_MXFP4, afmt, gateup, a, st) != hipSuccess) return MOE_EHIP;
+    GemmPlan pl = w.plan;
+    if (afmt == A_MX8X3) {
+      // the MX kernel covers fewer weight rows per work-group
+      pl.n_blocks = (N + prefill_mx_rows_per_wg(gateup) - 1) / prefill_mx_rows_per_wg(gateup);
+      pl.grid_logical = (long long)pl.max_chunks * pl.n_blocks;
+      a.n_blocks = pl.n_blocks;
+      a.grid_logical = (int)pl.grid_logical;
+    }
+    if (launch_gemm(pl, W_MXFP4, afmt, gateup, a, st) != hipSuccess) return MOE_EHIP;
     if (w.plan.splits > 1) {
       FinalizeArgs f{};
       f.partial = a.partial;

@@ -69,6 +69,7 @@ constexpr int PREFILL_NT = 6;
 constexpr int PREFILL_MT_PAIR = 2;
 constexpr int PREFILL_MT_SINGLE = 4;
 constexpr int PREFILL_NW = 8;
+constexpr int PREFILL_MX_NW = 4;  // MX-scaled variant: one wave per SIMD
 
 // kernel variant selection (host side)
 struct GemmPlan {
@@ -92,6 +93,7 @@ int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
 hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st);
 int prefill_rows_per_wg(bool pair);
+int prefill_mx_rows_per_wg(bool pair);
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st);
 size_t mx8_split_bytes(long long rows, int K);

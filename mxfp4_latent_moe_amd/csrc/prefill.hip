@@ -322,29 +322,73 @@ MOE_DEV f32x4_t mfma_mx_fp4_fp8(u32x4_t w, i32x8_t b, f32x4_t c, int sa, int sb)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
 }
 
+// LDS bytes of one activation stage with NT token tiles: fp8 terms
+// [term][K group g][token ^ g][half][16] and block scales [term][token] (dwords,
+// padded to whole wave loads)
+constexpr int mx_q_bytes(int nt) { return 3 * 4 * 16 * nt * 32; }
+constexpr int mx_s_bytes(int nt) { return (3 * 16 * nt * 4 + 255) / 256 * 256; }
+constexpr int mx_stage_bytes(int nt) { return mx_q_bytes(nt) + mx_s_bytes(nt); }
+constexpr int MX_DUMMY_BYTES = 8 * 1024;  // target of the padding loads
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int N, typename Fn>
+MOE_DEV void static_for(Fn &&fn) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(fn);
+    fn(std::integral_constant<int, N - 1>{});
+  }
+}
+
+MOE_DEV uint32_t lds_addr(uint8_t *p) { return (uint32_t)(uintptr_t)(lds_void *)p; }
+
+// 32 activation bytes at qa + QO and a scale dword at sa + SO, issued without waiting
+template <int QO, int SO>
+MOE_DEV void lds_read_frag(uint32_t qa, uint32_t sa, u32x4_t &lo, u32x4_t &hi, uint32_t &sc) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:%5\n\t"
+      "ds_read_b128 %1, %3 offset:%6\n\t"
+      "ds_read_b32 %2, %4 offset:%7"
+      : "=&v"(lo), "=&v"(hi), "=&v"(sc)
+      : "v"(qa), "v"(sa), "n"(QO), "n"(QO + 16), "n"(SO)
+      : "memory");
+}
+
+// wait until at most N LDS reads are outstanding; the operands tie the wait
+// to the registers it protects, so their users stay behind it
+template <int N>
+MOE_DEV void lds_wait_frag(u32x4_t &lo, u32x4_t &hi, uint32_t &sc) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo), "+v"(hi), "+v"(sc) : "n"(N) : "memory");
+}
+
 template <bool PAIR, int NTA, int MT, int NW>
-__device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *lds_base, int expert, int row0, int nrows,
-                                          int nb) {
+__device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8_t *st1, uint8_t *st2,
+                                          uint8_t *dummy, int expert, int row0, int nrows, int nb) {
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
   constexpr int CT = 16 * NTA;
   constexpr int ROWS_WG = 16 * NW * MT;
-  constexpr int NTHR = 64 * NW;
   constexpr int TERMS = 3;
-  constexpr int QBYTES = TERMS * 8 * CT * 16;  // per stage: [term][K group][token][32]
-  constexpr int SBYTES = TERMS * CT * 4;       // per stage: [term][token] dword of 4 block scales
-  auto qlds = [&](int b) { return lds_base + b * (QBYTES + SBYTES); };
-  auto slds = [&](int b) { return reinterpret_cast<uint32_t *>(lds_base + b * (QBYTES + SBYTES) + QBYTES); };
+  constexpr int QB = mx_q_bytes(NTA);
+  constexpr int QI = QB / 1024;                   // 1 KB wave loads per stage for the terms
+  constexpr int SI = mx_s_bytes(NTA) / 256;       // 256-byte wave loads per stage for the scales
+  constexpr int KQ = (QI + NW - 1) / NW;          // per wave, equal for all waves
+  constexpr int KS = (SI + NW - 1) / NW;
+  static_assert((KQ * NW - QI) * 1024 + (KS * NW - SI) * 256 <= MX_DUMMY_BYTES, "dummy area");
+  uint8_t *stage[3] = {st0, st1, st2};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
   const int kg = lane >> 4;
   const int r16 = lane & 15;
   const int N = g.N, K = g.K;
   const int nks = K / KSTEP;
 
-  // ---- weights: as in the bf16-dequantising path
+  // ---- weights: a three-deep register ring, two steps ahead
   const uint32_t row_bytes = K / 2, srow_bytes = K / 32;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
@@ -361,75 +405,62 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *lds_base, 
     woff[t] = (uint32_t)n * row_bytes + kg * 16;
     soff[t] = (uint32_t)n * srow_bytes;
   }
-  u32x4_t wq[2][NTILE];
-  uint32_t wsc[2][NTILE];
-  auto load_w = [&](int b, int s) {
-    s = min(s, nks - 1);
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) {
-      wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
-      wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
-    }
+  u32x4_t wq[3][NTILE];
+  uint32_t wsc[3][NTILE];
+  auto load_w_tile = [&](int b, int t, int s) {
+    wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
+    wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
   };
 
-  // ---- activation terms: each thread stages 16-byte chunk (tid & 7) of tokens
-  // (tid >> 3) + TPP*j of every term; rows past the chunk read past the buffer
-  // (zeros), stores past the staged tokens go to a per-thread trash slot
-  constexpr int TPP = NTHR / 8;                 // tokens per pass
-  constexpr int NP = (CT + TPP - 1) / TPP;      // passes per term
+  // ---- activation terms, loaded straight into LDS: wave load k of this wave
+  // covers 16-byte slots [64 (wave + NW k), +64); slot q of a stage is (term,
+  // g, token ^ g, half).  Rows past the chunk repeat its first row (their
+  // columns are never stored).
   const uint32_t plane = (uint32_t)(g.mx_rows * K), splane = (uint32_t)(g.mx_rows * (K / 32));
-  __amdgpu_buffer_rsrc_t qr[TERMS], sr8[TERMS];
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.mxq, 3u * plane);
+  const __amdgpu_buffer_rsrc_t sr8 = make_rsrc(g.mxs, 3u * splane);
+  auto arow_of = [&](int tok) -> long long {
+    const int p = row0 + (tok < nrows ? tok : 0);
+    return g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
+  };
+  uint32_t qoff[KQ];
 #pragma unroll
-  for (int term = 0; term < TERMS; ++term) {
-    qr[term] = make_rsrc(g.mxq + (size_t)term * plane, plane);
-    sr8[term] = make_rsrc(g.mxs + (size_t)term * splane, splane);
+  for (int k = 0; k < KQ; ++k) {
+    const int q = 64 * (wave + NW * k) + lane;
+    const int term = q / (8 * CT), rem = q - term * 8 * CT;
+    const int gg = rem / (2 * CT), rem2 = rem - gg * 2 * CT;
+    const int tok = (rem2 >> 1) ^ gg, half = rem2 & 1;
+    qoff[k] = q < QB / 16 ? (uint32_t)(term * (long long)plane + arow_of(tok) * K + (gg + 4 * half) * 16) : 0u;
   }
-  const int cidx = tid & 7;
-  uint32_t aoff[NP];
-  int aslot[NP];
+  uint32_t soffs[KS];
 #pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int tok = (tid >> 3) + TPP * j;
-    aoff[j] = 0xFFFFFF00u;
-    if (tok < nrows && tok < CT) {
-      const int p = row0 + tok;
-      const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
-      aoff[j] = (uint32_t)(arow * K + cidx * 16);
-    }
-    aslot[j] = tok < CT ? ((cidx & 3) * CT + (tok ^ (cidx & 3))) * 32 + (cidx >> 2) * 16 : QBYTES + SBYTES + tid * 16;
+  for (int k = 0; k < KS; ++k) {
+    const int q = 64 * (wave + NW * k) + lane;
+    const int term = q / CT, tok = q - term * CT;
+    soffs[k] = q < TERMS * CT ? (uint32_t)(term * (long long)splane + arow_of(tok) * (K / 32)) : 0u;
   }
-  // block scales: thread (term, token) for tid < 3 * CT loads the token's 4 scale bytes of the step
-  const int sterm = tid / CT, stok = tid - (tid / CT) * CT;
-  uint32_t soff8 = 0xFFFFFF00u;
-  if (tid < TERMS * CT && stok < nrows) {
-    const int p = row0 + stok;
-    const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
-    soff8 = (uint32_t)(arow * (K / 32));
-  }
-  u32x4_t aq[TERMS][NP];
-  uint32_t asc = 0;
-  auto load_a = [&](int s) {
+  auto load_q = [&](int b, int k, int s) {
+    const int ii = wave + NW * k;
+    uint8_t *dst = ii < QI ? stage[b] + ii * 1024 : dummy + (ii - QI) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)dst, 16, qoff[k], (uint32_t)s * 128u, 0, 0);
+  };
+  auto load_s = [&](int b, int k, int s) {
+    const int ii = wave + NW * k;
+    uint8_t *dst = ii < SI ? stage[b] + QB + ii * 256 : dummy + MX_DUMMY_BYTES / 2 + (ii - SI) * 256;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr8, (lds_void *)dst, 4, soffs[k], (uint32_t)s * 4u, 0, 0);
+  };
+  // the memory operations that fill ring slot b with step s: KQ + KS loads into
+  // LDS and NTILE weight tiles (two loads each)
+  constexpr int NOPS = KQ + KS + NTILE;
+  auto issue_op = [&](int o, int b, int s) {
+    if (o < KQ) load_q(b, o, s);
+    else if (o < KQ + KS) load_s(b, o - KQ, s);
+    else load_w_tile(b, o - KQ - KS, s);
+  };
+  auto load_all = [&](int b, int s) {
     s = min(s, nks - 1);
 #pragma unroll
-    for (int term = 0; term < TERMS; ++term)
-#pragma unroll
-      for (int j = 0; j < NP; ++j) aq[term][j] = buf_load16(qr[term], aoff[j], (uint32_t)s * 128u);
-    if (tid < TERMS * CT) {
-      __amdgpu_buffer_rsrc_t r = sterm == 0 ? sr8[0] : (sterm == 1 ? sr8[1] : sr8[2]);
-      asc = buf_load4(r, soff8, (uint32_t)s * 4u);
-    }
-  };
-  auto store_a = [&](int b) {
-#pragma unroll
-    for (int term = 0; term < TERMS; ++term)
-#pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        // trash slots lie past both stages; a real slot is offset by its stage and term
-        const int off = aslot[j] < QBYTES + SBYTES ? b * (QBYTES + SBYTES) + term * 8 * CT * 16 + aslot[j]
-                                                   : 2 * (QBYTES + SBYTES) + tid * 16;
-        *reinterpret_cast<u32x4_t *>(lds_base + off) = aq[term][j];
-      }
-    if (tid < TERMS * CT) slds(b)[tid] = stok < nrows ? asc : 0x7F7F7F7Fu;  // [term][token]
+    for (int o = 0; o < NOPS; ++o) issue_op(o, b, s);
   };
 
   f32x4_t acc[NTILE][NTA];
@@ -438,53 +469,77 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *lds_base, 
 #pragma unroll
     for (int n = 0; n < NTA; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int b) {
+  // LDS reads of the activation fragments are written as inline assembly with
+  // explicit lgkmcnt waits: the compiler would otherwise wait for every load
+  // into LDS still in flight (it cannot tell the stages apart) before each read.
+  // Fragment f = (term, token tile n); lane (token r16, group kg) reads 32
+  // contiguous bytes (K 16kg..+15 and 64+16kg..+15) and its token's scale dword.
+  uint32_t qlane[3], slane[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    qlane[b] = lds_addr(stage[b]) + (uint32_t)((kg * CT + (r16 ^ kg)) * 32);
+    slane[b] = lds_addr(stage[b]) + (uint32_t)(QB + r16 * 4);
+  }
+  // compute step s from slot b; after each fragment's products a share of the
+  // loads of step s + 2 (into slot b2) goes out, so that no wave stalls on a
+  // burst of memory instructions
+  auto compute = [&](int b, int b2, int s2) {
     int sa[NTILE];
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) sa[t] = (int)((wsc[b][t] >> (8 * kg)) & 0xFFu);
-    constexpr int F = TERMS * NTA;  // fragments (term, token tile) per step
+    constexpr int F = TERMS * NTA;
     constexpr int D = 2;
-    // lane (token r16 of tile n, group kg): 32 contiguous bytes = K 16kg..+15 and 64+16kg..+15
-    auto rd = [&](int f, int &sb) {
-      const int term = f / NTA, n = f % NTA;
-      const int tok = 16 * n + r16;
-      sb = (int)((slds(b)[term * CT + tok] >> (8 * kg)) & 0xFFu);
-      return *reinterpret_cast<const i32x8_t *>(qlds(b) + ((term * 4 + kg) * CT + (tok ^ kg)) * 32);
+    u32x4_t lo[D + 1], hi[D + 1];
+    uint32_t sc[D + 1];
+    auto issue = [&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      constexpr int term = f / NTA, n = f % NTA;
+      constexpr int QO = (term * 4 * CT + 16 * n) * 32, SO = (term * CT + 16 * n) * 4;
+      lds_read_frag<QO, SO>(qlane[b], slane[b], lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
     };
-    i32x8_t bq[D + 1];
-    int sbq[D + 1];
+    static_for<D>([&](auto fc) { issue(fc); });
+    static_for<F>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      constexpr int n = f % NTA;
+      if constexpr (f + D < F) issue(std::integral_constant<int, f + D>{});
+      constexpr int behind = (f + D < F) ? D : F - 1 - f;  // fragments issued after f
+      lds_wait_frag<3 * behind>(lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
+      const i32x8_t bq = __builtin_bit_cast(
+          i32x8_t, __builtin_shufflevector(lo[f % (D + 1)], hi[f % (D + 1)], 0, 1, 2, 3, 4, 5, 6, 7));
+      const int sb = (int)((sc[f % (D + 1)] >> (8 * kg)) & 0xFFu);
 #pragma unroll
-    for (int f = 0; f < D; ++f) bq[f] = rd(f, sbq[f]);
+      for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_mx_fp4_fp8(wq[b][t], bq, acc[t][n], sa[t], sb);
+      constexpr int J = (NOPS + F - 1) / F;
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const int n = f % NTA;
-      if (f + D < F) bq[(f + D) % (D + 1)] = rd(f + D, sbq[(f + D) % (D + 1)]);
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t)
-        acc[t][n] = mfma_mx_fp4_fp8(wq[b][t], bq[f % (D + 1)], acc[t][n], sa[t], sbq[f % (D + 1)]);
-      // keep the read-ahead distance as written: no LDS read moves across fragments
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, b2, s2);
+    });
   };
-  auto step = [&](int h, int s) {
-    load_a(s + 1);
-    compute(h);
-    load_w(h, s + 2);
-    store_a(h ^ 1);
-    __syncthreads();
+  // step s (ring slot b = s % 3): stage s+2's loads and weights of s+2 go out
+  // while s computes; then stage s+1 (requested a step earlier) must be in LDS
+  // for every wave before the barrier
+  auto step = [&](int b, int s) {
+    compute(b, (b + 2) % 3, min(s + 2, nks - 1));
+    // a bare barrier: a workgroup fence here would also wait for stage s+2
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(KQ + KS + 2 * NTILE));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);  // keep the next step's register work behind the wait
   };
 
-  load_w(0, 0);
-  load_a(0);
-  load_w(1, 1);
-  store_a(0);
-  __syncthreads();
+  load_all(0, 0);
+  load_all(1, 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NTILE + KQ + KS));  // stage 0 and weights 0 are here
+  __builtin_amdgcn_s_barrier();
   int s = 0;
-  for (; s + 1 < nks; s += 2) {
+  for (; s + 2 < nks; s += 3) {
     step(0, s);
     step(1, s + 1);
+    step(2, s + 2);
   }
   if (s < nks) step(0, s);
+  if (s + 1 < nks) step(1, s + 1);
+  // drain the loads past the last step before the LDS is reused
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   const int col_base = wrow_base + 4 * kg;
 #pragma unroll
@@ -513,7 +568,6 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *lds_base, 
           for (int r = 0; r < 4; ++r)
             if (col0 + r < N) cp[r] = g.accumulate ? cp[r] + v[r] : v[r];
         }
-        // one output group at a time: interleaving all of them costs registers
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -522,8 +576,12 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *lds_base, 
 
 template <bool PAIR, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
-  // two stages of [term][chunk][token][16] bytes + [term][token] scale dwords, then a trash slot per thread
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (3 * 8 * 16 * NT * 16 + 3 * 16 * NT * 4) + 64 * NW * 16];
+  // three activation stages (separate objects, so waits on one stage's loads
+  // do not cover the others) and the padding loads' target
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[mx_stage_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[mx_stage_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[mx_stage_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t dummy[MX_DUMMY_BYTES];
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
   const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
   const int logical = xcd_logical(total);
@@ -533,15 +591,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
   if (nta == NT) {
-    pfmx_item<PAIR, NT, MT, NW>(g, lds, c.x, c.y, c.z, nb);
+    pfmx_item<PAIR, NT, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb);
     return;
   }
   switch (nta) {
-    case 1: if constexpr (NT > 1) pfmx_item<PAIR, 1, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    case 2: if constexpr (NT > 2) pfmx_item<PAIR, 2, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    case 3: if constexpr (NT > 3) pfmx_item<PAIR, 3, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    case 4: if constexpr (NT > 4) pfmx_item<PAIR, 4, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
-    default: if constexpr (NT > 5) pfmx_item<PAIR, 5, MT, NW>(g, lds, c.x, c.y, c.z, nb); break;
+    case 1: if constexpr (NT > 1) pfmx_item<PAIR, 1, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 2: if constexpr (NT > 2) pfmx_item<PAIR, 2, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 3: if constexpr (NT > 3) pfmx_item<PAIR, 3, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 4: if constexpr (NT > 4) pfmx_item<PAIR, 4, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    default: if constexpr (NT > 5) pfmx_item<PAIR, 5, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
   }
 }
 
@@ -567,17 +625,19 @@ hipError_t launch_wf(int afmt, bool pair, const GemmArgs &a, long long grid, hip
 }  // namespace
 
 int prefill_rows_per_wg(bool pair) { return 16 * PREFILL_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
+int prefill_mx_rows_per_wg(bool pair) { return 16 * PREFILL_MX_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
 
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st) {
   if (afmt == A_MX8X3) {
     if (wfmt != W_MXFP4) return hipErrorInvalidValue;
+    // one wave per SIMD: the MX operands need the larger register budget
     if (pair)
-      hipLaunchKernelGGL((prefill_mx_kernel<true, PREFILL_NT, PREFILL_MT_PAIR, PREFILL_NW>), dim3((unsigned)grid),
-                         dim3(64 * PREFILL_NW), 0, st, a);
+      hipLaunchKernelGGL((prefill_mx_kernel<true, PREFILL_NT, PREFILL_MT_PAIR, PREFILL_MX_NW>), dim3((unsigned)grid),
+                         dim3(64 * PREFILL_MX_NW), 0, st, a);
     else
-      hipLaunchKernelGGL((prefill_mx_kernel<false, PREFILL_NT, PREFILL_MT_SINGLE, PREFILL_NW>), dim3((unsigned)grid),
-                         dim3(64 * PREFILL_NW), 0, st, a);
+      hipLaunchKernelGGL((prefill_mx_kernel<false, PREFILL_NT, PREFILL_MT_SINGLE, PREFILL_MX_NW>),
+                         dim3((unsigned)grid), dim3(64 * PREFILL_MX_NW), 0, st, a);
     return hipGetLastError();
   }
   return wfmt == W_MXFP4 ? launch_wf<W_MXFP4>(afmt, pair, a, grid, st) : launch_wf<W_BF16>(afmt, pair, a, grid, st);
