@@ -285,6 +285,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--operand-mode", default="bf16x2", choices=["bf16x2", "mx8x3", "mx6x3"],
+                    help="operand mode of the timed workload (the decode line's prefill extras cover all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--layers", type=int, default=4,
@@ -319,7 +321,8 @@ def main():
     layers = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(max(1, args.layers) - 1)]
     torch.cuda.synchronize()
     print("bench: timing", wl.name, file=sys.stderr, flush=True)
-    r = run_workload(mx, torch, synth, layers, wl, args.steps, args.warmup, args.cold_steps)
+    opnd = {"bf16x2": mx.MOE_OPND_BF16X2, "mx8x3": mx.MOE_OPND_MX8X3, "mx6x3": mx.MOE_OPND_MX6X3}[args.operand_mode]
+    r = run_workload(mx, torch, synth, layers, wl, args.steps, args.warmup, args.cold_steps, operand_mode=opnd)
     ms = 1e3 * r["wall_s"] / args.steps
     value = wl.tokens * args.steps / r["wall_s"]
 
@@ -361,7 +364,10 @@ def main():
                         f"{sh.n_shared} shared experts of {sh.shared_inter}",
             "tokens": wl.tokens,
             "operands": "MXFP4 expert weights (checkpoint bytes), bf16 dense weights, "
-                        "bf16 hi+lo split activations, fp32 accumulate, fp32 output",
+                        + {"bf16x2": "bf16 hi+lo split activations",
+                           "mx8x3": "expert GEMM activations as three e4m3 terms, other activations bf16 hi+lo",
+                           "mx6x3": "expert GEMM activations as three e2m3 terms, other activations bf16 hi+lo"}[
+                            args.operand_mode] + ", fp32 accumulate, fp32 output",
             "parallelism": "single GPU",
             "layers_rotated": len(layers),
         },
@@ -408,6 +414,21 @@ def main():
             "layer_mfma_frac_algorithmic": round(layer_flops / (mms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "gateup_tflops": round(gu_flops / (rm["dominant_ms"] * 1e-3) / 1e12, 1),
             "per_call_ms": {k: round(v, 4) for k, v in rm["per_call_ms"].items()},
+        }
+
+        # and with three fp6 (e2m3) activation terms, which the MX MFMA runs at the fp4 rate
+        print("bench: timing prefill, MX fp6 operand mode", file=sys.stderr, flush=True)
+        r6 = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2, breakdown_steps=2,
+                          operand_mode=mx.MOE_OPND_MX6X3)
+        m6 = 1e3 * r6["wall_s"] / max(2, args.steps // 5)
+        line["secondary_mx6x3"] = {
+            "workload": "prefill T=4096, expert GEMM activations as three e2m3 terms (operand mode MX6X3)",
+            "tokens_per_s": round(pf.tokens / (m6 * 1e-3), 1),
+            "ms_per_step": round(m6, 3),
+            "layer_tflops_algorithmic": round(layer_flops / (m6 * 1e-3) / 1e12, 1),
+            "layer_mfma_frac_algorithmic": round(layer_flops / (m6 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "gateup_tflops": round(gu_flops / (r6["dominant_ms"] * 1e-3) / 1e12, 1),
+            "per_call_ms": {k: round(v, 4) for k, v in r6["per_call_ms"].items()},
         }
 
     if args.calibrate_copy:

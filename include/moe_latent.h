@@ -58,6 +58,11 @@ extern "C" {
    A faster mode that departs from dequantise-to-bf16 arithmetic; its error
    against the exact layer is about 1e-4 of the output rms. */
 #define MOE_OPND_MX8X3 2
+/* As MOE_OPND_MX8X3 with three e2m3 (OCP MX fp6) terms per block of 32
+   (residual near 2^-12 of the block maximum): the MX MFMA runs fp4 x fp6 at
+   the fp4 rate, twice the fp8 rate.  Same departure from dequantise-to-bf16
+   arithmetic, error of the same order. */
+#define MOE_OPND_MX6X3 3
 
 /* mxfp4_grouped_gemm operations */
 #define MOE_OP_GATEUP_SITU 0
@@ -85,7 +90,7 @@ typedef struct {
   float beta;           /* SiTU-GLU gate saturation (4) */
   float beta_lin;       /* SiTU-GLU linear-branch saturation (25) */
   float rms_eps;        /* RMSNorm epsilon on the combined latent (1e-6) */
-  int32_t operand_mode; /* MOE_OPND_BF16X2, MOE_OPND_BF16 or MOE_OPND_MX8X3 */
+  int32_t operand_mode; /* MOE_OPND_BF16X2, MOE_OPND_BF16, MOE_OPND_MX8X3 or MOE_OPND_MX6X3 */
 } moe_shape;
 
 int moe_abi_version(void);

@@ -22,7 +22,7 @@ int check_shape(const moe_shape *s) {
       s->n_shared < 0 || s->shared_inter < 0)
     return MOE_EINVAL;
   if (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16 &&
-      s->operand_mode != MOE_OPND_MX8X3)
+      s->operand_mode != MOE_OPND_MX8X3 && s->operand_mode != MOE_OPND_MX6X3)
     return MOE_EINVAL;
   if (!(s->beta > 0.f) || !(s->beta_lin > 0.f) || !(s->rms_eps >= 0.f)) return MOE_EINVAL;
   if (s->top_k > s->n_experts) return MOE_EINVAL;
@@ -72,10 +72,11 @@ size_t permute_ws(const moe_shape *s, int T) {
   return align_up((size_t)permute_blocks(T) * s->n_experts * sizeof(int32_t));
 }
 
-// MX fp8 activation terms are used for fp32 activations on the tiled path,
-// while 3 term planes of P rows stay addressable with 32-bit offsets
+// MX activation terms (fp8 or fp6) are used for fp32 activations on the tiled
+// path, while 3 term planes of P rows stay addressable with 32-bit offsets
 bool use_mx8(const moe_shape *s, const GemmPlan &pl, int P, int K) {
-  return s->operand_mode == MOE_OPND_MX8X3 && pl.variant == 3 && 3LL * P * K < (1LL << 32) - 256;
+  return (s->operand_mode == MOE_OPND_MX8X3 || s->operand_mode == MOE_OPND_MX6X3) && pl.variant == 3 &&
+         3LL * P * K < (1LL << 32) - 256;
 }
 
 struct GroupedWs {
@@ -337,19 +338,20 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     a.beta_lin = s->beta_lin;
     int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
     if (a_dtype == MOE_DT_F32 && use_mx8(s, w.plan, P, K)) {
-      // split the fp32 activation rows into three MX fp8 terms, then the MX-scaled GEMM
+      // split the fp32 activation rows into three MX terms, then the MX-scaled GEMM
       // gate/up gathers rows of z [P / k, K] through sorted_pair; down reads H [P, K] in order
       const long long rows = (gateup && sorted_pair) ? (long long)(P / s->top_k) : (long long)P;
       uint8_t *mx = reinterpret_cast<uint8_t *>(wsp(ws, w.mx));
-      if (launch_mx8_split(static_cast<const float *>(A), K, (int)rows, K, mx, st) != hipSuccess)
+      const bool fp6 = s->operand_mode == MOE_OPND_MX6X3;
+      if (launch_mx_split(fp6, static_cast<const float *>(A), K, (int)rows, K, mx, st) != hipSuccess)
         return MOE_EHIP;
       a.mxq = mx;
       a.mxs = mx + (size_t)rows * K * 3;
       a.mx_rows = rows;
-      afmt = A_MX8X3;
+      afmt = fp6 ? A_MX6X3 : A_MX8X3;
     }
     GemmPlan pl = w.plan;
-    if (afmt == A_MX8X3) {
+    if (afmt == A_MX8X3 || afmt == A_MX6X3) {
       // the MX kernel covers fewer weight rows per work-group
       pl.n_blocks = (N + prefill_mx_rows_per_wg(gateup) - 1) / prefill_mx_rows_per_wg(gateup);
       pl.grid_logical = (long long)pl.max_chunks * pl.n_blocks;

@@ -9,7 +9,7 @@ namespace moe {
 
 // weight formats, activation formats
 enum { W_BF16 = 0, W_MXFP4 = 1 };
-enum { A_BF16 = 0, A_F32_SPLIT = 1, A_F32_ROUND = 2, A_MX8X3 = 3 };
+enum { A_BF16 = 0, A_F32_SPLIT = 1, A_F32_ROUND = 2, A_MX8X3 = 3, A_MX6X3 = 4 };
 
 // Weight-stationary GEMM: C[row, n] (+)= sum_k A[row, k] * W[n, k] over a
 // list of row chunks, optionally with two weight matrices combined by
@@ -36,8 +36,9 @@ struct GemmArgs {
   float *partial;         // split-K partial sums [splits][partial_rows][ncols]
   int partial_rows;
   float beta, beta_lin;
-  // MX fp8 activations (A_MX8X3): three e4m3 term planes [3][mx_rows][K] and
-  // their e8m0 block scales [3][mx_rows][K/32]; A is unused then
+  // MX activations (A_MX8X3, A_MX6X3): three e4m3 or packed e2m3 term planes
+  // [3][mx_rows][K] and their e8m0 block scales [3][mx_rows][K/32]; A is
+  // unused then
   const uint8_t *mxq, *mxs;
   long long mx_rows;
 };
@@ -70,6 +71,8 @@ constexpr int PREFILL_MT_PAIR = 2;
 constexpr int PREFILL_MT_SINGLE = 4;
 constexpr int PREFILL_NW = 8;
 constexpr int PREFILL_MX_NW = 4;  // MX-scaled variant: one wave per SIMD
+constexpr int PREFILL_MX_MT_PAIR = 4;
+constexpr int PREFILL_MX_MT_SINGLE = 8;
 
 // kernel variant selection (host side)
 struct GemmPlan {
@@ -97,7 +100,8 @@ int prefill_mx_rows_per_wg(bool pair);
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st);
 size_t mx8_split_bytes(long long rows, int K);
-hipError_t launch_mx8_split(const float *A, long long lda, int rows, int K, uint8_t *ws, hipStream_t st);
+hipError_t launch_mx_split(bool fp6, const float *A, long long lda, int rows, int K, uint8_t *ws,
+                           hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                               hipStream_t st);
 

@@ -322,12 +322,32 @@ MOE_DEV f32x4_t mfma_mx_fp4_fp8(u32x4_t w, i32x8_t b, f32x4_t c, int sa, int sb)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
 }
 
-// LDS bytes of one activation stage with NT token tiles: fp8 terms
-// [term][K group g][token ^ g][half][16] and block scales [term][token] (dwords,
-// padded to whole wave loads)
+// fp4 weights x e2m3 activations (format code 2): the fp6 operand is six
+// registers, 32 codes of K 32*(lane/16) .. +31 packed LSB first (checked on
+// the GPU against random operands); the instruction runs at the fp4 rate.
+MOE_DEV f32x4_t mfma_mx_fp4_fp6(u32x4_t w, u32x4_t blo, u32x2_t bhi, f32x4_t c, int sa, int sb) {
+  const i32x4_t w4 = __builtin_bit_cast(i32x4_t, w);
+  const i32x8_t a = __builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1);
+  const u32x4_t h4 = __builtin_shufflevector(bhi, bhi, 0, 1, -1, -1);
+  const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(blo, h4, 0, 1, 2, 3, 4, 5, -1, -1));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, sa, 0, sb);
+}
+
+// LDS bytes of one activation stage with NT token tiles: term bytes
+// [term][token][slot][16] and block scales [term][token] (dwords, padded to
+// whole wave loads).  A token's 128 bytes of one K step are eight 16-byte
+// parts; part p sits in slot p ^ (token & 7).  fp8: part g + 4h is K 16g +
+// 64h .. +15; fp6: parts 2g and 2g + 1 are the 32-byte slot of block g (24
+// code bytes, then padding that is loaded but never read).  Eight lanes load
+// one token's whole 128-byte line, and the eight tokens a fragment read
+// serves at a time hit eight different slots, so the reads are free of bank
+// conflicts.
 constexpr int mx_q_bytes(int nt) { return 3 * 4 * 16 * nt * 32; }
 constexpr int mx_s_bytes(int nt) { return (3 * 16 * nt * 4 + 255) / 256 * 256; }
-constexpr int mx_stage_bytes(int nt) { return mx_q_bytes(nt) + mx_s_bytes(nt); }
+// the step's e8m0 weight-scale dwords of the work-group's weight rows, [matrix][row]
+constexpr int MX_WS_BYTES = 2 * 16 * PREFILL_MX_NW * PREFILL_MX_MT_PAIR * 4;
+static_assert(MX_WS_BYTES == 16 * PREFILL_MX_NW * PREFILL_MX_MT_SINGLE * 4, "one scale area for both shapes");
+constexpr int mx_stage_bytes(int nt) { return mx_q_bytes(nt) + mx_s_bytes(nt) + MX_WS_BYTES; }
 constexpr int MX_DUMMY_BYTES = 8 * 1024;  // target of the padding loads
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -344,15 +364,16 @@ MOE_DEV void static_for(Fn &&fn) {
 
 MOE_DEV uint32_t lds_addr(uint8_t *p) { return (uint32_t)(uintptr_t)(lds_void *)p; }
 
-// 32 activation bytes at qa + QO and a scale dword at sa + SO, issued without waiting
+// 16 activation bytes at ql + QO, 16 more at qh + QO and a scale dword at
+// sa + SO, issued without waiting
 template <int QO, int SO>
-MOE_DEV void lds_read_frag(uint32_t qa, uint32_t sa, u32x4_t &lo, u32x4_t &hi, uint32_t &sc) {
+MOE_DEV void lds_read_frag(uint32_t ql, uint32_t qh, uint32_t sa, u32x4_t &lo, u32x4_t &hi, uint32_t &sc) {
   asm volatile(
-      "ds_read_b128 %0, %3 offset:%5\n\t"
-      "ds_read_b128 %1, %3 offset:%6\n\t"
-      "ds_read_b32 %2, %4 offset:%7"
+      "ds_read_b128 %0, %3 offset:%6\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b32 %2, %5 offset:%7"
       : "=&v"(lo), "=&v"(hi), "=&v"(sc)
-      : "v"(qa), "v"(sa), "n"(QO), "n"(QO + 16), "n"(SO)
+      : "v"(ql), "v"(qh), "v"(sa), "n"(QO), "n"(SO)
       : "memory");
 }
 
@@ -364,7 +385,31 @@ MOE_DEV void lds_wait_frag(u32x4_t &lo, u32x4_t &hi, uint32_t &sc) {
   asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo), "+v"(hi), "+v"(sc) : "n"(N) : "memory");
 }
 
-template <bool PAIR, int NTA, int MT, int NW>
+// the weight-scale dword at wa + WO (one per row; the four lanes of a row read
+// the same dword), issued without waiting
+template <int WO>
+MOE_DEV void lds_read_wscale(uint32_t wa, uint32_t &w) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=&v"(w) : "v"(wa), "n"(WO) : "memory");
+}
+
+// fp6 fragment: the 24 code bytes of a lane's block (16 at ql + QO, 8 at qh + QO)
+template <int QO, int SO>
+MOE_DEV void lds_read_frag6(uint32_t ql, uint32_t qh, uint32_t sa, u32x4_t &lo, u32x2_t &hi, uint32_t &sc) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:%6\n\t"
+      "ds_read_b64 %1, %4 offset:%6\n\t"
+      "ds_read_b32 %2, %5 offset:%7"
+      : "=&v"(lo), "=&v"(hi), "=&v"(sc)
+      : "v"(ql), "v"(qh), "v"(sa), "n"(QO), "n"(SO)
+      : "memory");
+}
+template <int N>
+MOE_DEV void lds_wait_frag6(u32x4_t &lo, u32x2_t &hi, uint32_t &sc) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo), "+v"(hi), "+v"(sc) : "n"(N) : "memory");
+}
+
+template <bool FP6, bool PAIR, int NTA, int MT, int NW>
 __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8_t *st1, uint8_t *st2,
                                           uint8_t *dummy, int expert, int row0, int nrows, int nb) {
   constexpr int NMAT = PAIR ? 2 : 1;
@@ -377,6 +422,10 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   constexpr int SI = mx_s_bytes(NTA) / 256;       // 256-byte wave loads per stage for the scales
   constexpr int KQ = (QI + NW - 1) / NW;          // per wave, equal for all waves
   constexpr int KS = (SI + NW - 1) / NW;
+  constexpr int WSO = QB + mx_s_bytes(NTA);        // weight scales in a stage
+  constexpr int WSI = NMAT * ROWS_WG * 4 / 256;    // 256-byte wave loads per stage for them
+  constexpr int KW = (WSI + NW - 1) / NW;
+  static_assert(NMAT * ROWS_WG * 4 == MX_WS_BYTES && WSI % NW == 0 && ROWS_WG % 64 == 0, "weight-scale loads");
   static_assert((KQ * NW - QI) * 1024 + (KS * NW - SI) * 256 <= MX_DUMMY_BYTES, "dummy area");
   uint8_t *stage[3] = {st0, st1, st2};
 
@@ -388,7 +437,8 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   const int N = g.N, K = g.K;
   const int nks = K / KSTEP;
 
-  // ---- weights: a three-deep register ring, two steps ahead
+  // ---- weights: a three-deep register ring, two steps ahead.  Their scales
+  // go through the LDS stage: one 4-byte load per row instead of one per lane.
   const uint32_t row_bytes = K / 2, srow_bytes = K / 32;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
@@ -398,24 +448,32 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
     sr[mat] = make_rsrc((mat ? g.S1 : g.S0) + expert * g.s_estride, (uint32_t)N * srow_bytes);
   }
   const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
-  uint32_t woff[NTILE], soff[NTILE];
+  uint32_t woff[NTILE];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
     const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
     woff[t] = (uint32_t)n * row_bytes + kg * 16;
-    soff[t] = (uint32_t)n * srow_bytes;
   }
   u32x4_t wq[3][NTILE];
-  uint32_t wsc[3][NTILE];
-  auto load_w_tile = [&](int b, int t, int s) {
-    wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
-    wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
+  auto load_w_tile = [&](int b, int t, int s) { wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u); };
+  // weight-scale load k of this wave: rows [64 (wave + NW k), +64) of [matrix][row]
+  uint32_t wsoff[KW];
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int q = 64 * (wave + NW * k) + lane;
+    const int n = min(nb * ROWS_WG + q % ROWS_WG, N - 1);
+    wsoff[k] = (uint32_t)n * srow_bytes;
+  }
+  auto load_ws = [&](int b, int k, int s) {
+    const int ii = wave + NW * k;  // uniform: the whole load is in one matrix
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr[(ii * 64) / ROWS_WG], (lds_void *)(stage[b] + WSO + ii * 256), 4,
+                                             wsoff[k], (uint32_t)s * 4u, 0, 0);
   };
 
   // ---- activation terms, loaded straight into LDS: wave load k of this wave
   // covers 16-byte slots [64 (wave + NW k), +64); slot q of a stage is (term,
-  // g, token ^ g, half).  Rows past the chunk repeat its first row (their
-  // columns are never stored).
+  // token, slot); eight consecutive lanes fetch one token's 128-byte line.
+  // Rows past the chunk repeat its first row (their columns are never stored).
   const uint32_t plane = (uint32_t)(g.mx_rows * K), splane = (uint32_t)(g.mx_rows * (K / 32));
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(g.mxq, 3u * plane);
   const __amdgpu_buffer_rsrc_t sr8 = make_rsrc(g.mxs, 3u * splane);
@@ -428,9 +486,8 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   for (int k = 0; k < KQ; ++k) {
     const int q = 64 * (wave + NW * k) + lane;
     const int term = q / (8 * CT), rem = q - term * 8 * CT;
-    const int gg = rem / (2 * CT), rem2 = rem - gg * 2 * CT;
-    const int tok = (rem2 >> 1) ^ gg, half = rem2 & 1;
-    qoff[k] = q < QB / 16 ? (uint32_t)(term * (long long)plane + arow_of(tok) * K + (gg + 4 * half) * 16) : 0u;
+    const int tok = rem >> 3, part = (rem & 7) ^ (tok & 7);  // 16-byte part of the token's 128-wide step
+    qoff[k] = q < QB / 16 ? (uint32_t)(term * (long long)plane + arow_of(tok) * K + part * 16) : 0u;
   }
   uint32_t soffs[KS];
 #pragma unroll
@@ -449,13 +506,14 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
     uint8_t *dst = ii < SI ? stage[b] + QB + ii * 256 : dummy + MX_DUMMY_BYTES / 2 + (ii - SI) * 256;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sr8, (lds_void *)dst, 4, soffs[k], (uint32_t)s * 4u, 0, 0);
   };
-  // the memory operations that fill ring slot b with step s: KQ + KS loads into
-  // LDS and NTILE weight tiles (two loads each)
-  constexpr int NOPS = KQ + KS + NTILE;
+  // the memory operations that fill ring slot b with step s: KQ + KS + KW
+  // loads into LDS and NTILE weight tiles
+  constexpr int NOPS = KQ + KS + KW + NTILE;
   auto issue_op = [&](int o, int b, int s) {
     if (o < KQ) load_q(b, o, s);
     else if (o < KQ + KS) load_s(b, o - KQ, s);
-    else load_w_tile(b, o - KQ - KS, s);
+    else if (o < KQ + KS + KW) load_ws(b, o - KQ - KS, s);
+    else load_w_tile(b, o - KQ - KS - KW, s);
   };
   auto load_all = [&](int b, int s) {
     s = min(s, nks - 1);
@@ -472,30 +530,41 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   // LDS reads of the activation fragments are written as inline assembly with
   // explicit lgkmcnt waits: the compiler would otherwise wait for every load
   // into LDS still in flight (it cannot tell the stages apart) before each read.
-  // Fragment f = (term, token tile n); lane (token r16, group kg) reads 32
-  // contiguous bytes (K 16kg..+15 and 64+16kg..+15) and its token's scale dword.
-  uint32_t qlane[3], slane[3];
+  // Fragment f = (term, token tile n); lane (token r16, group kg) reads the two
+  // 16-byte parts of its token and group and its token's scale dword.
+  const int plo = FP6 ? 2 * kg : kg, phi = FP6 ? 2 * kg + 1 : kg + 4;
+  uint32_t qlo[3], qhi[3], slane[3], wlane[3];
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
-    qlane[b] = lds_addr(stage[b]) + (uint32_t)((kg * CT + (r16 ^ kg)) * 32);
+    wlane[b] = lds_addr(stage[b]) + (uint32_t)(WSO + (wave * 16 * MT + r16) * 4);
+    qlo[b] = lds_addr(stage[b]) + (uint32_t)(r16 * 128 + ((plo ^ (r16 & 7)) << 4));
+    qhi[b] = lds_addr(stage[b]) + (uint32_t)(r16 * 128 + ((phi ^ (r16 & 7)) << 4));
     slane[b] = lds_addr(stage[b]) + (uint32_t)(QB + r16 * 4);
   }
   // compute step s from slot b; after each fragment's products a share of the
   // loads of step s + 2 (into slot b2) goes out, so that no wave stalls on a
   // burst of memory instructions
   auto compute = [&](int b, int b2, int s2) {
+    // weight scales first: the wait for the first fragment covers them
+    uint32_t wsv[NTILE];
+    static_for<NTILE>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      lds_read_wscale<((t / MT) * ROWS_WG + (t % MT) * 16) * 4>(wlane[b], wsv[t]);
+    });
     int sa[NTILE];
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) sa[t] = (int)((wsc[b][t] >> (8 * kg)) & 0xFFu);
     constexpr int F = TERMS * NTA;
     constexpr int D = 2;
     u32x4_t lo[D + 1], hi[D + 1];
+    u32x2_t hi6[D + 1];
     uint32_t sc[D + 1];
     auto issue = [&](auto fc) {
       constexpr int f = decltype(fc)::value;
       constexpr int term = f / NTA, n = f % NTA;
-      constexpr int QO = (term * 4 * CT + 16 * n) * 32, SO = (term * CT + 16 * n) * 4;
-      lds_read_frag<QO, SO>(qlane[b], slane[b], lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
+      constexpr int QO = (term * CT + 16 * n) * 128, SO = (term * CT + 16 * n) * 4;
+      if constexpr (FP6)
+        lds_read_frag6<QO, SO>(qlo[b], qhi[b], slane[b], lo[f % (D + 1)], hi6[f % (D + 1)], sc[f % (D + 1)]);
+      else
+        lds_read_frag<QO, SO>(qlo[b], qhi[b], slane[b], lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
     };
     static_for<D>([&](auto fc) { issue(fc); });
     static_for<F>([&](auto fc) {
@@ -503,12 +572,31 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
       constexpr int n = f % NTA;
       if constexpr (f + D < F) issue(std::integral_constant<int, f + D>{});
       constexpr int behind = (f + D < F) ? D : F - 1 - f;  // fragments issued after f
-      lds_wait_frag<3 * behind>(lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
-      const i32x8_t bq = __builtin_bit_cast(
-          i32x8_t, __builtin_shufflevector(lo[f % (D + 1)], hi[f % (D + 1)], 0, 1, 2, 3, 4, 5, 6, 7));
-      const int sb = (int)((sc[f % (D + 1)] >> (8 * kg)) & 0xFFu);
+      auto scales_ready = [&]() {
+        if constexpr (f == 0) {
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_mx_fp4_fp8(wq[b][t], bq, acc[t][n], sa[t], sb);
+          for (int t = 0; t < NTILE; ++t) {
+            asm volatile("" : "+v"(wsv[t]));  // after the first fragment's wait
+            sa[t] = (int)((wsv[t] >> (8 * kg)) & 0xFFu);
+          }
+        }
+      };
+      if constexpr (FP6) {
+        lds_wait_frag6<3 * behind>(lo[f % (D + 1)], hi6[f % (D + 1)], sc[f % (D + 1)]);
+        scales_ready();
+        const int sb = (int)((sc[f % (D + 1)] >> (8 * kg)) & 0xFFu);
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t)
+          acc[t][n] = mfma_mx_fp4_fp6(wq[b][t], lo[f % (D + 1)], hi6[f % (D + 1)], acc[t][n], sa[t], sb);
+      } else {
+        lds_wait_frag<3 * behind>(lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
+        scales_ready();
+        const int sb = (int)((sc[f % (D + 1)] >> (8 * kg)) & 0xFFu);
+        const i32x8_t bq = __builtin_bit_cast(
+            i32x8_t, __builtin_shufflevector(lo[f % (D + 1)], hi[f % (D + 1)], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_mx_fp4_fp8(wq[b][t], bq, acc[t][n], sa[t], sb);
+      }
       constexpr int J = (NOPS + F - 1) / F;
 #pragma unroll
       for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, b2, s2);
@@ -520,14 +608,14 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   auto step = [&](int b, int s) {
     compute(b, (b + 2) % 3, min(s + 2, nks - 1));
     // a bare barrier: a workgroup fence here would also wait for stage s+2
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(KQ + KS + 2 * NTILE));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NOPS));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);  // keep the next step's register work behind the wait
   };
 
   load_all(0, 0);
   load_all(1, 1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NTILE + KQ + KS));  // stage 0 and weights 0 are here
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NOPS));  // stage 0 and weights 0 are here
   __builtin_amdgcn_s_barrier();
   int s = 0;
   for (; s + 2 < nks; s += 3) {
@@ -574,7 +662,7 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   }
 }
 
-template <bool PAIR, int NT, int MT, int NW>
+template <bool FP6, bool PAIR, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   // three activation stages (separate objects, so waits on one stage's loads
   // do not cover the others) and the padding loads' target
@@ -591,15 +679,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
   if (nta == NT) {
-    pfmx_item<PAIR, NT, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb);
+    pfmx_item<FP6, PAIR, NT, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb);
     return;
   }
   switch (nta) {
-    case 1: if constexpr (NT > 1) pfmx_item<PAIR, 1, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    case 2: if constexpr (NT > 2) pfmx_item<PAIR, 2, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    case 3: if constexpr (NT > 3) pfmx_item<PAIR, 3, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    case 4: if constexpr (NT > 4) pfmx_item<PAIR, 4, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    default: if constexpr (NT > 5) pfmx_item<PAIR, 5, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 1: if constexpr (NT > 1) pfmx_item<FP6, PAIR, 1, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 2: if constexpr (NT > 2) pfmx_item<FP6, PAIR, 2, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 3: if constexpr (NT > 3) pfmx_item<FP6, PAIR, 3, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 4: if constexpr (NT > 4) pfmx_item<FP6, PAIR, 4, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    default: if constexpr (NT > 5) pfmx_item<FP6, PAIR, 5, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
   }
 }
 
@@ -625,19 +713,21 @@ hipError_t launch_wf(int afmt, bool pair, const GemmArgs &a, long long grid, hip
 }  // namespace
 
 int prefill_rows_per_wg(bool pair) { return 16 * PREFILL_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
-int prefill_mx_rows_per_wg(bool pair) { return 16 * PREFILL_MX_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
+int prefill_mx_rows_per_wg(bool pair) { return 16 * PREFILL_MX_NW * (pair ? PREFILL_MX_MT_PAIR : PREFILL_MX_MT_SINGLE); }
 
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st) {
-  if (afmt == A_MX8X3) {
+  if (afmt == A_MX8X3 || afmt == A_MX6X3) {
     if (wfmt != W_MXFP4) return hipErrorInvalidValue;
     // one wave per SIMD: the MX operands need the larger register budget
-    if (pair)
-      hipLaunchKernelGGL((prefill_mx_kernel<true, PREFILL_NT, PREFILL_MT_PAIR, PREFILL_MX_NW>), dim3((unsigned)grid),
-                         dim3(64 * PREFILL_MX_NW), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_mx_kernel<false, PREFILL_NT, PREFILL_MT_SINGLE, PREFILL_MX_NW>),
-                         dim3((unsigned)grid), dim3(64 * PREFILL_MX_NW), 0, st, a);
+    const dim3 gr((unsigned)grid), blk(64 * PREFILL_MX_NW);
+    if (afmt == A_MX6X3) {
+      if (pair) hipLaunchKernelGGL((prefill_mx_kernel<true, true, PREFILL_NT, PREFILL_MX_MT_PAIR, PREFILL_MX_NW>), gr, blk, 0, st, a);
+      else hipLaunchKernelGGL((prefill_mx_kernel<true, false, PREFILL_NT, PREFILL_MX_MT_SINGLE, PREFILL_MX_NW>), gr, blk, 0, st, a);
+    } else {
+      if (pair) hipLaunchKernelGGL((prefill_mx_kernel<false, true, PREFILL_NT, PREFILL_MX_MT_PAIR, PREFILL_MX_NW>), gr, blk, 0, st, a);
+      else hipLaunchKernelGGL((prefill_mx_kernel<false, false, PREFILL_NT, PREFILL_MX_MT_SINGLE, PREFILL_MX_NW>), gr, blk, 0, st, a);
+    }
     return hipGetLastError();
   }
   return wfmt == W_MXFP4 ? launch_wf<W_MXFP4>(afmt, pair, a, grid, st) : launch_wf<W_BF16>(afmt, pair, a, grid, st);

@@ -107,6 +107,16 @@ def test_prefill_T4096_mx8x3(mx, k3):
     assert err < 2e-3
 
 
+def test_prefill_T4096_mx6x3(mx, k3):
+    """Prefill through the MX-scaled expert GEMMs (three fp6 activation terms)."""
+    from mxfp4_latent_moe_amd import _lib
+    wl = synth.workload("prefill")
+    bias = synth.gen_bias(wl)
+    err = _full_check(mx, k3, wl, bias, np.array([2, 2500, 4093]), "prefill mx6x3", _lib.MOE_OPND_MX6X3,
+                      inter_tol=2e-3)
+    assert err < 2e-3
+
+
 def test_microbench_grouped_gemm(mx, k3):
     """Isolated grouped GEMM: segments ~ Multinomial(65536, Zipf(1.1)); A bf16 already permuted."""
     from mxfp4_latent_moe_amd import ops

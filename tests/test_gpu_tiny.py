@@ -226,3 +226,25 @@ def test_tiny_mx8x3_operand_mode(mx):
     say(f"tiny mx8x3: H {errH:.3e}, out {err:.3e}")
     assert err <= TOL
     assert err < 2e-3 and errH < 2e-3
+
+
+def test_tiny_mx6x3_operand_mode(mx):
+    """As the fp8 case, with the activations as three fp6 (e2m3) terms."""
+    from mxfp4_latent_moe_amd import _lib
+    wl = synth.workload("tiny")
+    x_bits = synth.gen_tokens(synth.Workload("tiny37", 11, wl.shape, 37, wl.wset, wl.router_std, wl.bias_std,
+                                             "normal", wl.exp_lo, wl.exp_hi))
+    d = synth.gen_dense(wl)
+    b = synth.gen_bias(wl)
+    st = synth.gen_expert_stack(wl)
+    say("case: tiny T=37, operand mode mx6x3")
+    g = _run(mx, wl, x_bits, operand_mode=_lib.MOE_OPND_MX6X3)
+    ref = _oracle(wl, x_bits, d, b, st)
+    excl = check_routing(g["topk_ids"], g["topk_w"], ref)
+    check_permutation(g, ref["ids"], wl.shape.n_experts, excl)
+    errH = rel_max_err(g["H"], ref["H_sorted"])
+    err = rel_max_err(g["out"], ref["out"])
+    say(f"tiny mx6x3: H {errH:.3e}, out {err:.3e}")
+    assert err <= TOL
+    # three e2m3 terms leave about 2^-12 of each 32-block's maximum, as three e4m3 terms do
+    assert err < 2e-3 and errH < 2e-3
