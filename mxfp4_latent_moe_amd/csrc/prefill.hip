@@ -343,11 +343,14 @@ MOE_DEV f32x4_t mfma_mx_fp4_fp6(u32x4_t w, u32x4_t blo, u32x2_t bhi, f32x4_t c, 
 // serves at a time hit eight different slots, so the reads are free of bank
 // conflicts.
 constexpr int mx_q_bytes(int nt) { return 3 * 4 * 16 * nt * 32; }
-constexpr int mx_s_bytes(int nt) { return (3 * 16 * nt * 4 + 255) / 256 * 256; }
-// the step's e8m0 weight-scale dwords of the work-group's weight rows, [matrix][row]
-constexpr int MX_WS_BYTES = 2 * 16 * PREFILL_MX_NW * PREFILL_MX_MT_PAIR * 4;
-static_assert(MX_WS_BYTES == 16 * PREFILL_MX_NW * PREFILL_MX_MT_SINGLE * 4, "one scale area for both shapes");
-constexpr int mx_stage_bytes(int nt) { return mx_q_bytes(nt) + mx_s_bytes(nt) + MX_WS_BYTES; }
+// Scale groups: the e8m0 scales of four consecutive K steps (16 bytes of a
+// row) are loaded once per group, a 16-byte load per row, into one of two
+// group buffers: activation scales [term][token][16] (padded to whole 1 KB
+// wave loads), then weight scales [matrix][row][16] of the work-group's rows.
+constexpr int mx_gsa_bytes(int nt) { return (3 * 16 * nt * 16 + 1023) / 1024 * 1024; }
+constexpr int MX_GSW_BYTES = 2 * 16 * PREFILL_MX_NW * PREFILL_MX_MT_PAIR * 16;
+static_assert(MX_GSW_BYTES == 16 * PREFILL_MX_NW * PREFILL_MX_MT_SINGLE * 16, "one scale area for both shapes");
+constexpr int mx_group_bytes(int nt) { return mx_gsa_bytes(nt) + MX_GSW_BYTES; }
 constexpr int MX_DUMMY_BYTES = 8 * 1024;  // target of the padding loads
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -385,8 +388,8 @@ MOE_DEV void lds_wait_frag(u32x4_t &lo, u32x4_t &hi, uint32_t &sc) {
   asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo), "+v"(hi), "+v"(sc) : "n"(N) : "memory");
 }
 
-// the weight-scale dword at wa + WO (one per row; the four lanes of a row read
-// the same dword), issued without waiting
+// a weight-scale dword at wa + WO (the four lanes of a row read the same
+// dword), issued without waiting
 template <int WO>
 MOE_DEV void lds_read_wscale(uint32_t wa, uint32_t &w) {
   asm volatile("ds_read_b32 %0, %1 offset:%2" : "=&v"(w) : "v"(wa), "n"(WO) : "memory");
@@ -411,7 +414,8 @@ MOE_DEV void lds_wait_frag6(u32x4_t &lo, u32x2_t &hi, uint32_t &sc) {
 
 template <bool FP6, bool PAIR, int NTA, int MT, int NW>
 __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8_t *st1, uint8_t *st2,
-                                          uint8_t *dummy, int expert, int row0, int nrows, int nb) {
+                                          uint8_t *grp0, uint8_t *dummy, int expert, int row0, int nrows,
+                                          int nb) {
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
   constexpr int CT = 16 * NTA;
@@ -419,14 +423,16 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   constexpr int TERMS = 3;
   constexpr int QB = mx_q_bytes(NTA);
   constexpr int QI = QB / 1024;                   // 1 KB wave loads per stage for the terms
-  constexpr int SI = mx_s_bytes(NTA) / 256;       // 256-byte wave loads per stage for the scales
   constexpr int KQ = (QI + NW - 1) / NW;          // per wave, equal for all waves
-  constexpr int KS = (SI + NW - 1) / NW;
-  constexpr int WSO = QB + mx_s_bytes(NTA);        // weight scales in a stage
-  constexpr int WSI = NMAT * ROWS_WG * 4 / 256;    // 256-byte wave loads per stage for them
-  constexpr int KW = (WSI + NW - 1) / NW;
-  static_assert(NMAT * ROWS_WG * 4 == MX_WS_BYTES && WSI % NW == 0 && ROWS_WG % 64 == 0, "weight-scale loads");
-  static_assert((KQ * NW - QI) * 1024 + (KS * NW - SI) * 256 <= MX_DUMMY_BYTES, "dummy area");
+  constexpr int GAI = mx_gsa_bytes(NTA) / 1024;    // 1 KB wave loads per group, activation scales
+  constexpr int KGA = (GAI + NW - 1) / NW;
+  constexpr int GSA = mx_gsa_bytes(PREFILL_NT);    // weight scales in a group buffer
+  constexpr int GB = mx_group_bytes(PREFILL_NT);   // bytes of a group buffer
+  constexpr int GWI = NMAT * ROWS_WG * 16 / 1024;  // 1 KB wave loads per group, weight scales
+  constexpr int KGW = GWI / NW;
+  static_assert(NMAT * ROWS_WG * 16 == MX_GSW_BYTES && GWI % NW == 0 && ROWS_WG % 64 == 0, "weight-scale loads");
+  static_assert((KQ * NW - QI) * 1024 <= MX_DUMMY_BYTES / 2 && (KGA * NW - GAI) * 1024 <= MX_DUMMY_BYTES / 2,
+                "dummy area");
   uint8_t *stage[3] = {st0, st1, st2};
 
   const int tid = threadIdx.x;
@@ -438,7 +444,7 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   const int nks = K / KSTEP;
 
   // ---- weights: a three-deep register ring, two steps ahead.  Their scales
-  // go through the LDS stage: one 4-byte load per row instead of one per lane.
+  // go through the LDS scale groups.
   const uint32_t row_bytes = K / 2, srow_bytes = K / 32;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
@@ -456,18 +462,18 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   }
   u32x4_t wq[3][NTILE];
   auto load_w_tile = [&](int b, int t, int s) { wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u); };
-  // weight-scale load k of this wave: rows [64 (wave + NW k), +64) of [matrix][row]
-  uint32_t wsoff[KW];
+  // weight-scale group load k of this wave: rows [64 (wave + NW k), +64) of [matrix][row]
+  uint32_t wsoff[KGW];
 #pragma unroll
-  for (int k = 0; k < KW; ++k) {
+  for (int k = 0; k < KGW; ++k) {
     const int q = 64 * (wave + NW * k) + lane;
     const int n = min(nb * ROWS_WG + q % ROWS_WG, N - 1);
     wsoff[k] = (uint32_t)n * srow_bytes;
   }
-  auto load_ws = [&](int b, int k, int s) {
+  auto load_gw = [&](uint8_t *grp, uint32_t oob, int k, int gi) {
     const int ii = wave + NW * k;  // uniform: the whole load is in one matrix
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr[(ii * 64) / ROWS_WG], (lds_void *)(stage[b] + WSO + ii * 256), 4,
-                                             wsoff[k], (uint32_t)s * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr[(ii * 64) / ROWS_WG], (lds_void *)(grp + GSA + ii * 1024), 16,
+                                             wsoff[k] | oob, (uint32_t)gi * 16u, 0, 0);
   };
 
   // ---- activation terms, loaded straight into LDS: wave load k of this wave
@@ -489,9 +495,9 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
     const int tok = rem >> 3, part = (rem & 7) ^ (tok & 7);  // 16-byte part of the token's 128-wide step
     qoff[k] = q < QB / 16 ? (uint32_t)(term * (long long)plane + arow_of(tok) * K + part * 16) : 0u;
   }
-  uint32_t soffs[KS];
+  uint32_t soffs[KGA];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
+  for (int k = 0; k < KGA; ++k) {
     const int q = 64 * (wave + NW * k) + lane;
     const int term = q / CT, tok = q - term * CT;
     soffs[k] = q < TERMS * CT ? (uint32_t)(term * (long long)splane + arow_of(tok) * (K / 32)) : 0u;
@@ -501,21 +507,36 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
     uint8_t *dst = ii < QI ? stage[b] + ii * 1024 : dummy + (ii - QI) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)dst, 16, qoff[k], (uint32_t)s * 128u, 0, 0);
   };
-  auto load_s = [&](int b, int k, int s) {
+  auto load_ga = [&](uint8_t *grp, uint32_t oob, int k, int gi) {
     const int ii = wave + NW * k;
-    uint8_t *dst = ii < SI ? stage[b] + QB + ii * 256 : dummy + MX_DUMMY_BYTES / 2 + (ii - SI) * 256;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr8, (lds_void *)dst, 4, soffs[k], (uint32_t)s * 4u, 0, 0);
+    uint8_t *dst = ii < GAI ? grp + ii * 1024 : dummy + MX_DUMMY_BYTES / 2 + (ii - GAI) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr8, (lds_void *)dst, 16, soffs[k] | oob, (uint32_t)gi * 16u, 0, 0);
   };
-  // the memory operations that fill ring slot b with step s: KQ + KS + KW
-  // loads into LDS and NTILE weight tiles
-  constexpr int NOPS = KQ + KS + KW + NTILE;
+  // the memory operations that fill ring slot b with step s: KQ loads into LDS
+  // and NTILE weight tiles, after NG scale-group loads.  Those fetch group
+  // s / 4 into group buffer (s / 4) % 2 on the first step of a group; on the
+  // other steps their offsets lie past the end of the buffers, so they read
+  // nothing (out-of-range buffer loads return zero) and they write the zeros
+  // to the dummy area.  The same instruction count on every step keeps the
+  // unrolled steps free of branches.
+  constexpr int NOPS = KQ + NTILE;
+  constexpr int NG = KGA + KGW;
   auto issue_op = [&](int o, int b, int s) {
     if (o < KQ) load_q(b, o, s);
-    else if (o < KQ + KS) load_s(b, o - KQ, s);
-    else if (o < KQ + KS + KW) load_ws(b, o - KQ - KS, s);
-    else load_w_tile(b, o - KQ - KS - KW, s);
+    else load_w_tile(b, o - KQ, s);
+  };
+  auto load_group = [&](int s) {
+    const bool real = (s & 3) == 0 && s < nks;
+    const int gi = min(s, nks - 1) >> 2;
+    uint8_t *grp = real ? grp0 + (gi & 1) * GB : dummy;
+    const uint32_t oob = real ? 0u : 0x80000000u;
+#pragma unroll
+    for (int k = 0; k < KGA; ++k) load_ga(grp, oob, k, gi);
+#pragma unroll
+    for (int k = 0; k < KGW; ++k) load_gw(real ? grp : dummy - GSA, oob, k, gi);
   };
   auto load_all = [&](int b, int s) {
+    load_group(s);
     s = min(s, nks - 1);
 #pragma unroll
     for (int o = 0; o < NOPS; ++o) issue_op(o, b, s);
@@ -533,23 +554,29 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   // Fragment f = (term, token tile n); lane (token r16, group kg) reads the two
   // 16-byte parts of its token and group and its token's scale dword.
   const int plo = FP6 ? 2 * kg : kg, phi = FP6 ? 2 * kg + 1 : kg + 4;
-  uint32_t qlo[3], qhi[3], slane[3], wlane[3];
+  uint32_t qlo[3], qhi[3];
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
-    wlane[b] = lds_addr(stage[b]) + (uint32_t)(WSO + (wave * 16 * MT + r16) * 4);
     qlo[b] = lds_addr(stage[b]) + (uint32_t)(r16 * 128 + ((plo ^ (r16 & 7)) << 4));
     qhi[b] = lds_addr(stage[b]) + (uint32_t)(r16 * 128 + ((phi ^ (r16 & 7)) << 4));
-    slane[b] = lds_addr(stage[b]) + (uint32_t)(QB + r16 * 4);
   }
+  // scale dword of (token r16, step) and (weight row of this lane, step) in group buffer 0
+  const uint32_t sbase = lds_addr(grp0) + (uint32_t)(r16 * 16);
+  const uint32_t wbase = lds_addr(grp0) + (uint32_t)(GSA + (wave * 16 * MT + r16) * 16);
   // compute step s from slot b; after each fragment's products a share of the
   // loads of step s + 2 (into slot b2) goes out, so that no wave stalls on a
   // burst of memory instructions
-  auto compute = [&](int b, int b2, int s2) {
+  auto compute = [&](int b, int b2, int s) {
+    const int s2 = min(s + 2, nks - 1);
+    const uint32_t gsel = (uint32_t)(((s >> 2) & 1) * GB + (s & 3) * 4);
+    const uint32_t slane = sbase + gsel, wlane = wbase + gsel;
+    // the scales of step s + 2's group go out before this step's reads
+    load_group(s + 2);
     // weight scales first: the wait for the first fragment covers them
     uint32_t wsv[NTILE];
     static_for<NTILE>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
-      lds_read_wscale<((t / MT) * ROWS_WG + (t % MT) * 16) * 4>(wlane[b], wsv[t]);
+      lds_read_wscale<((t / MT) * ROWS_WG + (t % MT) * 16) * 16>(wlane, wsv[t]);
     });
     int sa[NTILE];
     constexpr int F = TERMS * NTA;
@@ -560,11 +587,11 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
     auto issue = [&](auto fc) {
       constexpr int f = decltype(fc)::value;
       constexpr int term = f / NTA, n = f % NTA;
-      constexpr int QO = (term * CT + 16 * n) * 128, SO = (term * CT + 16 * n) * 4;
+      constexpr int QO = (term * CT + 16 * n) * 128, SO = (term * CT + 16 * n) * 16;
       if constexpr (FP6)
-        lds_read_frag6<QO, SO>(qlo[b], qhi[b], slane[b], lo[f % (D + 1)], hi6[f % (D + 1)], sc[f % (D + 1)]);
+        lds_read_frag6<QO, SO>(qlo[b], qhi[b], slane, lo[f % (D + 1)], hi6[f % (D + 1)], sc[f % (D + 1)]);
       else
-        lds_read_frag<QO, SO>(qlo[b], qhi[b], slane[b], lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
+        lds_read_frag<QO, SO>(qlo[b], qhi[b], slane, lo[f % (D + 1)], hi[f % (D + 1)], sc[f % (D + 1)]);
     };
     static_for<D>([&](auto fc) { issue(fc); });
     static_for<F>([&](auto fc) {
@@ -606,16 +633,16 @@ __device__ __forceinline__ void pfmx_item(const GemmArgs &g, uint8_t *st0, uint8
   // while s computes; then stage s+1 (requested a step earlier) must be in LDS
   // for every wave before the barrier
   auto step = [&](int b, int s) {
-    compute(b, (b + 2) % 3, min(s + 2, nks - 1));
+    compute(b, (b + 2) % 3, s);
     // a bare barrier: a workgroup fence here would also wait for stage s+2
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NOPS));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NOPS + NG));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);  // keep the next step's register work behind the wait
   };
 
   load_all(0, 0);
   load_all(1, 1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NOPS));  // stage 0 and weights 0 are here
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NOPS + NG));  // stage 0, scale group 0 and weights 0 are here
   __builtin_amdgcn_s_barrier();
   int s = 0;
   for (; s + 2 < nks; s += 3) {
@@ -666,10 +693,12 @@ template <bool FP6, bool PAIR, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   // three activation stages (separate objects, so waits on one stage's loads
   // do not cover the others) and the padding loads' target
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[mx_stage_bytes(NT)];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[mx_stage_bytes(NT)];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[mx_stage_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[mx_q_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[mx_q_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[mx_q_bytes(NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t grp[2 * mx_group_bytes(NT)];
   __shared__ __attribute__((aligned(1024))) uint8_t dummy[MX_DUMMY_BYTES];
+  static_assert(NT == PREFILL_NT, "group buffer layout assumes the compiled tile count");
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
   const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
   const int logical = xcd_logical(total);
@@ -679,15 +708,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
   if (nta == NT) {
-    pfmx_item<FP6, PAIR, NT, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb);
+    pfmx_item<FP6, PAIR, NT, MT, NW>(g, st0, st1, st2, grp, dummy, c.x, c.y, c.z, nb);
     return;
   }
   switch (nta) {
-    case 1: if constexpr (NT > 1) pfmx_item<FP6, PAIR, 1, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    case 2: if constexpr (NT > 2) pfmx_item<FP6, PAIR, 2, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    case 3: if constexpr (NT > 3) pfmx_item<FP6, PAIR, 3, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    case 4: if constexpr (NT > 4) pfmx_item<FP6, PAIR, 4, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
-    default: if constexpr (NT > 5) pfmx_item<FP6, PAIR, 5, MT, NW>(g, st0, st1, st2, dummy, c.x, c.y, c.z, nb); break;
+    case 1: if constexpr (NT > 1) pfmx_item<FP6, PAIR, 1, MT, NW>(g, st0, st1, st2, grp, dummy, c.x, c.y, c.z, nb); break;
+    case 2: if constexpr (NT > 2) pfmx_item<FP6, PAIR, 2, MT, NW>(g, st0, st1, st2, grp, dummy, c.x, c.y, c.z, nb); break;
+    case 3: if constexpr (NT > 3) pfmx_item<FP6, PAIR, 3, MT, NW>(g, st0, st1, st2, grp, dummy, c.x, c.y, c.z, nb); break;
+    case 4: if constexpr (NT > 4) pfmx_item<FP6, PAIR, 4, MT, NW>(g, st0, st1, st2, grp, dummy, c.x, c.y, c.z, nb); break;
+    default: if constexpr (NT > 5) pfmx_item<FP6, PAIR, 5, MT, NW>(g, st0, st1, st2, grp, dummy, c.x, c.y, c.z, nb); break;
   }
 }
 
