@@ -97,8 +97,14 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
   return w;
 }
 
+// bf16 planes of fp32 activations for the dense tiled kernel (hi, then lo)
+size_t planes_bytes(const GemmPlan &pl, int rows, int K, int afmt) {
+  if (pl.variant != 4 || afmt == A_BF16) return 0;
+  return align_up((size_t)rows * K * 2 * (afmt == A_F32_SPLIT ? 2 : 1));
+}
+
 struct CombineWs {
-  size_t yn, partial, total;
+  size_t yn, partial, planes, total;
   GemmPlan pu;
 };
 CombineWs combine_ws(const moe_shape *s, int T) {
@@ -106,12 +112,13 @@ CombineWs combine_ws(const moe_shape *s, int T) {
   w.pu = plan_dense(T, s->hidden, s->latent, false);
   w.yn = 0;
   w.partial = align_up((size_t)T * s->latent * sizeof(float));
-  w.total = w.partial + align_up(w.pu.partial_bytes);
+  w.planes = w.partial + align_up(w.pu.partial_bytes);
+  w.total = w.planes + planes_bytes(w.pu, T, s->latent, afmt_of(s));
   return w;
 }
 
 struct SharedWs {
-  size_t hs, partial, total;
+  size_t hs, partial, planes, total;
   GemmPlan pgu, pdn;
 };
 SharedWs shared_ws(const moe_shape *s, int T) {
@@ -121,7 +128,8 @@ SharedWs shared_ws(const moe_shape *s, int T) {
   w.pdn = plan_dense(T, s->hidden, NS, false);
   w.hs = 0;
   w.partial = align_up((size_t)T * NS * sizeof(float));
-  w.total = w.partial + align_up(std::max(w.pgu.partial_bytes, w.pdn.partial_bytes));
+  w.planes = w.partial + align_up(std::max(w.pgu.partial_bytes, w.pdn.partial_bytes));
+  w.total = w.planes + planes_bytes(w.pdn, T, NS, afmt_of(s));
   return w;
 }
 
@@ -154,11 +162,25 @@ GemmArgs dense_args(const GemmPlan &pl, const void *A, long long lda, const void
   a.partial_rows = rows;
   a.beta = s->beta;
   a.beta_lin = s->beta_lin;
+  a.A2 = nullptr;
+  a.dense_rows_tiles = pl.variant == 4 ? pl.max_chunks : 0;
   return a;
 }
 
-// dense GEMM plus, for split K, the finalize pass
-hipError_t run_dense(const GemmPlan &pl, int afmt, bool pair, const GemmArgs &a, hipStream_t st) {
+// dense GEMM plus, for split K, the finalize pass.  The tiled kernel takes
+// fp32 activations as bf16 planes, written first into `planes`.
+hipError_t run_dense(const GemmPlan &pl, int afmt, bool pair, const GemmArgs &a0, void *planes,
+                     hipStream_t st) {
+  GemmArgs a = a0;
+  if (pl.variant == 4 && afmt != A_BF16) {
+    uint16_t *hi = static_cast<uint16_t *>(planes);
+    uint16_t *lo = afmt == A_F32_SPLIT ? hi + (size_t)a.dense_rows * a.K : nullptr;
+    hipError_t e = launch_split_planes(static_cast<const float *>(a.A), a.lda, a.dense_rows, a.K, hi, lo, st);
+    if (e != hipSuccess) return e;
+    a.A = hi;
+    a.A2 = lo;
+    a.lda = a.K;
+  }
   hipError_t e = launch_gemm(pl, W_BF16, afmt, pair, a, st);
   if (e != hipSuccess || pl.splits == 1) return e;
   FinalizeArgs f{};
@@ -245,14 +267,14 @@ int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_ro
     if (routing) {
       GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
                               s->n_experts, 0, T, partial, s);
-      if (run_dense(w.pr, A_BF16, false, a, st) != hipSuccess) return MOE_EHIP;
+      if (run_dense(w.pr, A_BF16, false, a, nullptr, st) != hipSuccess) return MOE_EHIP;
       if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) != hipSuccess)
         return MOE_EHIP;
     }
     if (z) {
       GemmArgs d = dense_args(w.pd, x, s->hidden, w_down, nullptr, s->latent, s->hidden, z,
                               s->latent, 0, T, partial, s);
-      if (run_dense(w.pd, A_BF16, false, d, st) != hipSuccess) return MOE_EHIP;
+      if (run_dense(w.pd, A_BF16, false, d, nullptr, st) != hipSuccess) return MOE_EHIP;
     }
     return MOE_OK;
   });
@@ -399,7 +421,7 @@ int moe_combine_norm_up(const moe_shape *s, int T, const float *Y, const int32_t
     GemmArgs a = dense_args(w.pu, yn, s->latent, w_up, nullptr, s->hidden, s->latent, out,
                             s->hidden, accumulate, T, reinterpret_cast<float *>(wsp(ws, w.partial)),
                             s);
-    if (run_dense(w.pu, afmt_of(s), false, a, st) != hipSuccess) return MOE_EHIP;
+    if (run_dense(w.pu, afmt_of(s), false, a, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
     return MOE_OK;
   });
 }
@@ -426,10 +448,10 @@ int shared_expert_ffn(const moe_shape *s, int T, const uint16_t *x, const uint16
     float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
     GemmArgs g = dense_args(w.pgu, x, s->hidden, w_gate, w_up, NS, s->hidden, hs, NS, 0, T, partial,
                             s);
-    if (run_dense(w.pgu, A_BF16, true, g, st) != hipSuccess) return MOE_EHIP;
+    if (run_dense(w.pgu, A_BF16, true, g, nullptr, st) != hipSuccess) return MOE_EHIP;
     GemmArgs d = dense_args(w.pdn, hs, NS, w_down, nullptr, s->hidden, NS, out, s->hidden,
                             accumulate, T, partial, s);
-    if (run_dense(w.pdn, afmt_of(s), false, d, st) != hipSuccess) return MOE_EHIP;
+    if (run_dense(w.pdn, afmt_of(s), false, d, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
     return MOE_OK;
   });
 }

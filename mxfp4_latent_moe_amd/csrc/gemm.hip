@@ -391,16 +391,19 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair) {
     while (items * splits < 2048 && ceil_div(ksteps, splits * 2) >= 2) splits *= 2;
     p.splits = splits;
     p.grid_logical = items * splits;
-  } else if (rows >= 1024 && (long long)rows * K * 4 < (1LL << 31)) {
-    // enough row chunks to fill the chip without splitting K
-    p.variant = 3;
-    p.nt = PREFILL_NT;
-    p.chunk_rows = 16 * PREFILL_NT;
-    p.mt = prefill_rows_per_wg(pair) / 64;
-    p.n_blocks = ceil_div(N, prefill_rows_per_wg(pair));
+  } else if (rows >= 1024 && (long long)rows * K * 2 < (1LL << 31) && (long long)N * K * 2 < (1LL << 31)) {
+    // 256 x 256 tiles; K is split while the tiles alone leave CUs idle
+    p.variant = 4;
+    p.nt = 16;
+    p.chunk_rows = dense_tile_rows();
+    p.mt = 0;
+    p.n_blocks = ceil_div(N, dense_tile_cols(pair));
     p.max_chunks = ceil_div(rows, p.chunk_rows);
-    p.splits = 1;
-    p.grid_logical = (long long)p.max_chunks * p.n_blocks;
+    const long long items = (long long)p.max_chunks * p.n_blocks;
+    int splits = 1;
+    while (items * splits < 256 && K % (128 * splits * 2) == 0 && splits < 8) splits *= 2;
+    p.splits = splits;
+    p.grid_logical = items * splits;
   } else {
     p.variant = 0;
     p.nt = 8;
@@ -464,6 +467,11 @@ hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const 
   const long long grid = (pl.grid_logical + 7) / 8 * 8;
   if (pl.variant == 2) return launch_grouped_stream(afmt, pair, a, st);
   if (pl.variant == 3) return launch_prefill_gemm(wfmt, afmt, pair, a, grid, st);
+  if (pl.variant == 4) {
+    // activations arrive as bf16 planes (the caller splits fp32 ones)
+    if (wfmt != W_BF16) return hipErrorInvalidValue;
+    return launch_dense_tile(afmt == A_F32_SPLIT ? 2 : 1, pair, a, st);
+  }
   if (pl.variant == 1) return launch_stream_gemm(wfmt, afmt, pair, a, grid, st);
   if (wfmt == W_MXFP4) return launch_af<W_MXFP4>(pl, afmt, pair, a, grid, st);
   return launch_af<W_BF16>(pl, afmt, pair, a, grid, st);

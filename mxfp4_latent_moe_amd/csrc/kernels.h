@@ -41,6 +41,10 @@ struct GemmArgs {
   // unused then
   const uint8_t *mxq, *mxs;
   long long mx_rows;
+  // dense tiled kernel: the lo plane of split activations (A holds the hi
+  // plane, both bf16 [rows][lda]) and the number of 256-row token tiles
+  const void *A2;
+  int dense_rows_tiles;
 };
 
 struct FinalizeArgs {
@@ -77,7 +81,8 @@ constexpr int PREFILL_MX_MT_SINGLE = 8;
 // kernel variant selection (host side)
 struct GemmPlan {
   int variant;   // 0: tiled (LDS-staged K steps), 1: streaming (<= 16-row chunks),
-                 // 2: persistent streaming over expert row chunks, 3: tiled prefill
+                 // 2: persistent streaming over expert row chunks, 3: tiled prefill,
+                 // 4: dense 256 x 256 tiles (bf16 activation planes)
   int nt;        // 16-token tiles per chunk (1 or 8)
   int mt;        // 16-row weight tiles per wave and matrix
   int chunk_rows;
@@ -104,6 +109,11 @@ hipError_t launch_mx_split(bool fp6, const float *A, long long lda, int rows, in
                            hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                               hipStream_t st);
+int dense_tile_cols(bool pair);
+int dense_tile_rows();
+hipError_t launch_dense_tile(int nplanes, bool pair, const GemmArgs &a, hipStream_t st);
+hipError_t launch_split_planes(const float *A, long long lda, int rows, int K, uint16_t *hi, uint16_t *lo,
+                               hipStream_t st);
 
 hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
                        hipStream_t st);
