@@ -13,11 +13,11 @@
 // consecutive lanes fetch one 128-byte line, so every L1 request is a whole
 // line.  A stage holds KS values of K for the 256 weight rows and for the 256
 // tokens of each activation plane (one plane of bf16 activations, or the hi
-// and lo planes of fp32 activations split beforehand).  Inside LDS, 16-byte
+// and lo planes of fp32 activations split beforehand), in a ring of three or
+// four stages, so the loads run two or three K steps ahead.  Inside LDS, 16-byte
 // chunk c of row r sits at line r / RPL, slot ((r % RPL) * CPR + c) ^ (line
 // % 8): the eight lanes an MFMA operand read serves at a time hit eight
-// different slots, so the reads are free of bank conflicts.  Two stages: the
-// next K step's loads are in flight while the current one computes.
+// different slots, so the reads are free of bank conflicts.
 #include "common.h"
 #include "kernels.h"
 
@@ -66,9 +66,14 @@ struct DLayout {
   static constexpr int RPL = 128 / (2 * KS);  // rows per 128-byte line
   static constexpr int ROW_BYTES = 2 * KS;
   static constexpr int REGION = DT * ROW_BYTES;  // bytes of 256 rows
+  // slot swizzle of a line: the 8 rows (4 lines) one 128-byte read pass
+  // serves and the 16 rows (8 lines) of a 256-byte pass both land on distinct
+  // 16-byte bank groups; it repeats every 4 lines within a 16-line period and
+  // is unchanged by a shift of 16 lines (32 rows, one MFMA tile)
+  static MOE_DEV int swz(int line) { return (line + (line >> 2)) & 3; }
   static MOE_DEV int slot_offset(int r, int c) {
     const int line = r / RPL;
-    return line * 128 + ((((r % RPL) * CPR) + c) ^ (line & 7)) * 16;
+    return line * 128 + ((((r % RPL) * CPR) + c) ^ swz(line)) * 16;
   }
 };
 
@@ -81,7 +86,7 @@ MOE_DEV uint32_t dense_voff(int ii, int lane, int n0, int t0, int N, int K, int 
   constexpr int REG = Lay::REGION;
   const int region = (ii * 1024) / REG;
   const int line = ((ii * 1024) % REG) / 128 + lane / 8;
-  const int u = (lane % 8) ^ (line & 7);
+  const int u = (lane % 8) ^ Lay::swz(line);
   const int r = line * Lay::RPL + u / Lay::CPR;
   const int c = u % Lay::CPR;
   if (region == 0) {
@@ -94,11 +99,13 @@ MOE_DEV uint32_t dense_voff(int ii, int lane, int n0, int t0, int N, int K, int 
 }
 
 // K per stage and LDS bytes of a stage for NPL activation planes
-constexpr int dense_ks(int npl) { return npl == 1 ? 64 : 32; }
+constexpr int dense_ks(int npl) { return 32; }  // two 64-byte rows per 128-byte line
 constexpr int dense_stage_bytes(int npl) { return (1 + npl) * DT * 2 * dense_ks(npl); }
+// stages in the LDS ring: loads run NST - 1 K steps ahead of the MFMAs
+constexpr int dense_stages(int npl) { return npl == 1 ? 4 : 3; }
 
 template <int NPL, bool PAIR>
-MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *st0, uint8_t *st1) {
+MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
   constexpr int KS = dense_ks(NPL);
   using Lay = DLayout<KS>;
   constexpr int REG = Lay::REGION;
@@ -108,6 +115,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *st0, uint8_t *st1) {
   constexpr int KL = NL / DNW;            // per wave
   constexpr int J = KS / 16;              // MFMA K steps per stage
   static_assert(NL % DNW == 0 && (REG / 1024) % (2 * DNW) == 0, "loads split evenly; regions and halves whole");
+  static_assert(Lay::RPL == 2, "the swizzle is laid out for two rows per line");
 
   const int n_tiles = g.n_blocks;
   const int t_tiles = g.dense_rows_tiles;
@@ -124,7 +132,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *st0, uint8_t *st1) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = g.N, K = g.K, rows = g.dense_rows;
-  const int ksplit = K / g.splits;           // a multiple of 2 * KS (host-checked)
+  const int ksplit = K / g.splits;           // a multiple of 128 (host-checked)
   const int nks = ksplit / KS;
   const int k0 = split * ksplit;
   const int ncols = PAIR ? DT / 2 : DT;      // output columns of a weight tile
@@ -173,7 +181,8 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *st0, uint8_t *st1) {
     if constexpr (PAIR) return (a < 2 ? 64 * wn + 32 * a : DT / 2 + 64 * wn + 32 * (a - 2));
     else return 128 * wn + 32 * a;
   };
-  const uint32_t wbase0 = dlds_addr(st0), wbase1 = dlds_addr(st1);
+  constexpr int NST = dense_stages(NPL);
+  const uint32_t ring_base = dlds_addr(ring);
   // weight rows and token rows of the wave as region offsets
   const int wrow0 = wrow_tile(0);
   const int tokrow0 = 128 * wm;
@@ -185,69 +194,88 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *st0, uint8_t *st1) {
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16_t{};
 
   constexpr int R = 4 + 4 * NPL;  // fragment reads per MFMA step
-  auto compute = [&](uint32_t base) {
-    u32x4_t fw[2][4], ft[2][NPL][4];
-    auto issue = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const uint32_t aw = base + roff[j] + (uint32_t)(wrow0 / 32) * TILE_OFF;
-      const uint32_t at = base + roff[j] + (uint32_t)(tokrow0 / 32) * TILE_OFF;
-      if constexpr (PAIR) {
-        dread<0>(aw, fw[j & 1][0]);
-        dread<TILE_OFF>(aw, fw[j & 1][1]);
-        dread<(DT / 2 / 32) * TILE_OFF>(aw, fw[j & 1][2]);
-        dread<(DT / 2 / 32 + 1) * TILE_OFF>(aw, fw[j & 1][3]);
-      } else {
-        dread<0>(aw, fw[j & 1][0]);
-        dread<TILE_OFF>(aw, fw[j & 1][1]);
-        dread<2 * TILE_OFF>(aw, fw[j & 1][2]);
-        dread<3 * TILE_OFF>(aw, fw[j & 1][3]);
-      }
-      static_for_d<NPL>([&](auto pc) {
-        constexpr int p = decltype(pc)::value;
-        dread<(1 + p) * REG>(at, ft[j & 1][p][0]);
-        dread<(1 + p) * REG + TILE_OFF>(at, ft[j & 1][p][1]);
-        dread<(1 + p) * REG + 2 * TILE_OFF>(at, ft[j & 1][p][2]);
-        dread<(1 + p) * REG + 3 * TILE_OFF>(at, ft[j & 1][p][3]);
-      });
-    };
-    issue(std::integral_constant<int, 0>{});
+  static_assert(J % 2 == 0, "fragment buffers alternate with the MFMA step");
+  u32x4_t fw[2][4], ft[2][NPL][4];
+  // reads of MFMA step j of the stage at `base` into fragment buffer j % 2
+  auto issue = [&](uint32_t base, auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const uint32_t aw = base + roff[j] + (uint32_t)(wrow0 / 32) * TILE_OFF;
+    const uint32_t at = base + roff[j] + (uint32_t)(tokrow0 / 32) * TILE_OFF;
+    if constexpr (PAIR) {
+      dread<0>(aw, fw[j & 1][0]);
+      dread<TILE_OFF>(aw, fw[j & 1][1]);
+      dread<(DT / 2 / 32) * TILE_OFF>(aw, fw[j & 1][2]);
+      dread<(DT / 2 / 32 + 1) * TILE_OFF>(aw, fw[j & 1][3]);
+    } else {
+      dread<0>(aw, fw[j & 1][0]);
+      dread<TILE_OFF>(aw, fw[j & 1][1]);
+      dread<2 * TILE_OFF>(aw, fw[j & 1][2]);
+      dread<3 * TILE_OFF>(aw, fw[j & 1][3]);
+    }
+    static_for_d<NPL>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      dread<(1 + p) * REG>(at, ft[j & 1][p][0]);
+      dread<(1 + p) * REG + TILE_OFF>(at, ft[j & 1][p][1]);
+      dread<(1 + p) * REG + 2 * TILE_OFF>(at, ft[j & 1][p][2]);
+      dread<(1 + p) * REG + 3 * TILE_OFF>(at, ft[j & 1][p][3]);
+    });
+  };
+  auto tie = [&](int q) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) dtie(fw[q][a]);
+#pragma unroll
+    for (int p = 0; p < NPL; ++p)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dtie(ft[q][p][b]);
+  };
+  auto mfmas = [&](int q) {
+#pragma unroll
+    for (int p = 0; p < NPL; ++p)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fw[q][a], ft[q][p][b], acc[a][b]);
+  };
+  auto slot_base = [&](int s) { return ring_base + (uint32_t)((s % NST) * STAGE); };
+
+  // ring of NST stages, K step s in slot s % NST.  Step s first refills the
+  // slot step s - 1 used (every wave has passed the barrier after it) with
+  // step s + NST - 1, then computes; at its end step s + 1 must have landed,
+  // so NST - 2 stages of loads may stay in flight.  Loads past the last step
+  // re-read it into slots that are not read again.  The products of a step's
+  // last MFMA step run after the barrier, behind the next step's first reads,
+  // so no step starts on an exposed LDS latency.
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) load_stage(ring + s * STAGE, min(s, nks - 1));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(KL * (NST - 2)));
+  __builtin_amdgcn_s_barrier();
+  issue(slot_base(0), std::integral_constant<int, 0>{});
+  for (int s = 0; s < nks; ++s) {
+    const int fill = (s + NST - 1) % NST;
+    load_stage(ring + fill * STAGE, min(s + NST - 1, nks - 1));
+    const uint32_t base = slot_base(s);
     static_for_d<J>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       if constexpr (j + 1 < J) {
-        issue(std::integral_constant<int, j + 1>{});
+        issue(base, std::integral_constant<int, j + 1>{});
         dwait<R>();
+        tie(j & 1);
+        mfmas(j & 1);
       } else {
-        dwait<0>();
+        dwait<0>();  // this stage's reads are done before the barrier
+        tie(j & 1);
       }
-#pragma unroll
-      for (int a = 0; a < 4; ++a) dtie(fw[j & 1][a]);
-#pragma unroll
-      for (int p = 0; p < NPL; ++p)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) dtie(ft[j & 1][p][b]);
-#pragma unroll
-      for (int p = 0; p < NPL; ++p)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fw[j & 1][a], ft[j & 1][p][b], acc[a][b]);
     });
-  };
-
-  // two stages; K steps come in pairs (host-checked), so stage s % 2 is static
-  load_stage(st0, 0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(0));
-  __builtin_amdgcn_s_barrier();
-  for (int s = 0; s < nks; s += 2) {
-    load_stage(st1, s + 1);
-    compute(wbase0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(0));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(KL * (NST - 2)));
     __builtin_amdgcn_s_barrier();
-    load_stage(st0, min(s + 2, nks - 1));  // past the last step: a harmless reload
-    compute(wbase1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(0));
-    __builtin_amdgcn_s_barrier();
+    // the next step's first fragments (past the last step: a read of a slot
+    // that holds valid data, drained below), then the deferred products
+    issue(slot_base(min(s + 1, nks - 1)), std::integral_constant<int, 0>{});
+    mfmas((J - 1) & 1);
   }
+  dwait<0>();
+  tie(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(0));
 
   // ---- epilogue: acc[a][b] register i of lane l is weight row 32 a + (i % 4)
   // + 8 (i / 4) + 4 (l / 32) and token 32 b + l % 32 of the wave's tiles
@@ -302,9 +330,8 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *st0, uint8_t *st1) {
 
 template <int NPL, bool PAIR>
 __global__ __launch_bounds__(64 * DNW, 1) void dense_tile_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[dense_stage_bytes(NPL)];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[dense_stage_bytes(NPL)];
-  dense_tile_body<NPL, PAIR>(g, st0, st1);
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[dense_stages(NPL) * dense_stage_bytes(NPL)];
+  dense_tile_body<NPL, PAIR>(g, ring);
 }
 
 // fp32 activations -> bf16 planes: hi = bf16(a) and lo = bf16(a - hi), or
