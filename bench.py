@@ -220,7 +220,7 @@ def summarize_pmc(fetch_dir, write_dir):
         if not ks:
             sys.exit(f"no dispatch of {key!r}")
         v = [x for k in ks for x in acc[k]]
-        return sum(v) / len(v), len(v)
+        return sum(v) / len(v), len(v), _short(ks[0])
 
     copy_key = "elementwise"  # torch's mul kernel (the calibration copy)
     cf = [v for k in fetch if copy_key in k for v in fetch[k] if v * 1024 > COPY_BYTES / 4]
@@ -229,8 +229,8 @@ def summarize_pmc(fetch_dir, write_dir):
         sys.exit("calibration copy not found (run bench.py with --calibrate-copy)")
     f_scale = COPY_BYTES / (1024.0 * sum(cf) / len(cf))
     w_scale = COPY_BYTES / (1024.0 * sum(cw) / len(cw))
-    kf, nf = pick(fetch, DECODE_GATEUP_KERNEL)
-    kw, nw = pick(write, DECODE_GATEUP_KERNEL)
+    kf, nf, kname = pick(fetch, DECODE_GATEUP_KERNEL)
+    kw, nw, _ = pick(write, DECODE_GATEUP_KERNEL)
     traffic = kf * 1024 * f_scale + kw * 1024 * w_scale
     print("# HBM traffic of the decode gate/up grouped GEMM kernel (T=16, full K3 shapes)")
     print("# made by:")
@@ -239,7 +239,7 @@ def summarize_pmc(fetch_dir, write_dir):
     print("#   cd /tmp && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -o run -- "
           "python3 <repo>/bench.py --steps 3 --warmup 1 --no-secondary --no-cpu-baseline --calibrate-copy")
     print("#   python3 bench.py --summarize-pmc <F> <W>")
-    print(f"kernel: {DECODE_GATEUP_KERNEL}, 1, 2, 4>")
+    print(f"kernel: {kname}")
     print(f"source_sha256: {sources_sha256(DECODE_GATEUP_SOURCES)}")
     print(f"copy_bytes: {COPY_BYTES}")
     print(f"copy_fetch_kib_per_dispatch: {sum(cf) / len(cf):.1f}")
