@@ -279,6 +279,47 @@ def cpu_baseline(synth, wl, n_tokens):
                       f"oracle (expert dequantisation included), {dt:.1f} s"}
 
 
+def run_dense_ffn(mx, torch, synth):
+    """The first layer's dense FFN (H = 7168, intermediate 33792, bf16) through shared_expert_ffn:
+    decode T = 16 against HBM (its 1.45 GB of weights stream once per call, far more than the
+    last-level cache holds) and prefill T = 4096 against bf16 MFMA."""
+    from synth.device import to_dev_bf16
+    from mxfp4_latent_moe_amd import _lib, ops
+    dev = torch.device("cuda:0")
+    wl = synth.workload("dense_ffn")
+    sh = wl.shape
+    d = synth.gen_dense(wl)
+    w = {k: to_dev_bf16(d[k], dev) for k in ("sh_gate", "sh_up", "sh_down")}
+    del d
+    s = mx.shape_of(sh)
+    wbytes = 3 * sh.shared_inter * sh.hidden * 2
+    res = {"workload": "layer-0 dense FFN, H=7168, intermediate 33792, bf16 weights, SiTU-GLU"}
+    for T, steps in ((16, 20), (4096, 5)):
+        x = to_dev_bf16(synth.gen_tokens(wl, T), dev)
+        ws = torch.empty(ops.workspace_bytes(s, _lib.MOE_FN_SHARED_FFN, T), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ops.shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], out, 0, ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            ops.shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], out, 0, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        if T == 16:
+            gbs = wbytes / (ms * 1e-3) / 1e9
+            res["decode_T16"] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                                 "weight_bytes": wbytes, "gb_per_s": round(gbs, 1),
+                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            tf = 2.0 * T * sh.hidden * sh.shared_inter * 3 / (ms * 1e-3) / 1e12
+            res["prefill_T4096"] = {"ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                                    "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        del x, ws, out
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -430,6 +471,9 @@ def main():
             "gateup_tflops": round(gu_flops / (r6["dominant_ms"] * 1e-3) / 1e12, 1),
             "per_call_ms": {k: round(v, 4) for k, v in r6["per_call_ms"].items()},
         }
+
+        print("bench: timing the layer-0 dense FFN", file=sys.stderr, flush=True)
+        line["secondary_dense_ffn"] = run_dense_ffn(mx, torch, synth)
 
     if args.calibrate_copy:
         calibration_copy(torch)

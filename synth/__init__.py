@@ -11,6 +11,7 @@ from .inputs import (  # noqa: F401
     WORKLOADS,
     K3_SHAPE,
     TINY_SHAPE,
+    LAYER0_FFN_SHAPE,
     workload,
     f32_to_bf16_bits,
     bf16_bits_to_f32,

@@ -52,6 +52,10 @@ class LayerShape:
 # LatentMoE rows); K3 open-artifact audit section 4.3 (expert tensor shapes).
 K3_SHAPE = LayerShape(7168, 3584, 896, 16, 3072, 2, 3072)
 TINY_SHAPE = LayerShape(256, 128, 32, 4, 128, 1, 128)
+# The first layer is dense with a bf16 FFN of intermediate 33792 (K3 open-artifact audit section
+# 4.1 tensor table: gate/up 33792 x 7168, down 7168 x 33792; findrepo.work summary, architecture
+# table, Dense layer row); it runs through the shared-expert call as one expert of that width.
+LAYER0_FFN_SHAPE = LayerShape(7168, 3584, 896, 16, 3072, 1, 33792)
 
 
 @dataclass(frozen=True)
@@ -83,6 +87,9 @@ WORKLOADS = {
     "microbench": Workload("microbench", 5, K3_SHAPE, 4096, 2, 0.01, 0.05, "normal", 118, 120,
                            grouped_only=True,
                            notes="isolated grouped GEMM, Multinomial(65536, Zipf(1.1)) segments"),
+    # the dense first layer's FFN (intermediate 33792, bf16) as one "shared expert" of width 33792
+    "dense_ffn": Workload("dense_ffn", 6, LAYER0_FFN_SHAPE, 4096, 3, 0.01, 0.05, "normal", 118, 120,
+                          notes="layer-0 dense FFN, H=7168, intermediate 33792, bf16, T=16 and T=4096"),
 }
 
 

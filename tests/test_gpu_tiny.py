@@ -248,3 +248,60 @@ def test_tiny_mx6x3_operand_mode(mx):
     assert err <= TOL
     # three e2m3 terms leave about 2^-12 of each 32-block's maximum, as three e4m3 terms do
     assert err < 2e-3 and errH < 2e-3
+
+
+def _exact_mx_rows(rng, rows, K):
+    """Rows whose every 32-block is 2^e times e2m3 grid values (|q| <= 7.5, one |q| >= 4 per block):
+    exact in one e2m3 or e4m3 term and in bf16, so every operand mode sees the same values."""
+    grid = np.array([m / 8 for m in range(8)] + [(1 + m / 8) * 2.0 ** (e - 1) for e in (1, 2, 3) for m in range(8)])
+    q = rng.choice(grid, size=(rows, K)) * rng.choice([-1.0, 1.0], size=(rows, K))
+    q[:, ::32] = rng.choice([4.0, 5.0, 6.0, 7.5], size=(rows, K // 32)) * rng.choice([-1.0, 1.0], size=(rows, K // 32))
+    e = rng.integers(-4, 3, size=(rows, K // 32)).astype(np.float64)
+    return (q * np.repeat(2.0 ** e, 32, axis=1)).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3])
+def test_grouped_gemm_exact_activations_all_modes(mx, mode):
+    """Activations exact in every operand mode: the bf16 hi+lo path and the MX-scaled fp8 and fp6
+    paths must all reproduce the float64 oracle up to fp32 accumulation (1e-5), for gate/up +
+    SiTU-GLU and for down, on prefill-sized segments (0 to 130 rows: empty experts, two chunks)."""
+    from mxfp4_latent_moe_amd import _lib, ops
+    wl = synth.workload("tiny")
+    sh = wl.shape
+    E, L, I = sh.n_experts, sh.latent, sh.inter
+    rng = np.random.default_rng(77)
+    counts = rng.integers(0, 131, size=E)
+    counts[3] = 0
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = int(offsets[-1])
+    say(f"case: exact-activation grouped GEMM, tiny dims, P={P}, operand mode {mode}")
+    st = synth.gen_expert_stack(wl)
+    s = mx.shape_of(sh, mode)
+    ws = torch.empty(ops.workspace_bytes(s, _lib.MOE_FN_GROUPED_GEMM, P), dtype=torch.uint8, device=DEV)
+    dev_w = {k: to_dev(v, DEV) for k, v in st.items()}
+    off_d = to_dev(offsets, DEV)
+    for op, K, N in ((ops.MOE_OP_GATEUP_SITU, L, I), (ops.MOE_OP_DOWN, I, L)):
+        A = _exact_mx_rows(rng, P, K)
+        C = torch.empty((P, N), dtype=torch.float32, device=DEV)
+        if op == ops.MOE_OP_GATEUP_SITU:
+            ops.grouped_gemm(s, op, P, off_d, None, to_dev(A, DEV), dev_w["w1_packed"], dev_w["w1_scale"],
+                             dev_w["w3_packed"], dev_w["w3_scale"], None, C, ws)
+        else:
+            ops.grouped_gemm(s, op, P, off_d, None, to_dev(A, DEV), dev_w["w2_packed"], dev_w["w2_scale"],
+                             None, None, None, C, ws)
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        ref = np.zeros((P, N))
+        for e in range(E):
+            r0, r1 = offsets[e], offsets[e + 1]
+            if r1 == r0:
+                continue
+            deq = layer.dequant_expert({k: v[e] for k, v in st.items()})
+            a = A[r0:r1].astype(np.float64)
+            if op == ops.MOE_OP_GATEUP_SITU:
+                ref[r0:r1] = layer.situ_glu(a @ deq["w1"].T, a @ deq["w3"].T)
+            else:
+                ref[r0:r1] = a @ deq["w2"].T
+        err = rel_max_err(got, ref)
+        say(f"op {op} mode {mode}: max|gpu-oracle|/rms = {err:.3e}")
+        assert err <= 1e-5
