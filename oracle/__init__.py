@@ -27,6 +27,8 @@ Modules:
              shared experts, the layer forward, the grouped-GEMM microbench
   scalar  -- a second, structurally different tiny-shape oracle (per-token,
              per-pair Python loops, its own bit-level e2m1 decoding)
+  reap    -- REAP expert saliency over a calibration batch (README, REAP
+             section)
 
 Parity status: the whole-layer result has no worked input/output example on
 the pages; it is pinned by the independent scalar oracle, by closed forms and
@@ -34,4 +36,4 @@ limits (SiTU-GLU), brute force (e2m1 bytes, top-k subsets), invariants
 (RMSNorm scale invariance, pruning equivalence, zero codes) and the pages'
 printed shape and parameter counts.
 """
-from . import mxfp4, layer, scalar  # noqa: F401
+from . import mxfp4, layer, scalar, reap  # noqa: F401
