@@ -320,6 +320,42 @@ def run_dense_ffn(mx, torch, synth):
     return res
 
 
+def run_reap(mx, torch, synth):
+    """REAP saliency over one prefill batch (4096 tokens x top-16, L = 3584): the pass reads every
+    expert-output row once (940 MB), so it is timed against HBM."""
+    from mxfp4_latent_moe_amd import _lib, ops
+    dev = torch.device("cuda:0")
+    sh = synth.K3_SHAPE
+    T, k, E, L = 4096, sh.top_k, sh.n_experts, sh.latent
+    P = T * k
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    ids = torch.randint(0, E, (P,), device=dev, generator=g, dtype=torch.int32)
+    sorted_pair = torch.sort(ids, stable=True).indices.to(torch.int32)
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    offsets[1:] = torch.cumsum(torch.bincount(ids, minlength=E), 0).to(torch.int32)
+    Y = torch.randn((P, L), device=dev, generator=g, dtype=torch.float32)
+    w = torch.rand((P,), device=dev, generator=g, dtype=torch.float32)
+    s = mx.shape_of(sh)
+    ws = torch.empty(ops.workspace_bytes(s, _lib.MOE_FN_REAP_SALIENCY, P), dtype=torch.uint8, device=dev)
+    sal = torch.zeros(E, dtype=torch.float64, device=dev)
+    cnt = torch.zeros(E, dtype=torch.int64, device=dev)
+    for _ in range(3):
+        ops.reap_saliency(s, P, offsets, Y, w, sorted_pair, sal, cnt, 1, ws)
+    steps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ops.reap_saliency(s, P, offsets, Y, w, sorted_pair, sal, cnt, 1, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = P * L * 4 + P * 16 + E * 20
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "REAP saliency, 4096 tokens x top-16 over 896 experts, L=3584, synthetic rows",
+            "ms": round(ms, 4), "bytes": nbytes, "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,6 +510,8 @@ def main():
 
         print("bench: timing the layer-0 dense FFN", file=sys.stderr, flush=True)
         line["secondary_dense_ffn"] = run_dense_ffn(mx, torch, synth)
+        print("bench: timing the REAP saliency pass", file=sys.stderr, flush=True)
+        line["secondary_reap"] = run_reap(mx, torch, synth)
 
     if args.calibrate_copy:
         calibration_copy(torch)

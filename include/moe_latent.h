@@ -78,6 +78,7 @@ extern "C" {
 #define MOE_FN_GROUPED_GEMM 2
 #define MOE_FN_COMBINE_NORM_UP 3
 #define MOE_FN_SHARED_FFN 4
+#define MOE_FN_REAP_SALIENCY 5
 
 typedef struct {
   int32_t hidden;       /* H: residual width (7168 for K3) */
@@ -204,6 +205,34 @@ int moe_combine_norm_up(const moe_shape *shape, int T, const float *Y, const int
 int shared_expert_ffn(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *w_gate,
                       const uint16_t *w_up, const uint16_t *w_down, float *out, int accumulate,
                       void *ws, size_t ws_bytes, void *stream);
+
+/* REAP expert saliency over a calibration batch.
+ * Follows: kimi-k3-mlx README, REAP section (each expert scored on a
+ * calibration set by S_j = (1/|C|) * sum over tokens of g_j(x) * ||e_j(x)||_2,
+ * computed one layer at a time from the layer's router gates and expert
+ * outputs).  This call accumulates the numerator and the per-expert token
+ * counts; the caller divides by |C| (or by the counts).
+ *   P             rows of Y (T * top_k pairs), >= 0
+ *   expert_offsets [E+1] int32, expert j owns sorted rows offsets[j] .. offsets[j+1]
+ *                 (moe_permute's output)
+ *   Y             [P, L] fp32, the expert outputs e_j(x) in expert-sorted order,
+ *                 un-weighted (mxfp4_grouped_gemm(MOE_OP_DOWN) without pair weights);
+ *                 may be NULL when P == 0
+ *   pair_weight   [T*k] fp32 routing weights g in pair order (moe_route's topk_w)
+ *   sorted_pair   [P] int32, pair index of each sorted row (moe_permute's output);
+ *                 pair_weight and sorted_pair are both given, or both NULL when the
+ *                 rows of Y already carry their weight (g >= 0, so ||g e|| = g ||e||)
+ *   sal_sum       [E] float64: sum of g * ||e|| over the batch's rows of each expert
+ *   counts        [E] int64: the number of those rows
+ *   accumulate    0: overwrite sal_sum and counts; 1: add to them (a calibration
+ *                 pass calls this once per batch)
+ * Deterministic: fixed-order reductions, no atomics.  Workspace:
+ * moe_workspace_bytes(shape, MOE_FN_REAP_SALIENCY, P) bytes (one fp32 per row).
+ * Errors: MOE_EINVAL (null required pointer, P < 0, accumulate not 0/1, only
+ * one of pair_weight / sorted_pair, misaligned Y or ws), MOE_EWORKSPACE. */
+int moe_reap_saliency(const moe_shape *shape, int P, const int32_t *expert_offsets, const float *Y,
+                      const float *pair_weight, const int32_t *sorted_pair, double *sal_sum,
+                      int64_t *counts, int accumulate, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -239,6 +239,7 @@ size_t moe_workspace_bytes(const moe_shape *s, int fn, int n) {
     case MOE_FN_SHARED_FFN:
       if (s->n_shared * s->shared_inter == 0) return ALIGN;
       return shared_ws(s, n).total;
+    case MOE_FN_REAP_SALIENCY: return align_up((size_t)n * sizeof(float));
     default: return 0;
   }
 }
@@ -452,6 +453,26 @@ int shared_expert_ffn(const moe_shape *s, int T, const uint16_t *x, const uint16
     GemmArgs d = dense_args(w.pdn, hs, NS, w_down, nullptr, s->hidden, NS, out, s->hidden,
                             accumulate, T, partial, s);
     if (run_dense(w.pdn, afmt_of(s), false, d, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  });
+}
+
+int moe_reap_saliency(const moe_shape *s, int P, const int32_t *expert_offsets, const float *Y,
+                      const float *pair_weight, const int32_t *sorted_pair, double *sal_sum, int64_t *counts,
+                      int accumulate, void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (P < 0 || !expert_offsets || !sal_sum || !counts || (P > 0 && (!Y || !ws))) return MOE_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
+    if ((pair_weight == nullptr) != (sorted_pair == nullptr)) return MOE_EINVAL;
+    if ((Y && !aligned16(Y)) || (ws && !aligned16(ws))) return MOE_EINVAL;
+    if (ws_bytes < (size_t)P * sizeof(float)) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    if (launch_reap(Y, P, s->latent, pair_weight, sorted_pair, expert_offsets, s->n_experts, sal_sum,
+                    reinterpret_cast<long long *>(counts), accumulate, static_cast<float *>(ws),
+                    static_cast<hipStream_t>(stream)) != hipSuccess)
+      return MOE_EHIP;
     return MOE_OK;
   });
 }

@@ -130,6 +130,10 @@ hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *blk,
                           int32_t *sorted_pair, int32_t *pair_pos, int32_t *active,
                           hipStream_t st);
 
+hipError_t launch_reap(const float *Y, int P, int L, const float *pair_weight, const int32_t *sorted_pair,
+                       const int32_t *offsets, int E, double *sal_sum, long long *counts, int accumulate,
+                       float *contrib, hipStream_t st);
+
 hipError_t launch_combine_norm(const float *Y, const int32_t *pair_pos, const float *w,
                                const uint16_t *gamma, int T, int k, int L, float eps, float *yn,
                                hipStream_t st);

@@ -1,5 +1,5 @@
-"""Torch-facing wrappers of the five C-ABI calls, and a layer object that
-chains them on one stream.  Argument marshalling only: tensors are passed as
+"""Torch-facing wrappers of the C-ABI calls (the five of the layer and the REAP
+saliency), and a layer object that chains the layer's calls on one stream.  Argument marshalling only: tensors are passed as
 device pointers, the stream as its HIP handle; all compute runs in the HIP
 library."""
 from __future__ import annotations
@@ -62,6 +62,14 @@ def shared_ffn(shape, x, w_gate, w_up, w_down, out, accumulate, ws, stream=None)
     check("shared_expert_ffn",
           load().shared_expert_ffn(shape, x.shape[0], _p(x), _p(w_gate), _p(w_up), _p(w_down), _p(out),
                                    int(accumulate), _p(ws), ws.numel(), _s(stream)))
+
+
+def reap_saliency(shape, P, offsets, Y, pair_weight, sorted_pair, sal_sum, counts, accumulate, ws, stream=None):
+    """REAP saliency numerator (float64 [E]) and token counts (int64 [E]), see moe_reap_saliency."""
+    check("moe_reap_saliency",
+          load().moe_reap_saliency(shape, int(P), _p(offsets), _p(Y), _p(pair_weight), _p(sorted_pair),
+                                   _p(sal_sum), _p(counts), int(accumulate), _p(ws),
+                                   0 if ws is None else ws.numel(), _s(stream)))
 
 
 WEIGHT_KEYS = ("w_router", "bias", "w_down", "w_up", "gamma", "sh_gate", "sh_up", "sh_down",

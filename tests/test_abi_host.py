@@ -60,7 +60,7 @@ def _shape(**kw):
 
 def test_workspace_bytes(lib):
     s = _shape()
-    for fn in range(5):
+    for fn in range(6):
         assert lib.moe_workspace_bytes(s, fn, 16) > 0
     assert lib.moe_workspace_bytes(s, 7, 16) == 0
     assert lib.moe_workspace_bytes(s, 0, 0) == 0
@@ -155,3 +155,29 @@ def test_combine_and_shared_validation(lib):
 def test_no_cpu_fallback_when_library_missing(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_reap_saliency_validation(lib):
+    s = _shape()
+    P = 256
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_REAP_SALIENCY, P)
+    assert ws >= P * 4
+    args = [P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws, None]
+    assert lib.moe_reap_saliency(s, -1, *args[1:]) == _lib.MOE_EINVAL
+    for i in (1, 2, 5, 6):  # offsets, Y, sal_sum, counts
+        a = list(args)
+        a[i] = None
+        assert lib.moe_reap_saliency(s, *a) == _lib.MOE_EINVAL, i
+    for i in (3, 4):  # only one of pair_weight / sorted_pair
+        a = list(args)
+        a[i] = None
+        assert lib.moe_reap_saliency(s, *a) == _lib.MOE_EINVAL, i
+    a = list(args)
+    a[7] = 2
+    assert lib.moe_reap_saliency(s, *a) == _lib.MOE_EINVAL
+    a = list(args)
+    a[2] = FAKE + 4
+    assert lib.moe_reap_saliency(s, *a) == _lib.MOE_EINVAL
+    a = list(args)
+    a[9] = ws - 1
+    assert lib.moe_reap_saliency(s, *a) == _lib.MOE_EWORKSPACE
