@@ -388,7 +388,11 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair) {
     p.max_chunks = ceil_div(rows, 16);
     const long long items = (long long)p.max_chunks * p.n_blocks;
     int splits = ceil_div(ksteps, STREAM_KSMAX);
-    while (items * splits < 2048 && ceil_div(ksteps, splits * 2) >= 2) splits *= 2;
+    // a split below 8 K steps only pays while the grid would not cover the
+    // CUs: each work-group stages its token slice before streaming, and short
+    // streams spend more of their time in that ramp (measured on the shared
+    // experts at T = 16: 124 us with 2048 items, 86 us with 256)
+    while (items * splits < 256 && ceil_div(ksteps, splits * 2) >= 2) splits *= 2;
     p.splits = splits;
     p.grid_logical = items * splits;
   } else if (rows >= 1024 && (long long)rows * K * 2 < (1LL << 31) && (long long)N * K * 2 < (1LL << 31)) {

@@ -79,17 +79,20 @@ WEIGHT_KEYS = ("w_router", "bias", "w_down", "w_up", "gamma", "sh_gate", "sh_up"
 class LatentMoE:
     """One Stable LatentMoE layer on the GPU: weights resident, buffers per token count.
 
-    forward(x) enqueues the shared experts (shared_expert_ffn, writes out) on a
-    side stream, and on the caller's stream: moe_route, moe_permute, then,
-    after the side stream, mxfp4_grouped_gemm (gate/up + SiTU-GLU),
-    mxfp4_grouped_gemm (down) and moe_combine_norm_up (adds the routed part to
-    out).  The shared experts depend only on x, so they overlap the
-    latency-bound routing steps, and the expert GEMMs then stream alone; the
-    two output parts are added once, so the result is the same as running the
-    calls in sequence.
+    forward(x) enqueues the shared experts (shared_expert_ffn, writes out) and
+    the latent projection (moe_route without a router, writes z) on a side
+    stream, and on the caller's stream: moe_route (router and top-k),
+    moe_permute, then, after the side stream, mxfp4_grouped_gemm (gate/up +
+    SiTU-GLU), mxfp4_grouped_gemm (down) and moe_combine_norm_up (adds the
+    routed part to out).  The side stream's work depends only on x, so it
+    overlaps the latency-bound routing steps, and the expert GEMMs then stream
+    alone; the two output parts are added once, so the result is the same as
+    running the calls in sequence.  latent_on_side=False keeps z on the
+    caller's stream.
     """
 
-    def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True):
+    def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True,
+                 latent_on_side: bool = True):
         missing = [k for k in WEIGHT_KEYS if k not in weights]
         if missing:
             raise ValueError(f"missing weights: {missing}")
@@ -98,6 +101,9 @@ class LatentMoE:
         self.device = torch.device(device)
         self._bufs: dict = {}
         self.overlap_shared = overlap_shared
+        # the latent projection z joins the shared experts on the side stream,
+        # so the main stream's routing is only the router and the top-k
+        self.latent_on_side = latent_on_side and overlap_shared
         # default-priority side stream for the shared experts
         self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None
 
@@ -108,7 +114,7 @@ class LatentMoE:
         P = T * s.top_k
         ws = max(workspace_bytes(s, fn, P if fn == MOE_FN_GROUPED_GEMM else T)
                  for fn in (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP))
-        ws_sh = max(16, workspace_bytes(s, MOE_FN_SHARED_FFN, T))
+        ws_sh = max(16, workspace_bytes(s, MOE_FN_SHARED_FFN, T), workspace_bytes(s, MOE_FN_ROUTE, T))
         i32, f32 = torch.int32, torch.float32
         b = {
             "topk_ids": torch.empty((T, s.top_k), dtype=i32, device=dev),
@@ -159,13 +165,18 @@ class LatentMoE:
             call("shared_expert_ffn", side,
                  lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, b["ws_shared"],
                                     side))
+            if self.latent_on_side:
+                call("moe_route_latent", side,
+                     lambda: route(s, x, None, None, w["w_down"], None, None, b["z"], None, b["ws_shared"], side))
             side_done = torch.cuda.Event()
             side_done.record(side)
         elif shared:
             call("shared_expert_ffn", st,
                  lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, ws, st))
-        call("moe_route", st, lambda: route(s, x, w["w_router"], w["bias"], w["w_down"], b["topk_ids"],
-                                            b["topk_w"], b["z"], b["gap"], ws, st))
+        z_main = not (shared and side is not st and self.latent_on_side)
+        call("moe_route", st, lambda: route(s, x, w["w_router"], w["bias"], w["w_down"] if z_main else None,
+                                            b["topk_ids"], b["topk_w"], b["z"] if z_main else None, b["gap"],
+                                            ws, st))
         call("moe_permute", st, lambda: permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"],
                                                 b["active"], ws, st))
         if shared and side is not st:
