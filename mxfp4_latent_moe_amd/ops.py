@@ -76,19 +76,26 @@ WEIGHT_KEYS = ("w_router", "bias", "w_down", "w_up", "gamma", "sh_gate", "sh_up"
                "w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "w2_scale")
 
 
+# token counts up to which the dense products stream their weights (the
+# decode-sized path); the latent projection then runs on the side stream
+LATENT_SIDE_MAX_T = 64
+
+
 class LatentMoE:
     """One Stable LatentMoE layer on the GPU: weights resident, buffers per token count.
 
-    forward(x) enqueues the shared experts (shared_expert_ffn, writes out) and
-    the latent projection (moe_route without a router, writes z) on a side
-    stream, and on the caller's stream: moe_route (router and top-k),
+    forward(x) enqueues the shared experts (shared_expert_ffn, writes out) and,
+    at decode sizes, the latent projection (moe_route without a router,
+    writes z) on a side stream, and on the caller's stream: moe_route (router
+    and top-k, plus z at prefill sizes),
     moe_permute, then, after the side stream, mxfp4_grouped_gemm (gate/up +
     SiTU-GLU), mxfp4_grouped_gemm (down) and moe_combine_norm_up (adds the
     routed part to out).  The side stream's work depends only on x, so it
     overlaps the latency-bound routing steps, and the expert GEMMs then stream
     alone; the two output parts are added once, so the result is the same as
-    running the calls in sequence.  latent_on_side=False keeps z on the
-    caller's stream.
+    running the calls in sequence.  z runs on the side stream only at
+    decode-sized token counts (T <= 64); latent_on_side=False keeps it on the
+    caller's stream always.
     """
 
     def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True,
@@ -101,8 +108,10 @@ class LatentMoE:
         self.device = torch.device(device)
         self._bufs: dict = {}
         self.overlap_shared = overlap_shared
-        # the latent projection z joins the shared experts on the side stream,
-        # so the main stream's routing is only the router and the top-k
+        # at decode sizes the latent projection z joins the shared experts on
+        # the side stream, so the main stream's routing is only the router and
+        # the top-k; at prefill sizes z stays on the main stream, where it runs
+        # beside the shared experts instead of after them
         self.latent_on_side = latent_on_side and overlap_shared
         # default-priority side stream for the shared experts
         self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None
@@ -158,6 +167,7 @@ class LatentMoE:
             marks.append((name, e0, e1))
 
         shared = s.n_shared * s.shared_inter > 0
+        lat_side = self.latent_on_side and T <= LATENT_SIDE_MAX_T
         if shared and side is not st:
             # side stream: the shared experts, during the latency-bound routing steps
             side.wait_stream(st)
@@ -165,7 +175,7 @@ class LatentMoE:
             call("shared_expert_ffn", side,
                  lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, b["ws_shared"],
                                     side))
-            if self.latent_on_side:
+            if lat_side:
                 call("moe_route_latent", side,
                      lambda: route(s, x, None, None, w["w_down"], None, None, b["z"], None, b["ws_shared"], side))
             side_done = torch.cuda.Event()
@@ -173,7 +183,7 @@ class LatentMoE:
         elif shared:
             call("shared_expert_ffn", st,
                  lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, ws, st))
-        z_main = not (shared and side is not st and self.latent_on_side)
+        z_main = not (shared and side is not st and lat_side)
         call("moe_route", st, lambda: route(s, x, w["w_router"], w["bias"], w["w_down"] if z_main else None,
                                             b["topk_ids"], b["topk_w"], b["z"] if z_main else None, b["gap"],
                                             ws, st))
