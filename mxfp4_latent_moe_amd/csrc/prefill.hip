@@ -1,5 +1,5 @@
-// Tiled GEMM for prefill-sized work: MXFP4 expert segments (grouped) and the
-// bf16 dense products of the layer.
+// Tiled GEMM for prefill-sized work: MXFP4 expert segments (grouped).  The
+// dense bf16 products of the layer at prefill sizes run on dense.hip's tiles.
 //
 // Work item = (chunk of <= 16*NT expert-sorted token rows of one expert,
 // block of 64*MT weight rows).  Weight rows are the MFMA's M side, tokens its
@@ -54,6 +54,7 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   // MXFP4: lane group kg's 16 bytes of a 128-wide K step are its 32 codes (one
   // scale group); bf16: its 64 bytes (32 values), one 16-byte load per sub-step.
   constexpr bool FP4 = WF == W_MXFP4;
+  static_assert(FP4, "MXFP4 weights only");
   const uint32_t row_bytes = FP4 ? K / 2 : K * 2, srow_bytes = FP4 ? K / 32 : 0;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
@@ -86,27 +87,18 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     aoff[i] = (uint32_t)((arow * g.lda + a_oct * 8) * esz);
   }
 
-  u32x4_t wq[2][NTILE];    // MXFP4: codes of one K step per stage
+  u32x4_t wq[2][NTILE];    // codes of one K step per stage
   uint32_t wsc[2][NTILE];
-  u32x4_t wb[4][NTILE];    // bf16: ring of sub-steps, two ahead of use
   u32x4_t aq[NPASS][AW];
 
   // loads past the last K step re-read the last one (never past the rows)
   auto load_w = [&](int b, int s) {
-    if constexpr (!FP4) return;
     s = min(s, nks - 1);
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
       wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
     }
-  };
-  // bf16 sub-step j of step s into ring slot j (sub-steps past the last step re-read it)
-  auto load_wj = [&](int s, int j) {
-    if constexpr (FP4) return;
-    s = min(s, nks - 1);
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) wb[j][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 256u + 16u * j);
   };
   auto load_a = [&](int s) {
     s = min(s, nks - 1);
@@ -159,10 +151,8 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   // sub-step j+1 are converted while sub-step j's MFMAs run.
   auto compute = [&](int b, int s) {
     float scl[NTILE];
-    if constexpr (FP4) {
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[b][t] >> (8 * kg)) & 0xFFu);
-    }
+    for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[b][t] >> (8 * kg)) & 0xFFu);
     constexpr int FJ = NPL * NTA;  // fragments per sub-step
     constexpr int F = 4 * FJ;      // fragments per K step
     constexpr int D = 2;           // read-ahead distance
@@ -170,10 +160,7 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
       const int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
       return *reinterpret_cast<const bf16x8_t *>(lds(b, p) + slot(4 * kg + j, 16 * n + r16));
     };
-    auto wfrag = [&](int j, int t) {
-      if constexpr (FP4) return fp4x8_to_bf16(wq[b][t][j], scl[t]);
-      else return __builtin_bit_cast(bf16x8_t, wb[j][t]);
-    };
+    auto wfrag = [&](int j, int t) { return fp4x8_to_bf16(wq[b][t][j], scl[t]); };
     bf16x8_t bq[D + 1];
 #pragma unroll
     for (int f = 0; f < D; ++f) bq[f] = rd(f);
@@ -184,14 +171,9 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     for (int f = 0; f < F; ++f) {
       const int j = f / FJ, n = f % NTA;
       if (f + D < F) bq[(f + D) % (D + 1)] = rd(f + D);
-      if (f % FJ == 0) {
-        if (j + 1 < 4) {
+      if (f % FJ == 0 && j + 1 < 4) {
 #pragma unroll
-          for (int t = 0; t < NTILE; ++t) wa[(j + 1) & 1][t] = wfrag(j + 1, t);
-        }
-        // bf16: sub-step j+2 (of this step or the next) into its ring slot,
-        // whose previous sub-step was converted before sub-step j began
-        load_wj(j + 2 < 4 ? s : s + 1, (j + 2) & 3);
+        for (int t = 0; t < NTILE; ++t) wa[(j + 1) & 1][t] = wfrag(j + 1, t);
       }
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bq[f % (D + 1)], acc[t][n]);
@@ -209,8 +191,6 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   };
 
   load_w(0, 0);
-  load_wj(0, 0);
-  load_wj(0, 1);
   load_a(0);
   load_w(1, 1);
   store_a(0);
@@ -263,31 +243,16 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * NPL * 16 * NT * KSTEP];
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
 
-  // ---- work item (XCD-aware over the items that exist on the device).
-  // Expert chunks come from the chunk list, chunk-major (the weight blocks of
-  // one chunk share its activations); dense rows are cut into chunks of 16*NT
-  // here, block-major (the chunks of one weight block share its weights).
-  int expert, row0, nrows, nb;
-  if (g.chunks != nullptr) {
-    const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
-    const int logical = xcd_logical(total);
-    if (logical < 0) return;
-    const int chunk = logical / g.n_blocks;
-    nb = logical - chunk * g.n_blocks;
-    const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
-    expert = c.x;
-    row0 = c.y;
-    nrows = c.z;
-  } else {
-    const int nch = (g.dense_rows + 16 * NT - 1) / (16 * NT);
-    const int logical = xcd_logical(min(nch * g.n_blocks, g.grid_logical));
-    if (logical < 0) return;
-    nb = logical / nch;
-    const int chunk = logical - nb * nch;
-    expert = 0;
-    row0 = chunk * 16 * NT;
-    nrows = min(16 * NT, g.dense_rows - row0);
-  }
+  // ---- work item (XCD-aware over the items that exist on the device): expert
+  // chunks from the chunk list, chunk-major (the weight blocks of one chunk
+  // share its activations)
+  const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
+  const int logical = xcd_logical(total);
+  if (logical < 0) return;
+  const int chunk = logical / g.n_blocks;
+  const int nb = logical - chunk * g.n_blocks;
+  const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
+  const int expert = c.x, row0 = c.y, nrows = c.z;
   const int nta = min((nrows + 15) >> 4, NT);  // active 16-token tiles
   if (nta == NT) {
     pf_item<WF, AF, PAIR, NT, MT, NW>(g, lds, expert, row0, nrows, nb);
@@ -759,7 +724,8 @@ hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a,
     }
     return hipGetLastError();
   }
-  return wfmt == W_MXFP4 ? launch_wf<W_MXFP4>(afmt, pair, a, grid, st) : launch_wf<W_BF16>(afmt, pair, a, grid, st);
+  if (wfmt != W_MXFP4 || a.chunks == nullptr) return hipErrorInvalidValue;  // expert segments only
+  return launch_wf<W_MXFP4>(afmt, pair, a, grid, st);
 }
 
 }  // namespace moe
