@@ -359,7 +359,7 @@ def run_reap(mx, torch, synth):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
     ap.add_argument("--operand-mode", default="bf16x2", choices=["bf16x2", "mx8x3", "mx6x3"],

@@ -16,12 +16,29 @@ namespace {
 
 constexpr int SLOTS = 16;  // experts per lane: E <= 64 * SLOTS = 1024
 
-MOE_DEV bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Order-preserving map of a biased score onto uint32 (larger score, larger
+// key); -0 is folded onto +0 so the two compare equal, as floats do.
+MOE_DEV uint32_t order_key(float b) {
+  uint32_t u = __float_as_uint(b);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+MOE_DEV float key_value(uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key); }
 
 MOE_DEV float sigmoid(float l) { return 1.0f / (1.0f + expf(-l)); }
 
+// lanes below this one with their bit set in m
+MOE_DEV int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Lane l holds experts l + 64 i.  The k-th largest key is found by a binary
+// descent over its 32 bits, each step counting the keys at or above the
+// candidate with one ballot per slot (no cross-lane data movement).  The
+// selection is every key above it plus, among the keys equal to it, the
+// lowest expert indices; expert index order is slot-major, lane-minor, so
+// walking the slots in order with a per-slot prefix count resolves the ties
+// and also emits the selected ids in ascending order.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
@@ -34,70 +51,59 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const bool live = t < T;
   const float *lr = logits + (long long)(live ? t : 0) * E;
 
-  float v[SLOTS];
+  uint32_t key[SLOTS];  // 0 for slots past E: below every real expert
+  float sg[SLOTS];
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + 64 * i;
-    float b = -INFINITY;
+    key[i] = 0u;
+    sg[i] = 0.f;
     if (e < E) {
-      b = sigmoid(lr[e]) + bias[e];
+      sg[i] = sigmoid(lr[e]);
+      float b = sg[i] + bias[e];
       if (b != b) b = -INFINITY;
+      key[i] = order_key(b);
     }
-    v[i] = b;
   }
-  uint32_t taken = 0;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  auto rescan = [&]() {
-    bv = -INFINITY;
-    bi = 0x7fffffff;
+  auto count_ge = [&](uint32_t c) {
+    int n = 0;
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
+    for (int i = 0; i < SLOTS; ++i) n += __popcll(__ballot(key[i] >= c));
+    return n;
   };
-  rescan();
-
-  int my_sel = 0x7fffffff;
-  float kth = 0.f, kp1 = -INFINITY;
-  const int rounds = (k < E) ? k + 1 : k;
-  for (int r = 0; r < rounds; ++r) {
-    float wv = bv;
-    int wi = bi;
+  uint32_t th = 0u;  // the largest c with at least k keys >= c: the k-th largest key
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = th | (1u << bit);
+    if (count_ge(c) >= k) th = c;
+  }
+  int above = 0, at_or_above = 0;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(wv, d, 64);
-      const int oi = __shfl_xor(wi, d, 64);
-      if (better(ov, oi, wv, wi)) {
-        wv = ov;
-        wi = oi;
-      }
-    }
-    if (r < k) {
-      if (lane == r) my_sel = wi;
-      if (r == k - 1) kth = wv;
-    } else {
-      kp1 = wv;
-    }
-    if ((wi & 63) == lane) {
-      taken |= 1u << (wi >> 6);
-      rescan();
-    }
+  for (int i = 0; i < SLOTS; ++i) {
+    above += __popcll(__ballot(key[i] > th));
+    at_or_above += __popcll(__ballot(key[i] >= th));
   }
+  // (k+1)-th largest: th again if more keys equal it, else the largest key below it
+  uint32_t below = 0u;
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) below = max(below, key[i] < th ? key[i] : 0u);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) below = max(below, (uint32_t)__shfl_xor((int)below, d, 64));
+  const uint32_t kp1 = at_or_above > k ? th : below;
 
-  // ascending order of the selected ids: rank = number of smaller selected ids
-  int rank = 0;
-  for (int q = 0; q < k; ++q) {
-    const int o = __shfl(my_sel, q, 64);
-    rank += (o < my_sel) ? 1 : 0;
-  }
-  if (lane < k) {
-    sel_lds[wave][rank] = my_sel;
-    s_lds[wave][rank] = sigmoid(lr[my_sel]);
+  int need = k - above;  // keys equal to th that are selected, lowest indices first
+  int pos = 0;
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const uint64_t eq = __ballot(key[i] == th);
+    const bool sel = key[i] > th || (key[i] == th && lanes_below(eq) < need);
+    need -= min(__popcll(eq), max(need, 0));
+    const uint64_t m = __ballot(sel);
+    if (sel) {
+      const int q = pos + lanes_below(m);
+      sel_lds[wave][q] = lane + 64 * i;
+      s_lds[wave][q] = sg[i];
+    }
+    pos += __popcll(m);
   }
   __syncthreads();
   if (!live) return;
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     ids[(long long)t * k + lane] = sel_lds[wave][lane];
     w[(long long)t * k + lane] = s_lds[wave][lane] / sum;
   }
-  if (lane == 0 && gap != nullptr) gap[t] = (k < E) ? kth - kp1 : INFINITY;
+  if (lane == 0 && gap != nullptr) gap[t] = (k < E) ? key_value(th) - key_value(kp1) : INFINITY;
 }
 
 }  // namespace

@@ -84,22 +84,26 @@ LATENT_SIDE_MAX_T = 64
 class LatentMoE:
     """One Stable LatentMoE layer on the GPU: weights resident, buffers per token count.
 
-    forward(x) enqueues the shared experts (shared_expert_ffn, writes out) and,
-    at decode sizes, the latent projection (moe_route without a router,
-    writes z) on a side stream, and on the caller's stream: moe_route (router
-    and top-k, plus z at prefill sizes),
-    moe_permute, then, after the side stream, mxfp4_grouped_gemm (gate/up +
-    SiTU-GLU), mxfp4_grouped_gemm (down) and moe_combine_norm_up (adds the
+    forward(x) enqueues on a side stream, at decode sizes, the latent
+    projection (moe_route without a router, writes z) and then the shared
+    experts (shared_expert_ffn, writes out); on the caller's stream: moe_route
+    (router and top-k, plus z at prefill sizes), moe_permute, then, once z is
+    there, mxfp4_grouped_gemm (gate/up + SiTU-GLU), mxfp4_grouped_gemm (down)
+    and, once the shared experts are done, moe_combine_norm_up (adds the
     routed part to out).  The side stream's work depends only on x, so it
-    overlaps the latency-bound routing steps, and the expert GEMMs then stream
-    alone; the two output parts are added once, so the result is the same as
-    running the calls in sequence.  z runs on the side stream only at
-    decode-sized token counts (T <= 64); latent_on_side=False keeps it on the
-    caller's stream always.
+    overlaps the latency-bound routing steps; the two output parts are added
+    once, so the result is the same as running the calls in sequence.
+
+    z runs on the side stream only at decode-sized token counts (T <= 64);
+    latent_on_side=False keeps it on the caller's stream always.
+    late_shared_join=False joins the whole side stream before the expert
+    GEMMs instead (at decode sizes that puts the shared experts on the path to
+    the expert GEMMs; at prefill sizes the two joins measure the same).
+    overlap_shared=False runs everything on the caller's stream.
     """
 
     def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True,
-                 latent_on_side: bool = True):
+                 latent_on_side: bool = True, late_shared_join: bool = True):
         missing = [k for k in WEIGHT_KEYS if k not in weights]
         if missing:
             raise ValueError(f"missing weights: {missing}")
@@ -113,6 +117,10 @@ class LatentMoE:
         # the top-k; at prefill sizes z stays on the main stream, where it runs
         # beside the shared experts instead of after them
         self.latent_on_side = latent_on_side and overlap_shared
+        # late join: z runs first on the side stream and the expert GEMMs wait
+        # only for it; the shared experts then overlap the expert GEMMs and are
+        # joined before moe_combine_norm_up, which adds onto their output
+        self.late_shared_join = late_shared_join and overlap_shared
         # default-priority side stream for the shared experts
         self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None
 
@@ -168,21 +176,30 @@ class LatentMoE:
 
         shared = s.n_shared * s.shared_inter > 0
         lat_side = self.latent_on_side and T <= LATENT_SIDE_MAX_T
+        late = self.late_shared_join
+        z_done = None
         if shared and side is not st:
             # side stream: the shared experts, during the latency-bound routing steps
             side.wait_stream(st)
             x.record_stream(side)
+            latent = lambda: call("moe_route_latent", side,  # noqa: E731
+                                  lambda: route(s, x, None, None, w["w_down"], None, None, b["z"], None,
+                                                b["ws_shared"], side))
+            if lat_side and late:
+                latent()
+                z_done = torch.cuda.Event()
+                z_done.record(side)
             call("shared_expert_ffn", side,
                  lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, b["ws_shared"],
                                     side))
-            if lat_side:
-                call("moe_route_latent", side,
-                     lambda: route(s, x, None, None, w["w_down"], None, None, b["z"], None, b["ws_shared"], side))
+            if lat_side and not late:
+                latent()
             side_done = torch.cuda.Event()
             side_done.record(side)
         elif shared:
             call("shared_expert_ffn", st,
-                 lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, ws, st))
+                 lambda: shared_ffn(s, x, w["sh_gate"], w["sh_up"], w["sh_down"], b["out"], 0, b["ws_shared"],
+                                    st))
         z_main = not (shared and side is not st and lat_side)
         call("moe_route", st, lambda: route(s, x, w["w_router"], w["bias"], w["w_down"] if z_main else None,
                                             b["topk_ids"], b["topk_w"], b["z"] if z_main else None, b["gap"],
@@ -190,8 +207,11 @@ class LatentMoE:
         call("moe_permute", st, lambda: permute(s, b["topk_ids"], b["offsets"], b["sorted_pair"], b["pair_pos"],
                                                 b["active"], ws, st))
         if shared and side is not st:
-            # the expert GEMMs stream weights at full bandwidth on their own
-            st.wait_event(side_done)
+            if not late:
+                # the expert GEMMs stream weights at full bandwidth on their own
+                st.wait_event(side_done)
+            elif z_done is not None:
+                st.wait_event(z_done)
         call("grouped_gemm_gateup", st,
              lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"],
                                   w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"],
@@ -199,6 +219,8 @@ class LatentMoE:
         call("grouped_gemm_down", st,
              lambda: grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
                                   w["w2_scale"], None, None, None, b["Y"], ws, st))
+        if shared and side is not st and late:
+            st.wait_event(side_done)
         call("moe_combine_norm_up", st,
              lambda: combine_norm_up(s, T, b["Y"], b["pair_pos"], b["topk_w"], w["gamma"], w["w_up"], b["out"],
                                      1 if shared else 0, ws, st))

@@ -37,11 +37,11 @@ def k3(mx):
     return {"w": w, "dense": dense, "cache": expert_cache(wl)}
 
 
-def _run_layer(mx, k3, wl, bias_np=None, operand_mode=0):
+def _run_layer(mx, k3, wl, bias_np=None, operand_mode=0, **schedule):
     w = dict(k3["w"])
     if bias_np is not None:
         w["bias"] = to_dev(bias_np, DEV)
-    moe = mx.LatentMoE(mx.shape_of(wl.shape, operand_mode), w, DEV)
+    moe = mx.LatentMoE(mx.shape_of(wl.shape, operand_mode), w, DEV, **schedule)
     x = upload_tokens(wl, DEV)
     bufs = moe.forward(x)
     torch.cuda.synchronize()
@@ -82,6 +82,22 @@ def test_decode_T16(mx, k3):
     bias = synth.gen_bias(wl)
     err = _full_check(mx, k3, wl, bias, np.array([0, 7, 15]), "decode")
     assert err < 1e-3
+
+
+@pytest.mark.parametrize("wl_name", ["decode", "batched_decode"])
+def test_schedules_bitwise_equal(mx, k3, wl_name):
+    """The layer's stream schedules (z, at decode sizes, joined before the
+    expert GEMMs and the shared experts before the combine; the whole side
+    stream joined before the expert GEMMs; one stream) run the same kernels on
+    the same data, so every buffer is bitwise the same."""
+    wl = synth.workload(wl_name)
+    bias = None if wl.bias_mode == "normal" else synth.gen_bias(wl, ZIPF_BIAS)
+    say(f"case: {wl_name} (T={wl.tokens}) layer under three stream schedules")
+    base = _run_layer(mx, k3, wl, bias)
+    for sched in ({"overlap_shared": False}, {"late_shared_join": False}):
+        g = _run_layer(mx, k3, wl, bias, **sched)
+        for key in ("topk_ids", "topk_w", "z", "sorted_pair", "pair_pos", "H", "Y", "out"):
+            assert np.array_equal(g[key], base[key]), (sched, key)
 
 
 def test_batched_decode_T256_zipf(mx, k3):
