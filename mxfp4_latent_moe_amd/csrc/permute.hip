@@ -3,7 +3,8 @@
 // kimi-k3-mlx README, REAP section, two-bank paragraph: once the pairs are
 // sorted by expert index each expert owns a contiguous slice of rows.  Pair
 // p = t*k + j; inside an expert's slice the pairs keep their order, so tokens
-// ascend.  Three passes, none with an order-dependent result:
+// ascend.  Three passes, none with an order-dependent result (one workgroup
+// runs all three when the tokens fit one block):
 //   1. per block of 64 tokens, a histogram of expert ids (LDS counters);
 //   2. one workgroup turns the histograms into per-block absolute bases,
 //      expert offsets and the list of active experts (scans);
@@ -111,6 +112,56 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t *__restr
   }
 }
 
+// All three passes in one workgroup for a single block of tokens (T <= 64):
+// histogram in LDS, the two scans, then wavefront 0 scatters the tokens in
+// order.  Same results as the three kernels, one launch instead of three.
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int k,
+                                                          int E, int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ sorted_pair,
+                                                          int32_t *__restrict__ pair_pos,
+                                                          int32_t *__restrict__ active) {
+  __shared__ int cur[1024];
+  __shared__ int wave_tot[16];
+  const int e = threadIdx.x;
+  if (e < E) cur[e] = 0;
+  __syncthreads();
+  const int P = T * k;
+  for (int i = threadIdx.x; i < P; i += 1024) {
+    const int x = ids[i];
+    if ((unsigned)x < (unsigned)E) atomicAdd(&cur[x], 1);  // ids outside [0, E) are dropped
+  }
+  __syncthreads();
+  const int cnt = e < E ? cur[e] : 0;
+  int total;
+  const int off = block_excl_scan(cnt, wave_tot, &total);
+  if (e < E) {
+    offsets[e] = off;
+    cur[e] = off;  // this thread's own counter: the scan's barriers ordered every read of it
+  }
+  if (e == 0) offsets[E] = P;
+  const int flag = (e < E && cnt > 0) ? 1 : 0;
+  int nact;
+  const int pos = block_excl_scan(flag, wave_tot, &nact);
+  if (active != nullptr) {
+    if (flag) active[1 + pos] = e;
+    if (e == 0) active[0] = nact;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  for (int t = 0; t < T; ++t) {
+    if (lane < k) {
+      const int p = t * k + lane;
+      const int x = ids[p];
+      if ((unsigned)x >= (unsigned)E) continue;
+      const int q = cur[x];
+      cur[x] = q + 1;  // a token holds each expert at most once
+      sorted_pair[q] = p;
+      pair_pos[p] = q;
+    }
+  }
+}
+
 }  // namespace
 
 int permute_blocks(int T) { return (T + TB - 1) / TB; }
@@ -119,6 +170,11 @@ hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *blk,
                           int32_t *sorted_pair, int32_t *pair_pos, int32_t *active,
                           hipStream_t st) {
   const int nblk = permute_blocks(T);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, st, ids, T, k, E, offsets, sorted_pair,
+                       pair_pos, active);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(256), 0, st, ids, T, k, E, blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
