@@ -10,15 +10,20 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_norm_kernel(const float *__restrict__ Y,
-                                                           const int32_t *__restrict__ pair_pos,
-                                                           const float *__restrict__ w,
-                                                           const uint16_t *__restrict__ gamma,
-                                                           int k, int L, float eps,
-                                                           float *__restrict__ yn) {
+// One workgroup of 1024 threads per token: each thread owns 4 columns (one
+// pass covers L <= 4096), loads its k rows in batches of 8 before summing them
+// in order j = 0..k-1, and the sum of squares goes through a fixed-order
+// reduction over the 16 waves.
+__global__ __launch_bounds__(1024) void combine_norm_kernel(const float *__restrict__ Y,
+                                                            const int32_t *__restrict__ pair_pos,
+                                                            const float *__restrict__ w,
+                                                            const uint16_t *__restrict__ gamma,
+                                                            int k, int L, float eps,
+                                                            float *__restrict__ yn) {
+  constexpr int NTHR = 1024, B = 8;
   __shared__ long long rows[32];
   __shared__ float wts[32];
-  __shared__ float red[4];
+  __shared__ float red[NTHR / 64];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid < k) {
@@ -28,11 +33,16 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float *__restri
   __syncthreads();
   float *out = yn + (long long)t * L;
   float ss = 0.f;
-  for (int c = tid * 4; c < L; c += 1024) {
+  for (int c = tid * 4; c < L; c += NTHR * 4) {
     f32x4_t y = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(Y + rows[j] * L + c);
-      y += wts[j] * v;
+    for (int j0 = 0; j0 < k; j0 += B) {
+      f32x4_t v[B];
+#pragma unroll
+      for (int jj = 0; jj < B; ++jj)
+        if (j0 + jj < k) v[jj] = *reinterpret_cast<const f32x4_t *>(Y + rows[j0 + jj] * L + c);
+#pragma unroll
+      for (int jj = 0; jj < B; ++jj)
+        if (j0 + jj < k) y += wts[j0 + jj] * v[jj];
     }
     *reinterpret_cast<f32x4_t *>(out + c) = y;
     ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
@@ -41,9 +51,11 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float *__restri
   for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NTHR / 64; ++i) tot += red[i];
   const float scale = 1.0f / sqrtf(tot / (float)L + eps);
-  for (int c = tid * 4; c < L; c += 1024) {
+  for (int c = tid * 4; c < L; c += NTHR * 4) {
     f32x4_t y = *reinterpret_cast<const f32x4_t *>(out + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = y[e] * scale * __uint_as_float((uint32_t)gamma[c + e] << 16);
@@ -56,7 +68,7 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float *__restri
 hipError_t launch_combine_norm(const float *Y, const int32_t *pair_pos, const float *w,
                                const uint16_t *gamma, int T, int k, int L, float eps, float *yn,
                                hipStream_t st) {
-  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(256), 0, st, Y, pair_pos, w, gamma, k, L, eps,
+  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(1024), 0, st, Y, pair_pos, w, gamma, k, L, eps,
                      yn);
   return hipGetLastError();
 }
