@@ -352,8 +352,34 @@ def run_reap(mx, torch, synth):
     ms = e0.elapsed_time(e1) / steps
     nbytes = P * L * 4 + P * 16 + E * 20
     gbs = nbytes / (ms * 1e-3) / 1e9
+
+    # the same sums fused into the combine (moe_combine_norm_up_reap), timed
+    # against the plain combine + RMSNorm + up_proj over the same batch
+    pair_pos = torch.empty_like(sorted_pair)
+    pair_pos[sorted_pair.long()] = torch.arange(P, device=dev, dtype=torch.int32)
+    gamma = torch.ones(L, device=dev, dtype=torch.bfloat16)
+    w_up = (torch.randn((sh.hidden, L), device=dev, generator=g) * L ** -0.5).to(torch.bfloat16)
+    out = torch.empty((T, sh.hidden), device=dev, dtype=torch.float32)
+    wsc = torch.empty(ops.workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP_REAP, T), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    plain_ms = timed(lambda: ops.combine_norm_up(s, T, Y, pair_pos, w, gamma, w_up, out, 0, wsc))
+    fused_ms = timed(lambda: ops.combine_norm_up_reap(s, T, Y, pair_pos, w, gamma, w_up, out, 0, offsets, sal,
+                                                      cnt, 1, wsc))
     return {"workload": "REAP saliency, 4096 tokens x top-16 over 896 experts, L=3584, synthetic rows",
-            "ms": round(ms, 4), "bytes": nbytes, "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "ms": round(ms, 4), "bytes": nbytes, "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "fused_into_combine": {"combine_norm_up_ms": round(plain_ms, 4), "with_reap_ms": round(fused_ms, 4),
+                                   "reap_extra_ms": round(fused_ms - plain_ms, 4)}}
 
 
 def main():

@@ -79,6 +79,7 @@ extern "C" {
 #define MOE_FN_COMBINE_NORM_UP 3
 #define MOE_FN_SHARED_FFN 4
 #define MOE_FN_REAP_SALIENCY 5
+#define MOE_FN_COMBINE_NORM_UP_REAP 6
 
 typedef struct {
   int32_t hidden;       /* H: residual width (7168 for K3) */
@@ -233,6 +234,28 @@ int shared_expert_ffn(const moe_shape *shape, int T, const uint16_t *x, const ui
 int moe_reap_saliency(const moe_shape *shape, int P, const int32_t *expert_offsets, const float *Y,
                       const float *pair_weight, const int32_t *sorted_pair, double *sal_sum,
                       int64_t *counts, int accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_combine_norm_up with the REAP saliency accumulation fused into it: the
+ * combine reads every expert output row of the batch anyway, so the row norms
+ * ||e_j(x)||_2 are taken in the same pass instead of a second read of Y.
+ * Follows: kimi-k3-mlx README, REAP section (S_j as for moe_reap_saliency) and
+ * the sources cited at moe_combine_norm_up.
+ *   T .. accumulate   as for moe_combine_norm_up; out is bitwise what that call
+ *                     writes.  g is topk_w, or 1 when topk_w is NULL (the rows
+ *                     of Y already carry their weight: ||g e|| = g ||e||).
+ *   expert_offsets    [E+1] int32 from moe_permute (expert j owns sorted rows
+ *                     offsets[j] .. offsets[j+1] of Y)
+ *   sal_sum, counts   [E] float64 / int64, as for moe_reap_saliency
+ *   reap_accumulate   0: overwrite sal_sum and counts; 1: add to them
+ * Deterministic: fixed-order reductions, no atomics.  Workspace:
+ * moe_workspace_bytes(shape, MOE_FN_COMBINE_NORM_UP_REAP, T) bytes.
+ * Errors: those of moe_combine_norm_up; MOE_EINVAL (null expert_offsets,
+ * sal_sum or counts, reap_accumulate not 0/1); MOE_ENOTSUP (latent > 4096:
+ * the fused pass holds a whole row per workgroup pass). */
+int moe_combine_norm_up_reap(const moe_shape *shape, int T, const float *Y, const int32_t *pair_pos,
+                             const float *topk_w, const uint16_t *gamma, const uint16_t *w_up, float *out,
+                             int accumulate, const int32_t *expert_offsets, double *sal_sum, int64_t *counts,
+                             int reap_accumulate, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

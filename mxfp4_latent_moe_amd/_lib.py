@@ -17,10 +17,11 @@ MOE_OPND_BF16X2, MOE_OPND_BF16, MOE_OPND_MX8X3, MOE_OPND_MX6X3 = 0, 1, 2, 3
 MOE_OP_GATEUP_SITU, MOE_OP_DOWN = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP, MOE_FN_SHARED_FFN,
- MOE_FN_REAP_SALIENCY) = range(6)
+ MOE_FN_REAP_SALIENCY, MOE_FN_COMBINE_NORM_UP_REAP) = range(7)
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute",
-           "mxfp4_grouped_gemm", "moe_combine_norm_up", "shared_expert_ffn", "moe_reap_saliency")
+           "mxfp4_grouped_gemm", "moe_combine_norm_up", "shared_expert_ffn", "moe_reap_saliency",
+           "moe_combine_norm_up_reap")
 
 
 class MoeShape(ctypes.Structure):
@@ -70,6 +71,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.shared_expert_ffn.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.moe_reap_saliency.restype = i32
     lib.moe_reap_saliency.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.moe_combine_norm_up_reap.restype = i32
+    lib.moe_combine_norm_up_reap.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
     if path is None:
         _lib = lib
     return lib

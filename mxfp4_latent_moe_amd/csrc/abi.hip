@@ -117,6 +117,11 @@ CombineWs combine_ws(const moe_shape *s, int T) {
   return w;
 }
 
+// the combine's workspace, then one fp32 REAP contribution per pair
+size_t combine_reap_ws(const moe_shape *s, int T) {
+  return combine_ws(s, T).total + align_up((size_t)T * s->top_k * sizeof(float));
+}
+
 struct SharedWs {
   size_t hs, partial, planes, total;
   GemmPlan pgu, pdn;
@@ -210,6 +215,38 @@ int guarded(F &&f) {
 
 }  // namespace
 
+// The combine call, with the REAP saliency pass fused in when sal_sum is given
+// (its per-row contributions go to the workspace after the combine's own).
+static int combine_norm_up_impl(const moe_shape *s, int T, const float *Y, const int32_t *pair_pos,
+                                const float *topk_w, const uint16_t *gamma, const uint16_t *w_up, float *out,
+                         int accumulate, const int32_t *expert_offsets, double *sal_sum, int64_t *counts,
+                         int reap_accumulate, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T <= 0 || !Y || !pair_pos || !gamma || !w_up || !out || !ws) return MOE_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
+  if (!aligned16(Y) || !aligned16(w_up) || !aligned16(out) || !aligned16(ws)) return MOE_EINVAL;
+  const bool reap = sal_sum != nullptr;
+  if (reap && s->latent > 4096) return MOE_ENOTSUP;
+  const CombineWs w = combine_ws(s, T);
+  const size_t need = reap ? combine_reap_ws(s, T) : w.total;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float *yn = reinterpret_cast<float *>(wsp(ws, w.yn));
+  float *contrib = reap ? reinterpret_cast<float *>(wsp(ws, w.total)) : nullptr;
+  if (launch_combine_norm(Y, pair_pos, topk_w, gamma, T, s->top_k, s->latent, s->rms_eps, yn, contrib, st) !=
+      hipSuccess)
+    return MOE_EHIP;
+  if (reap && launch_reap_experts(contrib, expert_offsets, s->n_experts, sal_sum,
+                                  reinterpret_cast<long long *>(counts), reap_accumulate, st) != hipSuccess)
+    return MOE_EHIP;
+  GemmArgs a = dense_args(w.pu, yn, s->latent, w_up, nullptr, s->hidden, s->latent, out, s->hidden, accumulate,
+                          T, reinterpret_cast<float *>(wsp(ws, w.partial)), s);
+  if (run_dense(w.pu, afmt_of(s), false, a, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -240,6 +277,7 @@ size_t moe_workspace_bytes(const moe_shape *s, int fn, int n) {
       if (s->n_shared * s->shared_inter == 0) return ALIGN;
       return shared_ws(s, n).total;
     case MOE_FN_REAP_SALIENCY: return align_up((size_t)n * sizeof(float));
+    case MOE_FN_COMBINE_NORM_UP_REAP: return combine_reap_ws(s, n);
     default: return 0;
   }
 }
@@ -406,24 +444,20 @@ int moe_combine_norm_up(const moe_shape *s, int T, const float *Y, const int32_t
                         const float *topk_w, const uint16_t *gamma, const uint16_t *w_up,
                         float *out, int accumulate, void *ws, size_t ws_bytes, void *stream) {
   return guarded([&]() -> int {
-    int rc = check_shape(s);
-    if (rc) return rc;
-    if (T <= 0 || !Y || !pair_pos || !gamma || !w_up || !out || !ws) return MOE_EINVAL;
-    if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
-    if (!aligned16(Y) || !aligned16(w_up) || !aligned16(out) || !aligned16(ws)) return MOE_EINVAL;
-    const CombineWs w = combine_ws(s, T);
-    if (ws_bytes < w.total) return MOE_EWORKSPACE;
-    if ((rc = check_device())) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    float *yn = reinterpret_cast<float *>(wsp(ws, w.yn));
-    if (launch_combine_norm(Y, pair_pos, topk_w, gamma, T, s->top_k, s->latent, s->rms_eps, yn,
-                            st) != hipSuccess)
-      return MOE_EHIP;
-    GemmArgs a = dense_args(w.pu, yn, s->latent, w_up, nullptr, s->hidden, s->latent, out,
-                            s->hidden, accumulate, T, reinterpret_cast<float *>(wsp(ws, w.partial)),
-                            s);
-    if (run_dense(w.pu, afmt_of(s), false, a, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
-    return MOE_OK;
+    return combine_norm_up_impl(s, T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, nullptr, nullptr,
+                                nullptr, 0, ws, ws_bytes, stream);
+  });
+}
+
+int moe_combine_norm_up_reap(const moe_shape *s, int T, const float *Y, const int32_t *pair_pos,
+                             const float *topk_w, const uint16_t *gamma, const uint16_t *w_up, float *out,
+                             int accumulate, const int32_t *expert_offsets, double *sal_sum, int64_t *counts,
+                             int reap_accumulate, void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    if (!expert_offsets || !sal_sum || !counts) return MOE_EINVAL;
+    if (reap_accumulate != 0 && reap_accumulate != 1) return MOE_EINVAL;
+    return combine_norm_up_impl(s, T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, expert_offsets,
+                                sal_sum, counts, reap_accumulate, ws, ws_bytes, stream);
   });
 }
 

@@ -14,16 +14,25 @@ namespace {
 // pass covers L <= 4096), loads its k rows in batches of 8 before summing them
 // in order j = 0..k-1, and the sum of squares goes through a fixed-order
 // reduction over the 16 waves.
+//
+// REAP: the same pass also takes each row's sum of squares (the unweighted
+// expert output e_j(x)), reduces it per row over the wavefronts in a fixed
+// order and writes g * ||e_j(x)||_2 to contrib at the row's sorted position
+// (kimi-k3-mlx README, REAP section).  That needs every column of a row in one
+// pass, so L <= 4096; the combined output is computed exactly as without it.
+template <bool REAP>
 __global__ __launch_bounds__(1024) void combine_norm_kernel(const float *__restrict__ Y,
                                                             const int32_t *__restrict__ pair_pos,
                                                             const float *__restrict__ w,
                                                             const uint16_t *__restrict__ gamma,
                                                             int k, int L, float eps,
-                                                            float *__restrict__ yn) {
-  constexpr int NTHR = 1024, B = 8;
+                                                            float *__restrict__ yn,
+                                                            float *__restrict__ contrib) {
+  constexpr int NTHR = 1024, B = 8, NWV = NTHR / 64;
   __shared__ long long rows[32];
   __shared__ float wts[32];
-  __shared__ float red[NTHR / 64];
+  __shared__ float red[NWV];
+  __shared__ float rsq[REAP ? 32 : 1][NWV];  // per row, per wave: partial sums of squares
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid < k) {
@@ -33,24 +42,54 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(const float *__restr
   __syncthreads();
   float *out = yn + (long long)t * L;
   float ss = 0.f;
-  for (int c = tid * 4; c < L; c += NTHR * 4) {
+  // y_t over this thread's columns: k rows loaded in batches of B, summed in
+  // order j = 0..k-1 (the same arithmetic with and without REAP)
+  auto combine = [&](int c, bool in) {
     f32x4_t y = {0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += B) {
       f32x4_t v[B];
 #pragma unroll
-      for (int jj = 0; jj < B; ++jj)
-        if (j0 + jj < k) v[jj] = *reinterpret_cast<const f32x4_t *>(Y + rows[j0 + jj] * L + c);
+      for (int jj = 0; jj < B; ++jj) {
+        v[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (in && j0 + jj < k) v[jj] = *reinterpret_cast<const f32x4_t *>(Y + rows[j0 + jj] * L + c);
+      }
 #pragma unroll
       for (int jj = 0; jj < B; ++jj)
         if (j0 + jj < k) y += wts[j0 + jj] * v[jj];
+      if constexpr (REAP) {
+        // every lane takes part (lanes past L hold zeros), so the wave sums are whole
+#pragma unroll
+        for (int jj = 0; jj < B; ++jj) {
+          if (j0 + jj >= k) break;
+          float q = v[jj][0] * v[jj][0] + v[jj][1] * v[jj][1] + v[jj][2] * v[jj][2] + v[jj][3] * v[jj][3];
+#pragma unroll
+          for (int d = 32; d >= 1; d >>= 1) q += __shfl_xor(q, d, 64);
+          if ((tid & 63) == 0) rsq[j0 + jj][tid >> 6] = q;
+        }
+      }
     }
-    *reinterpret_cast<f32x4_t *>(out + c) = y;
-    ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+    if (in) {
+      *reinterpret_cast<f32x4_t *>(out + c) = y;
+      ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+    }
+  };
+  if constexpr (REAP) {
+    combine(tid * 4, tid * 4 < L);  // one pass: L <= 4 * NTHR
+  } else {
+    for (int c = tid * 4; c < L; c += NTHR * 4) combine(c, true);
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
+  if constexpr (REAP) {
+    if (tid < k) {
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) q += rsq[tid][i];
+      contrib[rows[tid]] = wts[tid] * __builtin_sqrtf(q);
+    }
+  }
   float tot = 0.f;
 #pragma unroll
   for (int i = 0; i < NTHR / 64; ++i) tot += red[i];
@@ -67,9 +106,15 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(const float *__restr
 
 hipError_t launch_combine_norm(const float *Y, const int32_t *pair_pos, const float *w,
                                const uint16_t *gamma, int T, int k, int L, float eps, float *yn,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(1024), 0, st, Y, pair_pos, w, gamma, k, L, eps,
-                     yn);
+                               float *contrib, hipStream_t st) {
+  if (contrib != nullptr) {
+    if (L > 4096) return hipErrorInvalidValue;  // the REAP pass needs a row in one pass
+    hipLaunchKernelGGL(combine_norm_kernel<true>, dim3(T), dim3(1024), 0, st, Y, pair_pos, w, gamma, k, L,
+                       eps, yn, contrib);
+  } else {
+    hipLaunchKernelGGL(combine_norm_kernel<false>, dim3(T), dim3(1024), 0, st, Y, pair_pos, w, gamma, k, L,
+                       eps, yn, contrib);
+  }
   return hipGetLastError();
 }
 

@@ -134,8 +134,12 @@ hipError_t launch_reap(const float *Y, int P, int L, const float *pair_weight, c
                        const int32_t *offsets, int E, double *sal_sum, long long *counts, int accumulate,
                        float *contrib, hipStream_t st);
 
+// contrib != nullptr: also g * ||Y row||_2 per sorted row (L <= 4096)
 hipError_t launch_combine_norm(const float *Y, const int32_t *pair_pos, const float *w,
                                const uint16_t *gamma, int T, int k, int L, float eps, float *yn,
-                               hipStream_t st);
+                               float *contrib, hipStream_t st);
+// the per-expert pass of launch_reap alone, over contributions already made
+hipError_t launch_reap_experts(const float *contrib, const int32_t *offsets, int E, double *sal_sum,
+                               long long *counts, int accumulate, hipStream_t st);
 
 }  // namespace moe

@@ -78,6 +78,11 @@ hipError_t launch_reap(const float *Y, int P, int L, const float *pair_weight, c
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return launch_reap_experts(contrib, offsets, E, sal_sum, counts, accumulate, st);
+}
+
+hipError_t launch_reap_experts(const float *contrib, const int32_t *offsets, int E, double *sal_sum,
+                               long long *counts, int accumulate, hipStream_t st) {
   hipLaunchKernelGGL(reap_experts_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, st, contrib, offsets, E,
                      sal_sum, counts, accumulate);
   return hipGetLastError();

@@ -1,5 +1,5 @@
-"""Torch-facing wrappers of the C-ABI calls (the five of the layer and the REAP
-saliency), and a layer object that chains the layer's calls on one stream.  Argument marshalling only: tensors are passed as
+"""Torch-facing wrappers of the C-ABI calls (the five of the layer, the REAP
+saliency and the combine with REAP fused in), and a layer object that chains the layer's calls on one stream.  Argument marshalling only: tensors are passed as
 device pointers, the stream as its HIP handle; all compute runs in the HIP
 library."""
 from __future__ import annotations
@@ -70,6 +70,15 @@ def reap_saliency(shape, P, offsets, Y, pair_weight, sorted_pair, sal_sum, count
           load().moe_reap_saliency(shape, int(P), _p(offsets), _p(Y), _p(pair_weight), _p(sorted_pair),
                                    _p(sal_sum), _p(counts), int(accumulate), _p(ws),
                                    0 if ws is None else ws.numel(), _s(stream)))
+
+
+def combine_norm_up_reap(shape, T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, offsets, sal_sum, counts,
+                         reap_accumulate, ws, stream=None):
+    """moe_combine_norm_up plus the REAP saliency sums of the batch, see moe_combine_norm_up_reap."""
+    check("moe_combine_norm_up_reap",
+          load().moe_combine_norm_up_reap(shape, T, _p(Y), _p(pair_pos), _p(topk_w), _p(gamma), _p(w_up),
+                                          _p(out), int(accumulate), _p(offsets), _p(sal_sum), _p(counts),
+                                          int(reap_accumulate), _p(ws), ws.numel(), _s(stream)))
 
 
 WEIGHT_KEYS = ("w_router", "bias", "w_down", "w_up", "gamma", "sh_gate", "sh_up", "sh_down",

@@ -60,9 +60,12 @@ def _shape(**kw):
 
 def test_workspace_bytes(lib):
     s = _shape()
-    for fn in range(6):
+    for fn in range(7):
         assert lib.moe_workspace_bytes(s, fn, 16) > 0
     assert lib.moe_workspace_bytes(s, 7, 16) == 0
+    # the fused combine needs the combine's workspace plus one fp32 per pair
+    assert (lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP_REAP, 16)
+            >= lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP, 16) + 16 * s.top_k * 4)
     assert lib.moe_workspace_bytes(s, 0, 0) == 0
     bad = _shape(latent=100)
     assert lib.moe_workspace_bytes(bad, 0, 16) == 0
@@ -181,3 +184,26 @@ def test_reap_saliency_validation(lib):
     a = list(args)
     a[9] = ws - 1
     assert lib.moe_reap_saliency(s, *a) == _lib.MOE_EWORKSPACE
+
+
+def test_combine_reap_validation(lib):
+    s = _shape()
+    T = 16
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP_REAP, T)
+    # T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, offsets, sal_sum, counts, reap_accumulate, ws, bytes
+    args = [T, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 0, FAKE, ws, None]
+    for i in (8, 9, 10):  # offsets, sal_sum, counts
+        a = list(args)
+        a[i] = None
+        assert lib.moe_combine_norm_up_reap(s, *a) == _lib.MOE_EINVAL, i
+    for i, v in ((7, 2), (11, 2), (0, 0)):  # accumulate, reap_accumulate, T
+        a = list(args)
+        a[i] = v
+        assert lib.moe_combine_norm_up_reap(s, *a) == _lib.MOE_EINVAL, i
+    a = list(args)
+    a[13] = lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP, T)  # the plain combine's is too small
+    assert lib.moe_combine_norm_up_reap(s, *a) == _lib.MOE_EWORKSPACE
+    wide = _shape(latent=4224)  # a whole row per pass: latent <= 4096
+    a = list(args)
+    a[13] = lib.moe_workspace_bytes(wide, _lib.MOE_FN_COMBINE_NORM_UP_REAP, T)
+    assert lib.moe_combine_norm_up_reap(wide, *a) == _lib.MOE_ENOTSUP
