@@ -29,6 +29,8 @@ Modules:
              per-pair Python loops, its own bit-level e2m1 decoding)
   reap    -- REAP expert saliency over a calibration batch (README, REAP
              section)
+  promotion -- the moe_k_hi cap on promoted (MXFP4) experts per token
+             (Kimi-K3-Alis-MLX-Dynamic card, Build recipe)
 
 Parity status: the whole-layer result has no worked input/output example on
 the pages; it is pinned by the independent scalar oracle, by closed forms and
