@@ -130,6 +130,26 @@ int moe_route(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *
               const float *bias, const uint16_t *w_down, int32_t *topk_ids, float *topk_w,
               float *z, float *gap, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route with the moe_k_hi cap on promoted experts.
+ * Follows: Kimi-K3-Alis-MLX-Dynamic card, Build recipe (experts that matter
+ * stay in MXFP4, "promoted"; the serving configuration caps that path at
+ * moe_k_hi = 4 promoted experts per token of the 16 routed, and the
+ * contribution of a token's 5th and later promoted expert is dropped rather
+ * than downgraded).
+ *   promoted  [E] uint8, device: nonzero marks a promoted expert
+ *   k_hi      >= 0; k_hi >= top_k leaves the routing as moe_route's
+ *   the rest  as for moe_route (w_router required)
+ * Routing order is the top-k's: larger biased score first, ties to the lower
+ * index.  A selected promoted expert with k_hi selected promoted experts ahead
+ * of it gets topk_w = 0; ids, gap and the other weights (normalised over all k
+ * selected experts) are exactly moe_route's.
+ * Errors: those of moe_route; MOE_EINVAL for a null promoted or w_router, or
+ * k_hi < 0. */
+int moe_route_capped(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *w_router,
+                     const float *bias, const uint16_t *w_down, const uint8_t *promoted, int k_hi,
+                     int32_t *topk_ids, float *topk_w, float *z, float *gap, void *ws, size_t ws_bytes,
+                     void *stream);
+
 /* Token permutation: stable counting sort of the pairs p = t*k + j by expert.
  * Follows: kimi-k3-mlx README, REAP section, two-bank paragraph (pairs sorted
  * by expert index give each expert a contiguous slice).

@@ -21,7 +21,7 @@ MOE_DT_F32, MOE_DT_BF16 = 0, 1
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute",
            "mxfp4_grouped_gemm", "moe_combine_norm_up", "shared_expert_ffn", "moe_reap_saliency",
-           "moe_combine_norm_up_reap")
+           "moe_combine_norm_up_reap", "moe_route_capped")
 
 
 class MoeShape(ctypes.Structure):
@@ -71,6 +71,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.shared_expert_ffn.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.moe_reap_saliency.restype = i32
     lib.moe_reap_saliency.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.moe_route_capped.restype = i32
+    lib.moe_route_capped.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine_norm_up_reap.restype = i32
     lib.moe_combine_norm_up_reap.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
     if path is None:

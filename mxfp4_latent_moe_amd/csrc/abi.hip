@@ -215,6 +215,43 @@ int guarded(F &&f) {
 
 }  // namespace
 
+// Router, top-k (capped when `promoted` is given) and the latent projection.
+static int route_impl(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_router, const float *bias,
+                      const uint16_t *w_down, const uint8_t *promoted, int k_hi, int32_t *topk_ids, float *topk_w,
+                      float *z, float *gap, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (T <= 0 || !x || !ws) return MOE_EINVAL;
+  if ((w_down == nullptr) != (z == nullptr)) return MOE_EINVAL;
+  // routing needs the router, bias and both outputs; without a router only z is computed
+  const bool routing = w_router != nullptr;
+  if (routing && (!bias || !topk_ids || !topk_w)) return MOE_EINVAL;
+  if (!routing && (bias || topk_ids || topk_w || gap || !z)) return MOE_EINVAL;
+  if ((routing && !aligned16(w_router)) || (w_down && !aligned16(w_down)) || !aligned16(x) ||
+      (z && !aligned16(z)) || !aligned16(ws))
+    return MOE_EINVAL;
+  const RouteWs w = route_ws(s, T);
+  if (ws_bytes < w.total) return MOE_EWORKSPACE;
+  if ((rc = check_device())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float *logits = reinterpret_cast<float *>(wsp(ws, w.logits));
+  float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
+  if (routing) {
+    GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
+                            s->n_experts, 0, T, partial, s);
+    if (run_dense(w.pr, A_BF16, false, a, nullptr, st) != hipSuccess) return MOE_EHIP;
+    if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, promoted, k_hi, st) !=
+        hipSuccess)
+      return MOE_EHIP;
+  }
+  if (z) {
+    GemmArgs d = dense_args(w.pd, x, s->hidden, w_down, nullptr, s->latent, s->hidden, z, s->latent, 0, T,
+                            partial, s);
+    if (run_dense(w.pd, A_BF16, false, d, nullptr, st) != hipSuccess) return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
 // The combine call, with the REAP saliency pass fused in when sal_sum is given
 // (its per-row contributions go to the workspace after the combine's own).
 static int combine_norm_up_impl(const moe_shape *s, int T, const float *Y, const int32_t *pair_pos,
@@ -286,36 +323,17 @@ int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_ro
               const float *bias, const uint16_t *w_down, int32_t *topk_ids, float *topk_w, float *z,
               float *gap, void *ws, size_t ws_bytes, void *stream) {
   return guarded([&]() -> int {
-    int rc = check_shape(s);
-    if (rc) return rc;
-    if (T <= 0 || !x || !ws) return MOE_EINVAL;
-    if ((w_down == nullptr) != (z == nullptr)) return MOE_EINVAL;
-    // routing needs the router, bias and both outputs; without a router only z is computed
-    const bool routing = w_router != nullptr;
-    if (routing && (!bias || !topk_ids || !topk_w)) return MOE_EINVAL;
-    if (!routing && (bias || topk_ids || topk_w || gap || !z)) return MOE_EINVAL;
-    if ((routing && !aligned16(w_router)) || (w_down && !aligned16(w_down)) || !aligned16(x) ||
-        (z && !aligned16(z)) || !aligned16(ws))
-      return MOE_EINVAL;
-    const RouteWs w = route_ws(s, T);
-    if (ws_bytes < w.total) return MOE_EWORKSPACE;
-    if ((rc = check_device())) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    float *logits = reinterpret_cast<float *>(wsp(ws, w.logits));
-    float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
-    if (routing) {
-      GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
-                              s->n_experts, 0, T, partial, s);
-      if (run_dense(w.pr, A_BF16, false, a, nullptr, st) != hipSuccess) return MOE_EHIP;
-      if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, st) != hipSuccess)
-        return MOE_EHIP;
-    }
-    if (z) {
-      GemmArgs d = dense_args(w.pd, x, s->hidden, w_down, nullptr, s->latent, s->hidden, z,
-                              s->latent, 0, T, partial, s);
-      if (run_dense(w.pd, A_BF16, false, d, nullptr, st) != hipSuccess) return MOE_EHIP;
-    }
-    return MOE_OK;
+    return route_impl(s, T, x, w_router, bias, w_down, nullptr, 0, topk_ids, topk_w, z, gap, ws, ws_bytes, stream);
+  });
+}
+
+int moe_route_capped(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_router, const float *bias,
+                     const uint16_t *w_down, const uint8_t *promoted, int k_hi, int32_t *topk_ids, float *topk_w,
+                     float *z, float *gap, void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    if (!promoted || !w_router || k_hi < 0) return MOE_EINVAL;
+    return route_impl(s, T, x, w_router, bias, w_down, promoted, k_hi, topk_ids, topk_w, z, gap, ws, ws_bytes,
+                      stream);
   });
 }
 

@@ -6,6 +6,12 @@
 // scores divided by their sum.  Order: larger biased score first, then the
 // lower expert index (NaN ranks last).  Output slots hold the selected ids in
 // ascending order.
+//
+// Capped promotion (Kimi-K3-Alis-MLX-Dynamic card, Build recipe: the serving
+// configuration keeps at most moe_k_hi promoted MXFP4 experts per token and
+// drops the contribution of the later ones): with a promoted mask given, a
+// selected promoted expert that has k_hi selected promoted experts ahead of
+// it in routing order gets weight 0.
 #include <math.h>
 
 #include "common.h"
@@ -42,9 +48,11 @@ MOE_DEV int lanes_below(uint64_t m) {
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
-                                                   float *__restrict__ w, float *__restrict__ gap) {
+                                                   float *__restrict__ w, float *__restrict__ gap,
+                                                   const uint8_t *__restrict__ promoted, int k_hi) {
   __shared__ int sel_lds[4][32];
   __shared__ float s_lds[4][32];
+  __shared__ uint32_t key_lds[4][32];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -102,6 +110,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
       const int q = pos + lanes_below(m);
       sel_lds[wave][q] = lane + 64 * i;
       s_lds[wave][q] = sg[i];
+      key_lds[wave][q] = key[i];
     }
     pos += __popcll(m);
   }
@@ -110,8 +119,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   float sum = 0.f;
   for (int q = 0; q < k; ++q) sum += s_lds[wave][q];
   if (lane < k) {
-    ids[(long long)t * k + lane] = sel_lds[wave][lane];
-    w[(long long)t * k + lane] = s_lds[wave][lane] / sum;
+    const int id = sel_lds[wave][lane];
+    float wt = s_lds[wave][lane] / sum;
+    if (promoted != nullptr && promoted[id]) {
+      // capped promotion: a promoted expert with k_hi selected promoted experts
+      // ahead of it in routing order (larger key, or equal key and lower id)
+      // has its contribution dropped; the other weights stay as they are
+      const uint32_t my = key_lds[wave][lane];
+      int ahead = 0;
+      for (int q = 0; q < k; ++q) {
+        const int o = sel_lds[wave][q];
+        const uint32_t ok = key_lds[wave][q];
+        ahead += (promoted[o] && (ok > my || (ok == my && o < id))) ? 1 : 0;
+      }
+      if (ahead >= k_hi) wt = 0.f;
+    }
+    ids[(long long)t * k + lane] = id;
+    w[(long long)t * k + lane] = wt;
   }
   if (lane == 0 && gap != nullptr) gap[t] = (k < E) ? key_value(th) - key_value(kp1) : INFINITY;
 }
@@ -119,9 +143,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 }  // namespace
 
 hipError_t launch_topk(const float *logits, const float *bias, int T, int E, int k, int32_t *ids,
-                       float *w, float *gap, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, T, E, k, ids, w,
-                     gap);
+                       float *w, float *gap, const uint8_t *promoted, int k_hi, hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, T, E, k, ids, w, gap,
+                     promoted, k_hi);
   return hipGetLastError();
 }
 

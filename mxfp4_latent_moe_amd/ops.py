@@ -1,5 +1,5 @@
-"""Torch-facing wrappers of the C-ABI calls (the five of the layer, the REAP
-saliency and the combine with REAP fused in), and a layer object that chains the layer's calls on one stream.  Argument marshalling only: tensors are passed as
+"""Torch-facing wrappers of the C-ABI calls (the five of the layer, the capped
+routing, the REAP saliency and the combine with REAP fused in), and a layer object that chains the layer's calls on one stream.  Argument marshalling only: tensors are passed as
 device pointers, the stream as its HIP handle; all compute runs in the HIP
 library."""
 from __future__ import annotations
@@ -35,6 +35,14 @@ def route(shape, x, w_router, bias, w_down, topk_ids, topk_w, z, gap, ws, stream
     check("moe_route", load().moe_route(shape, x.shape[0], _p(x), _p(w_router), _p(bias), _p(w_down),
                                         _p(topk_ids), _p(topk_w), _p(z), _p(gap), _p(ws), ws.numel(),
                                         _s(stream)))
+
+
+def route_capped(shape, x, w_router, bias, w_down, promoted, k_hi, topk_ids, topk_w, z, gap, ws, stream=None):
+    """moe_route with the moe_k_hi cap: promoted experts past the first k_hi of a token get weight 0."""
+    check("moe_route_capped",
+          load().moe_route_capped(shape, x.shape[0], _p(x), _p(w_router), _p(bias), _p(w_down), _p(promoted),
+                                  int(k_hi), _p(topk_ids), _p(topk_w), _p(z), _p(gap), _p(ws), ws.numel(),
+                                  _s(stream)))
 
 
 def permute(shape, topk_ids, offsets, sorted_pair, pair_pos, active, ws, stream=None):

@@ -207,3 +207,18 @@ def test_combine_reap_validation(lib):
     a = list(args)
     a[13] = lib.moe_workspace_bytes(wide, _lib.MOE_FN_COMBINE_NORM_UP_REAP, T)
     assert lib.moe_combine_norm_up_reap(wide, *a) == _lib.MOE_ENOTSUP
+
+
+def test_route_capped_validation(lib):
+    s = _shape()
+    T = 16
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_ROUTE, T)
+    # T, x, w_router, bias, w_down, promoted, k_hi, ids, w, z, gap, ws, bytes, stream
+    args = [T, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    for i, v in ((5, None), (2, None), (6, -1), (0, 0), (3, None)):  # promoted, router, k_hi, T, bias
+        a = list(args)
+        a[i] = v
+        assert lib.moe_route_capped(s, *a) == _lib.MOE_EINVAL, i
+    a = list(args)
+    a[12] = ws - 1
+    assert lib.moe_route_capped(s, *a) == _lib.MOE_EWORKSPACE
