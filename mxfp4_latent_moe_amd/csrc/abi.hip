@@ -239,9 +239,11 @@ static int route_impl(const moe_shape *s, int T, const uint16_t *x, const uint16
   if (routing) {
     GemmArgs a = dense_args(w.pr, x, s->hidden, w_router, nullptr, s->n_experts, s->hidden, logits,
                             s->n_experts, 0, T, partial, s);
-    if (run_dense(w.pr, A_BF16, false, a, nullptr, st) != hipSuccess) return MOE_EHIP;
-    if (launch_topk(logits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, promoted, k_hi, st) !=
-        hipSuccess)
+    // no finalize pass: the top-k kernel adds the split-K partials itself
+    if (launch_gemm(w.pr, W_BF16, A_BF16, false, a, st) != hipSuccess) return MOE_EHIP;
+    const float *part = w.pr.splits > 1 ? partial : nullptr;
+    if (launch_topk(logits, part, w.pr.splits, bias, T, s->n_experts, s->top_k, topk_ids, topk_w, gap, promoted,
+                    k_hi, st) != hipSuccess)
       return MOE_EHIP;
   }
   if (z) {

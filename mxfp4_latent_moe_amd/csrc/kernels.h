@@ -121,9 +121,11 @@ hipError_t launch_finalize(const FinalizeArgs &f, hipStream_t st);
 hipError_t launch_plan_chunks(const int32_t *offsets, int E, int chunk_rows, int32_t *chunks,
                               int32_t *count, hipStream_t st);
 
-// promoted == nullptr: no cap
-hipError_t launch_topk(const float *logits, const float *bias, int T, int E, int k, int32_t *ids,
-                       float *w, float *gap, const uint8_t *promoted, int k_hi, hipStream_t st);
+// partial != nullptr: logits are the sum of `splits` split-K partials [splits][T][E]
+// (logits unused); promoted == nullptr: no cap
+hipError_t launch_topk(const float *logits, const float *partial, int splits, const float *bias, int T, int E,
+                       int k, int32_t *ids, float *w, float *gap, const uint8_t *promoted, int k_hi,
+                       hipStream_t st);
 
 // permutation: workspace holds blk_counts [nblk][E] int32
 int permute_blocks(int T);

@@ -46,6 +46,7 @@ MOE_DEV int lanes_below(uint64_t m) {
 // walking the slots in order with a per-slot prefix count resolves the ties
 // and also emits the selected ids in ascending order.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
+                                                   const float *__restrict__ partial, int splits,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
                                                    float *__restrict__ w, float *__restrict__ gap,
@@ -59,6 +60,38 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const bool live = t < T;
   const float *lr = logits + (long long)(live ? t : 0) * E;
 
+  // logits: read, or summed here from the router's split-K partials in split
+  // order from zero (the same additions a separate finalize pass makes)
+  float lg[SLOTS];
+  if (partial != nullptr) {
+    const float *pt = partial + (long long)(live ? t : 0) * E;
+    const long long sstride = (long long)T * E;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) lg[i] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float v[4][SLOTS];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+          const int e = lane + 64 * i;
+          v[u][i] = (s0 + u < splits && e < E) ? pt[(s0 + u) * sstride + e] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (s0 + u < splits) {
+#pragma unroll
+          for (int i = 0; i < SLOTS; ++i) lg[i] += v[u][i];
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int e = lane + 64 * i;
+      lg[i] = e < E ? lr[e] : 0.f;
+    }
+  }
+
   uint32_t key[SLOTS];  // 0 for slots past E: below every real expert
   float sg[SLOTS];
 #pragma unroll
@@ -67,7 +100,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     key[i] = 0u;
     sg[i] = 0.f;
     if (e < E) {
-      sg[i] = sigmoid(lr[e]);
+      sg[i] = sigmoid(lg[i]);
       float b = sg[i] + bias[e];
       if (b != b) b = -INFINITY;
       key[i] = order_key(b);
@@ -142,10 +175,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 
 }  // namespace
 
-hipError_t launch_topk(const float *logits, const float *bias, int T, int E, int k, int32_t *ids,
-                       float *w, float *gap, const uint8_t *promoted, int k_hi, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, T, E, k, ids, w, gap,
-                     promoted, k_hi);
+hipError_t launch_topk(const float *logits, const float *partial, int splits, const float *bias, int T, int E,
+                       int k, int32_t *ids, float *w, float *gap, const uint8_t *promoted, int k_hi,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, partial, splits, bias, T, E, k,
+                     ids, w, gap, promoted, k_hi);
   return hipGetLastError();
 }
 
