@@ -122,12 +122,14 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
                                                           int32_t *__restrict__ active) {
   __shared__ int cur[1024];
   __shared__ int wave_tot[16];
+  __shared__ int ids_lds[TB * 32];  // the block's ids, so the in-order scatter reads LDS only
   const int e = threadIdx.x;
   if (e < E) cur[e] = 0;
   __syncthreads();
   const int P = T * k;
   for (int i = threadIdx.x; i < P; i += 1024) {
     const int x = ids[i];
+    ids_lds[i] = x;
     if ((unsigned)x < (unsigned)E) atomicAdd(&cur[x], 1);  // ids outside [0, E) are dropped
   }
   __syncthreads();
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
   for (int t = 0; t < T; ++t) {
     if (lane < k) {
       const int p = t * k + lane;
-      const int x = ids[p];
+      const int x = ids_lds[p];
       if ((unsigned)x >= (unsigned)E) continue;
       const int q = cur[x];
       cur[x] = q + 1;  // a token holds each expert at most once
