@@ -408,7 +408,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU expert parallelism "
-              "is not part of this build", file=sys.stderr)
+              "is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
