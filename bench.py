@@ -45,6 +45,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 (the fp4 x fp8 MX MFMA runs at this rate)
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense fp6 / fp4 (the fp4 x fp6 MX MFMA runs at this rate)
+PREFILL_STEPS = 10              # timed steps of each prefill line
 FLUSH_BYTES = 512 << 20         # > the 256 MB last-level (MALL) cache
 COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
 
@@ -125,10 +128,11 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, brea
     dom = []
     t0 = time.perf_counter()
     for i in range(steps):
-        moes[i % len(moes)].forward(x, marks=dom, mark_names=(DOMINANT,))
+        moes[i % len(moes)].forward(x, marks=dom, mark_names=(DOMINANT, "grouped_gemm_down"))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = [e0.elapsed_time(e1) for _, e0, e1 in dom]
+    dom_ms = [e0.elapsed_time(e1) for n, e0, e1 in dom if n == DOMINANT]
+    down_ms = [e0.elapsed_time(e1) for n, e0, e1 in dom if n != DOMINANT]
 
     # per-call breakdown (events around every call; a little slower than the timed loop)
     marks_all = []
@@ -146,7 +150,7 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, brea
     b = moes[0].buffers(wl.tokens)
     e_act = int(b["active"][0].item())
     r = {"wall_s": wall, "per_call_ms": per_call, "e_act": e_act, "T": wl.tokens,
-         "dominant_ms": float(np.mean(dom_ms)),
+         "dominant_ms": float(np.mean(dom_ms)), "down_ms": float(np.mean(down_ms)),
          "step_ms": {"median": _pct(spans, 50), "p10": _pct(spans, 10), "p90": _pct(spans, 90)}}
     if cold_steps > 0:
         # every step after a write of FLUSH_BYTES: nothing is left in the last-level cache
@@ -251,32 +255,43 @@ def summarize_pmc(fetch_dir, write_dir):
     print(f"traffic_bytes_per_launch: {traffic:.0f}")
 
 
-def cpu_baseline(synth, wl, n_tokens):
-    """The float64 oracle as it stands, on the first n_tokens tokens of the workload."""
+def cpu_baseline(synth, wl, n_tokens, bias=None):
+    """The float64 oracle as it stands, on the first n_tokens tokens of the workload.
+
+    Only the oracle's arithmetic is timed: the seeded fixtures (tokens, dense
+    weights and the raw checkpoint bytes of every expert the sample routes to)
+    are generated before the clock starts; dequantisation stays inside, as it
+    is part of the oracle's forward.  BLAS runs on every core this process may
+    use; the per-expert steps run one after another, as the oracle has them."""
     from oracle import layer
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
         cores = os.cpu_count() or 1
     x_bits = synth.gen_tokens(wl, n_tokens)
     d = synth.gen_dense(wl)
-    bias = synth.gen_bias(wl)
-
-    def fetch(e):
-        out = {}
+    bias = synth.gen_bias(wl) if bias is None else bias
+    ids = layer.route(x_bits, d["w_router"], bias, wl.shape.top_k)["ids"]
+    raw = {}
+    for e in sorted(set(ids.reshape(-1).tolist())):
+        raw[e] = {}
         for m in ("w1", "w3", "w2"):
-            p, s = synth.gen_expert(wl, e, m)
-            out[m + "_packed"], out[m + "_scale"] = p, s
-        return out
-
-    cache = layer.ExpertCache(fetch, max_items=4 * wl.shape.top_k)
+            raw[e][m + "_packed"], raw[e][m + "_scale"] = synth.gen_expert(wl, e, m)
+    cache = layer.ExpertCache(lambda e: raw[e], max_items=4 * wl.shape.top_k)
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:  # pragma: no cover
+        limit = None
     t0 = time.perf_counter()
     layer.layer_forward(x_bits, d, bias, cache, wl.shape)
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_tokens} of the {wl.tokens} tokens of the {wl.name} workload, float64 numpy "
-                      f"oracle (expert dequantisation included), {dt:.1f} s"}
+    if limit is not None:
+        limit.restore_original_limits()
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_tokens} of the {wl.tokens} tokens of the {wl.name} workload ({len(raw)} experts), "
+                      f"float64 numpy oracle, expert dequantisation included, fixtures generated beforehand; "
+                      f"BLAS on {cores} threads, the rest single-threaded; {dt:.1f} s"}
 
 
 def run_dense_ffn(mx, torch, synth):
@@ -380,6 +395,140 @@ def run_reap(mx, torch, synth):
             "ms": round(ms, 4), "bytes": nbytes, "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "fused_into_combine": {"combine_norm_up_ms": round(plain_ms, 4), "with_reap_ms": round(fused_ms, 4),
                                    "reap_extra_ms": round(fused_ms - plain_ms, 4)}}
+
+
+PEAK_OF_MODE = {"bf16x2": ("bf16", BF16_MFMA_PEAK_TFLOPS), "mx8x3": ("fp8", FP8_MFMA_PEAK_TFLOPS),
+                "mx6x3": ("fp6/fp4", FP4_MFMA_PEAK_TFLOPS)}
+# MFMA products executed per algorithmic product in each operand mode's expert
+# GEMMs (gate/up with z, down with H): hi + lo planes, or three MX terms
+EXEC_PER_ALG = {"bf16x2": 2, "mx8x3": 3, "mx6x3": 3}
+
+
+def _layer_flops(sh, T):
+    """Algorithmic FLOPs of one layer forward over T tokens: routed experts
+    (gate, up, down), router, latent down and up projections, shared experts."""
+    return 2.0 * T * (sh.top_k * 3 * sh.latent * sh.inter + sh.n_experts * sh.hidden
+                      + 2 * sh.latent * sh.hidden + 3 * sh.n_shared * sh.shared_inter * sh.hidden)
+
+
+def prefill_line(mx, torch, synth, layers, pf, mode, label):
+    """Prefill T=4096 in one operand mode: tokens/s, the layer's algorithmic
+    TFLOP/s against bf16 peak, and the expert GEMMs against the peak of the
+    MFMA type they run (bf16, or fp8 / fp6 for the MX modes), algorithmic and
+    executed (hi + lo planes or three MX terms)."""
+    sh = pf.shape
+    r = run_workload(mx, torch, synth, layers, pf, PREFILL_STEPS, 2, breakdown_steps=2, operand_mode=mode)
+    ms = 1e3 * r["wall_s"] / PREFILL_STEPS
+    P = pf.tokens * sh.top_k
+    gu_flops = 2.0 * P * sh.latent * sh.inter * 2
+    dn_flops = 2.0 * P * sh.inter * sh.latent
+    dt_name, dt_peak = PEAK_OF_MODE[label]
+    gu_tf = gu_flops / (r["dominant_ms"] * 1e-3) / 1e12
+    dn_tf = dn_flops / (r["down_ms"] * 1e-3) / 1e12
+    lt = _layer_flops(sh, pf.tokens) / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"prefill T={pf.tokens}, full K3 shapes, operand mode {label}",
+        "steps": PREFILL_STEPS,
+        "tokens_per_s": round(pf.tokens / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 3),
+        "layer_tflops_algorithmic": round(lt, 1),
+        "layer_mfma_frac_algorithmic": round(lt / BF16_MFMA_PEAK_TFLOPS, 4),
+        "gateup_ms": round(r["dominant_ms"], 4), "down_ms": round(r["down_ms"], 4),
+        "gateup_tflops": round(gu_tf, 1), "down_tflops": round(dn_tf, 1),
+        "expert_gemm_mfma_type": dt_name, "expert_gemm_type_peak_tflops": dt_peak,
+        "gateup_frac_of_type_peak": round(gu_tf / dt_peak, 4),
+        "gateup_frac_of_type_peak_executed": round(gu_tf * EXEC_PER_ALG[label] / dt_peak, 4),
+        "gateup_frac_of_bf16_peak": round(gu_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+        "per_call_ms": {k: round(v, 4) for k, v in r["per_call_ms"].items()},
+    }
+
+
+def run_batched_decode(mx, torch, synth, layers, steps):
+    """Batched decode T=256 with the Zipf-calibrated correction bias: tokens/s
+    and the grouped GEMMs' expert-weight bytes over their event-timed time."""
+    wl = synth.workload("batched_decode")
+    sh = wl.shape
+    bias = synth.gen_bias(wl, os.path.join(ROOT, "tests", "golden", "zipf_bias_T256.txt"))
+    bias_d = torch.from_numpy(bias).to("cuda:0")
+    zl = [dict(w, bias=bias_d) for w in layers]
+    r = run_workload(mx, torch, synth, zl, wl, steps, 5, breakdown_steps=5)
+    ms = 1e3 * r["wall_s"] / steps
+    eb = r["e_act"] * _expert_bytes(sh)
+    g_ms = r["dominant_ms"] + r["down_ms"]
+    gbs = eb / (g_ms * 1e-3) / 1e9
+    return {"workload": f"batched decode T={wl.tokens}, full K3 shapes, Zipf(1.1)-calibrated expert load",
+            "steps": steps, "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "active_experts": r["e_act"], "expert_weight_bytes": eb,
+            "grouped_gemm_ms": round(g_ms, 4), "gateup_ms": round(r["dominant_ms"], 4),
+            "down_ms": round(r["down_ms"], 4),
+            "expert_gb_per_s": round(gbs, 1), "expert_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "expert_hbm_frac_layer": round(eb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_call_ms": {k: round(v, 4) for k, v in r["per_call_ms"].items()}}
+
+
+def run_microbench(mx, torch, synth, w, steps=10):
+    """Isolated grouped GEMM: segments ~ Multinomial(65536, Zipf(1.1)) over the
+    896 experts, A = bf16 N(0, 1) rows already in expert order; gate/up +
+    SiTU-GLU then down, in the default and the MX fp6 operand modes."""
+    from synth.device import to_dev
+    from mxfp4_latent_moe_amd import _lib, ops
+    dev = torch.device("cuda:0")
+    wl = synth.workload("microbench")
+    sh = wl.shape
+    counts = synth.gen_microbench_counts(wl)
+    P = int(counts.sum())
+    offsets = np.zeros(sh.n_experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    A = torch.from_numpy(synth.gen_microbench_activations(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    off_d = to_dev(offsets, dev)
+    H = torch.empty((P, sh.inter), dtype=torch.float32, device=dev)
+    Y = torch.empty((P, sh.latent), dtype=torch.float32, device=dev)
+    gu_flops = 2.0 * P * sh.latent * sh.inter * 2
+    dn_flops = 2.0 * P * sh.inter * sh.latent
+    out = {"workload": f"isolated grouped GEMM, {P} rows over {sh.n_experts} experts (Multinomial(65536, "
+                       f"Zipf(1.1)) segments, largest {int(counts.max())}), A bf16 already permuted",
+           "steps": steps, "weight_bytes": sh.n_experts * _expert_bytes(sh)}
+    for label, mode in (("bf16x2", _lib.MOE_OPND_BF16X2), ("mx6x3", _lib.MOE_OPND_MX6X3)):
+        s = mx.shape_of(sh, mode)
+        ws = torch.empty(ops.workspace_bytes(s, _lib.MOE_FN_GROUPED_GEMM, P), dtype=torch.uint8, device=dev)
+
+        def gu():
+            ops.grouped_gemm(s, _lib.MOE_OP_GATEUP_SITU, P, off_d, None, A, w["w1_packed"], w["w1_scale"],
+                             w["w3_packed"], w["w3_scale"], None, H, ws)
+
+        def dn():
+            ops.grouped_gemm(s, _lib.MOE_OP_DOWN, P, off_d, None, H, w["w2_packed"], w["w2_scale"], None, None,
+                             None, Y, ws)
+        for _ in range(2):
+            gu()
+            dn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1, e2 in ev:
+            e0.record()
+            gu()
+            e1.record()
+            dn()
+            e2.record()
+        torch.cuda.synchronize()
+        gu_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        dn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        tf = (gu_flops + dn_flops) / ((gu_ms + dn_ms) * 1e-3) / 1e12
+        # gate/up takes the exact bf16 rows with one MFMA (or as MX terms); down takes H as hi + lo
+        dt_name, dt_peak = PEAK_OF_MODE[label]
+        out[label] = {"gateup_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
+                      "gateup_tflops": round(gu_flops / (gu_ms * 1e-3) / 1e12, 1),
+                      "down_tflops": round(dn_flops / (dn_ms * 1e-3) / 1e12, 1),
+                      "tflops": round(tf, 1), "mfma_frac_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                      "expert_gemm_mfma_type": dt_name, "frac_of_type_peak": round(tf / dt_peak, 4),
+                      "weight_gb_per_s": round(out["weight_bytes"] / ((gu_ms + dn_ms) * 1e-3) / 1e9, 1)}
+        if label == "bf16x2":
+            out["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                               "kernel": "mxfp4_grouped_gemm gate/up + down", "algorithmic_flops": gu_flops + dn_flops}
+        del ws
+    del A, H, Y
+    return out
 
 
 def main():
@@ -486,54 +635,16 @@ def main():
             r["e_act"] * _expert_bytes(sh) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
     if not args.no_secondary and args.workload == "decode":
+        print("bench: timing batched decode T=256 (Zipf load)", file=sys.stderr, flush=True)
+        line["secondary_batched_decode"] = run_batched_decode(mx, torch, synth, layers, args.steps)
         pf = synth.workload("prefill")
-        print("bench: timing prefill", file=sys.stderr, flush=True)
-        rp = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2, breakdown_steps=2)
-        pms = 1e3 * rp["wall_s"] / max(2, args.steps // 5)
-        layer_flops = 2.0 * pf.tokens * (sh.top_k * 3 * sh.latent * sh.inter + sh.n_experts * sh.hidden
-                                         + 2 * sh.latent * sh.hidden
-                                         + 3 * sh.n_shared * sh.shared_inter * sh.hidden)
-        gu = rp["dominant_ms"]
-        gu_flops = 2.0 * pf.tokens * sh.top_k * sh.latent * sh.inter * 2
-        line["secondary"] = {
-            "workload": "prefill T=4096, same shapes and weights",
-            "tokens_per_s": round(pf.tokens / (pms * 1e-3), 1),
-            "ms_per_step": round(pms, 3),
-            "layer_tflops_algorithmic": round(layer_flops / (pms * 1e-3) / 1e12, 1),
-            "layer_mfma_frac_algorithmic": round(layer_flops / (pms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-            "gateup_tflops": round(gu_flops / (gu * 1e-3) / 1e12, 1),
-            "per_call_ms": {k: round(v, 4) for k, v in rp["per_call_ms"].items()},
-        }
-        # the same prefill with the MX-scaled expert GEMMs (three fp8 activation terms)
-        print("bench: timing prefill, MX fp8 operand mode", file=sys.stderr, flush=True)
-        rm = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2, breakdown_steps=2,
-                          operand_mode=mx.MOE_OPND_MX8X3)
-        mms = 1e3 * rm["wall_s"] / max(2, args.steps // 5)
-        line["secondary_mx8x3"] = {
-            "workload": "prefill T=4096, expert GEMM activations as three e4m3 terms (operand mode MX8X3)",
-            "tokens_per_s": round(pf.tokens / (mms * 1e-3), 1),
-            "ms_per_step": round(mms, 3),
-            "layer_tflops_algorithmic": round(layer_flops / (mms * 1e-3) / 1e12, 1),
-            "layer_mfma_frac_algorithmic": round(layer_flops / (mms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-            "gateup_tflops": round(gu_flops / (rm["dominant_ms"] * 1e-3) / 1e12, 1),
-            "per_call_ms": {k: round(v, 4) for k, v in rm["per_call_ms"].items()},
-        }
-
-        # and with three fp6 (e2m3) activation terms, which the MX MFMA runs at the fp4 rate
-        print("bench: timing prefill, MX fp6 operand mode", file=sys.stderr, flush=True)
-        r6 = run_workload(mx, torch, synth, layers, pf, max(2, args.steps // 5), 2, breakdown_steps=2,
-                          operand_mode=mx.MOE_OPND_MX6X3)
-        m6 = 1e3 * r6["wall_s"] / max(2, args.steps // 5)
-        line["secondary_mx6x3"] = {
-            "workload": "prefill T=4096, expert GEMM activations as three e2m3 terms (operand mode MX6X3)",
-            "tokens_per_s": round(pf.tokens / (m6 * 1e-3), 1),
-            "ms_per_step": round(m6, 3),
-            "layer_tflops_algorithmic": round(layer_flops / (m6 * 1e-3) / 1e12, 1),
-            "layer_mfma_frac_algorithmic": round(layer_flops / (m6 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-            "gateup_tflops": round(gu_flops / (r6["dominant_ms"] * 1e-3) / 1e12, 1),
-            "per_call_ms": {k: round(v, 4) for k, v in r6["per_call_ms"].items()},
-        }
-
+        for key, mode, label in (("secondary", mx.MOE_OPND_BF16X2, "bf16x2"),
+                                 ("secondary_mx8x3", mx.MOE_OPND_MX8X3, "mx8x3"),
+                                 ("secondary_mx6x3", mx.MOE_OPND_MX6X3, "mx6x3")):
+            print(f"bench: timing prefill, operand mode {label}", file=sys.stderr, flush=True)
+            line[key] = prefill_line(mx, torch, synth, layers, pf, mode, label)
+        print("bench: timing the grouped-GEMM microbenchmark", file=sys.stderr, flush=True)
+        line["secondary_microbench"] = run_microbench(mx, torch, synth, layers[0])
         print("bench: timing the layer-0 dense FFN", file=sys.stderr, flush=True)
         line["secondary_dense_ffn"] = run_dense_ffn(mx, torch, synth)
         print("bench: timing the REAP saliency pass", file=sys.stderr, flush=True)
@@ -544,6 +655,8 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(synth, wl, 8 if args.workload == "decode" else 4)
+        if "secondary" in line:
+            line["secondary"]["cpu_baseline"] = cpu_baseline(synth, synth.workload("prefill"), 4)
     print(json.dumps(line), flush=True)
 
 

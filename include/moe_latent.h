@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* return codes */
 #define MOE_OK 0
@@ -174,26 +174,39 @@ int moe_permute(const moe_shape *shape, int T, const int32_t *topk_ids, int32_t 
  * Weight tensors are the checkpoint bytes as-is, stacked over experts:
  * packed [E, N, K/2] (byte b of a row holds element 2b in its low nibble),
  * scale [E, N, K/32] (element k of row n is code * 2^(scale[n][k/32]-127)).
+ * e8m0 range: for scale bytes 2..252 every weight is exact in the kernels
+ * (bf16 and MX paths alike), as the OCP MX definition gives it.  Outside that
+ * range the result is unspecified but the call stays memory-safe: bytes 0 and
+ * 1 give values below 2^-126 that the bf16 path may flush to zero, bytes 253
+ * and 254 overflow bf16 for the largest codes in the bf16 path, and 255 (NaN
+ * in OCP MX) gives non-finite outputs for the rows that use it.
  *   op = MOE_OP_GATEUP_SITU: H[p] = SiTU-GLU(A_p w1_e^T, A_p w3_e^T) for every
  *        sorted row p of expert e; K = latent, N = inter.
  *        w_packed/w_scale = w1 (gate), w3_packed/w3_scale = w3 (up).
  *        A row of sorted row p: A[sorted_pair[p] / top_k] when sorted_pair is
- *        given (A = z [T, L]), else A[p] (A already permuted, [P, L]).
- *        C = H [P, inter] fp32.
+ *        given (A = z [a_rows, L], gathered), else A[p] (A already permuted,
+ *        [a_rows >= P, L]).  C = H [P, inter] fp32.
  *   op = MOE_OP_DOWN: Y[p] = A[p] w2_e^T; K = inter, N = latent.
- *        A = H [P, inter] fp32 in sorted order; w3_* must be NULL.
+ *        A = H [a_rows >= P, inter] fp32 in sorted order; w3_* must be NULL.
  *        pair_weight [T*k] fp32 (optional, needs sorted_pair): row p is
  *        scaled by pair_weight[sorted_pair[p]].  C = Y [P, latent] fp32.
- *   P              number of sorted rows (T*k)
- *   expert_offsets [E+1] device int32 from moe_permute
+ *   P              number of sorted rows (T*k, or an expert slice's rows)
+ *   expert_offsets [E+1] device int32 from moe_permute (or a slice of it
+ *                  rebased to 0)
+ *   a_rows         rows of A.  Gathered A (gate/up with sorted_pair): every
+ *                  sorted_pair[p] / top_k must be below a_rows (a device
+ *                  precondition), which holds for a call over an expert slice
+ *                  with the full token count T; a_rows * K * (4 for fp32, 2 for
+ *                  bf16) must stay below 2^31.  Otherwise a_rows >= P.
  *   a_dtype        MOE_DT_F32 (split or rounded per shape->operand_mode) or
  *                  MOE_DT_BF16 (exact, single MFMA)
  * Experts with no rows cost nothing and nothing waits on the host: the grid
  * is sized from P and each workgroup reads its work item on the device.
- * Errors: MOE_EINVAL for bad op/dtype, P < 1, null required pointers, or
- * w3 given for MOE_OP_DOWN. */
+ * Errors: MOE_EINVAL for bad op/dtype, P < 1, a_rows < 1 (or below P when A
+ * is not gathered), null required pointers, or w3 given for MOE_OP_DOWN;
+ * MOE_ENOTSUP for a gathered A of 2^31 bytes or more. */
 int mxfp4_grouped_gemm(const moe_shape *shape, int op, int P, const int32_t *expert_offsets,
-                       const int32_t *sorted_pair, const void *A, int a_dtype,
+                       const int32_t *sorted_pair, const void *A, int a_rows, int a_dtype,
                        const uint8_t *w_packed, const uint8_t *w_scale, const uint8_t *w3_packed,
                        const uint8_t *w3_scale, const float *pair_weight, float *C, void *ws,
                        size_t ws_bytes, void *stream);

@@ -64,7 +64,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.moe_permute.restype = i32
     lib.moe_permute.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mxfp4_grouped_gemm.restype = i32
-    lib.mxfp4_grouped_gemm.argtypes = [sp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mxfp4_grouped_gemm.argtypes = [sp, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine_norm_up.restype = i32
     lib.moe_combine_norm_up.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.shared_expert_ffn.restype = i32

@@ -73,10 +73,10 @@ size_t permute_ws(const moe_shape *s, int T) {
 }
 
 // MX activation terms (fp8 or fp6) are used for fp32 activations on the tiled
-// path, while 3 term planes of P rows stay addressable with 32-bit offsets
-bool use_mx8(const moe_shape *s, const GemmPlan &pl, int P, int K) {
+// path, while 3 term planes of `rows` rows stay addressable with 32-bit offsets
+bool use_mx8(const moe_shape *s, const GemmPlan &pl, long long rows, int K) {
   return (s->operand_mode == MOE_OPND_MX8X3 || s->operand_mode == MOE_OPND_MX6X3) && pl.variant == 3 &&
-         3LL * P * K < (1LL << 32) - 256;
+         3LL * rows * K < (1LL << 32) - 256;
 }
 
 struct GroupedWs {
@@ -92,7 +92,8 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
   w.count = align_up((size_t)w.plan.max_chunks * 16);
   w.partial = w.count + ALIGN;
   w.mx = w.partial + align_up(w.plan.partial_bytes);
-  // activation rows are at most P (T = P / k rows when they are gathered by sorted_pair)
+  // the MX term planes hold at most P rows (gathered activations with more
+  // rows than P are split per sorted row)
   w.total = w.mx + (use_mx8(s, w.plan, P, K) ? align_up(mx8_split_bytes(P, K)) : 0);
   return w;
 }
@@ -359,7 +360,7 @@ int moe_permute(const moe_shape *s, int T, const int32_t *topk_ids, int32_t *exp
 }
 
 int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_offsets,
-                       const int32_t *sorted_pair, const void *A, int a_dtype,
+                       const int32_t *sorted_pair, const void *A, int a_rows, int a_dtype,
                        const uint8_t *w_packed, const uint8_t *w_scale, const uint8_t *w3_packed,
                        const uint8_t *w3_scale, const float *pair_weight, float *C, void *ws,
                        size_t ws_bytes, void *stream) {
@@ -370,6 +371,12 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     if (a_dtype != MOE_DT_F32 && a_dtype != MOE_DT_BF16) return MOE_EINVAL;
     if (P <= 0 || !expert_offsets || !A || !w_packed || !w_scale || !C || !ws) return MOE_EINVAL;
     const bool gateup = op == MOE_OP_GATEUP_SITU;
+    // gate/up with sorted_pair gathers rows of A (z [T, L]); otherwise A holds the P sorted rows
+    const bool gathered = gateup && sorted_pair != nullptr;
+    if (a_rows < 1 || (!gathered && a_rows < P)) return MOE_EINVAL;
+    if (gathered && (long long)a_rows * (gateup ? s->latent : s->inter) * (a_dtype == MOE_DT_BF16 ? 2 : 4) >=
+                        (1LL << 31))
+      return MOE_ENOTSUP;
     if (gateup && (!w3_packed || !w3_scale)) return MOE_EINVAL;
     if (!gateup && (w3_packed || w3_scale)) return MOE_EINVAL;
     if (gateup && pair_weight) return MOE_EINVAL;
@@ -392,8 +399,9 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     GemmArgs a{};
     a.A = A;
     a.lda = K;
-    a.a_map = gateup ? sorted_pair : nullptr;
+    a.a_map = gathered ? sorted_pair : nullptr;
     a.a_div = s->top_k;
+    a.a_rows = a_rows;
     a.W0 = w_packed;
     a.W1 = w3_packed;
     a.S0 = w_scale;
@@ -419,16 +427,22 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     a.beta_lin = s->beta_lin;
     int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
     if (a_dtype == MOE_DT_F32 && use_mx8(s, w.plan, P, K)) {
-      // split the fp32 activation rows into three MX terms, then the MX-scaled GEMM
-      // gate/up gathers rows of z [P / k, K] through sorted_pair; down reads H [P, K] in order
-      const long long rows = (gateup && sorted_pair) ? (long long)(P / s->top_k) : (long long)P;
+      // split the fp32 activation rows into three MX terms, then the MX-scaled GEMM.
+      // Gathered rows of z [a_rows, K]: the split covers z's rows and the GEMM gathers
+      // them through sorted_pair, or, when z has more rows than the call has pairs (an
+      // expert slice), the split gathers row p = z[sorted_pair[p] / k] and the GEMM
+      // reads the P split rows in order.  Down reads H [P, K] in order.
+      const bool split_gathers = gathered && a_rows > P;
+      const long long rows = (gathered && !split_gathers) ? (long long)a_rows : (long long)P;
       uint8_t *mx = reinterpret_cast<uint8_t *>(wsp(ws, w.mx));
       const bool fp6 = s->operand_mode == MOE_OPND_MX6X3;
-      if (launch_mx_split(fp6, static_cast<const float *>(A), K, (int)rows, K, mx, st) != hipSuccess)
+      if (launch_mx_split(fp6, static_cast<const float *>(A), K, (int)rows, K, split_gathers ? sorted_pair : nullptr,
+                          s->top_k, mx, st) != hipSuccess)
         return MOE_EHIP;
       a.mxq = mx;
       a.mxs = mx + (size_t)rows * K * 3;
       a.mx_rows = rows;
+      if (split_gathers) a.a_map = nullptr;
       afmt = fp6 ? A_MX6X3 : A_MX8X3;
     }
     GemmPlan pl = w.plan;

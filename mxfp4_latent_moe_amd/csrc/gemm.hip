@@ -444,20 +444,14 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
     p.mt = stream_rows_per_wg(W_MXFP4, pair) / 64;
     p.n_blocks = ceil_div(N, stream_rows_per_wg(W_MXFP4, pair));
     p.splits = ceil_div(ksteps, STREAM_GROUPED_KSMAX);
-  } else if ((long long)P * K * 4 < (1LL << 31)) {
-    // activation offsets fit the 32-bit buffer addressing of the prefill kernel
+  } else {
+    // the prefill kernel addresses sorted rows from each chunk's first row, so
+    // any P fits its 32-bit buffer offsets (gathered rows are bounded at the ABI)
     p.variant = 3;
     p.nt = PREFILL_NT;
     p.chunk_rows = 16 * PREFILL_NT;
     p.mt = prefill_rows_per_wg(pair) / 64;
     p.n_blocks = ceil_div(N, prefill_rows_per_wg(pair));
-    p.splits = 1;
-  } else {
-    p.variant = 0;
-    p.nt = 8;
-    p.mt = 2;
-    p.chunk_rows = 128;
-    p.n_blocks = ceil_div(N, 64 * p.mt);
     p.splits = 1;
   }
   p.max_chunks = P / p.chunk_rows + (E < P ? E : P);
@@ -477,7 +471,9 @@ hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const 
     return launch_dense_tile(afmt == A_F32_SPLIT ? 2 : 1, pair, a, st);
   }
   if (pl.variant == 1) return launch_stream_gemm(wfmt, afmt, pair, a, grid, st);
-  if (wfmt == W_MXFP4) return launch_af<W_MXFP4>(pl, afmt, pair, a, grid, st);
+  // the tiled variant 0 serves the mid-size dense products only (grouped
+  // MXFP4 segments run on the stream, persistent or prefill kernels)
+  if (wfmt == W_MXFP4) return hipErrorInvalidValue;
   return launch_af<W_BF16>(pl, afmt, pair, a, grid, st);
 }
 

@@ -19,6 +19,7 @@ struct GemmArgs {
   long long lda;          // elements per activation row
   const int32_t *a_map;   // chunk row p reads A row a_map[p] / a_div (NULL: row p)
   int a_div;
+  long long a_rows;       // rows of A (grouped calls; gathered reads stay below it)
   const void *W0, *W1;    // weights [E][N][K] bf16 or packed [E][N][K/2]; W1 for SiTU pairs
   const uint8_t *S0, *S1; // e8m0 scales [E][N][K/32] (MXFP4)
   long long w_estride;    // per-expert stride of W (elements for bf16, bytes for packed)
@@ -105,8 +106,9 @@ int prefill_mx_rows_per_wg(bool pair);
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st);
 size_t mx8_split_bytes(long long rows, int K);
-hipError_t launch_mx_split(bool fp6, const float *A, long long lda, int rows, int K, uint8_t *ws,
-                           hipStream_t st);
+// map != nullptr: term row r is activation row map[r] / div
+hipError_t launch_mx_split(bool fp6, const float *A, long long lda, int rows, int K, const int32_t *map, int div,
+                           uint8_t *ws, hipStream_t st);
 hipError_t launch_stream_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                               hipStream_t st);
 int dense_tile_cols(bool pair);

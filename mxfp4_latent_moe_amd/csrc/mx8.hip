@@ -11,7 +11,9 @@
 // significant bits, so three terms leave a residual near 2^-12 of the block
 // maximum.
 //
-// Layout (ws): q [3][rows][K] bytes, then scales [3][rows][K/32] bytes.
+// Layout (ws): q [3][rows][K] bytes, then scales [3][rows][K/32] bytes.  Row r
+// of the planes is row r of the activations, or row map[r] / div of them when
+// a gather map is given.
 //
 // fp6: the same three-term recursion with e2m3 (OCP MX) codes: 1 sign, 2
 // exponent (bias 1) and 3 mantissa bits, magnitudes m/8 for exponent 0 and
@@ -48,14 +50,15 @@ MOE_DEV int block_exp(float amax) {
 
 // One thread per (row, block of 32): 128 bytes in, 3 x 32 bytes + 3 scale bytes out.
 __global__ __launch_bounds__(256) void mx8_split_kernel(const float *__restrict__ A, long long lda, int rows,
-                                                        int K, uint8_t *__restrict__ q,
-                                                        uint8_t *__restrict__ sc) {
+                                                        int K, const int32_t *__restrict__ map, int div,
+                                                        uint8_t *__restrict__ q, uint8_t *__restrict__ sc) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const int nb = K / 32;
   if (i >= (long long)rows * nb) return;
   const long long row = i / nb;
   const int blk = (int)(i - row * nb);
-  const f32x4_t *src = reinterpret_cast<const f32x4_t *>(A + row * lda + blk * 32);
+  const long long arow = map ? (long long)(map[row] / div) : row;
+  const f32x4_t *src = reinterpret_cast<const f32x4_t *>(A + arow * lda + blk * 32);
   float a[32];
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
@@ -119,14 +122,15 @@ MOE_DEV uint32_t to_e2m3(float v, float &q) {
 
 // One thread per (row, block of 32): 128 bytes in, 3 x 32 bytes + 3 scale bytes out.
 __global__ __launch_bounds__(256) void mx6_split_kernel(const float *__restrict__ A, long long lda, int rows,
-                                                        int K, uint8_t *__restrict__ q,
-                                                        uint8_t *__restrict__ sc) {
+                                                        int K, const int32_t *__restrict__ map, int div,
+                                                        uint8_t *__restrict__ q, uint8_t *__restrict__ sc) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const int nb = K / 32;
   if (i >= (long long)rows * nb) return;
   const long long row = i / nb;
   const int blk = (int)(i - row * nb);
-  const f32x4_t *src = reinterpret_cast<const f32x4_t *>(A + row * lda + blk * 32);
+  const long long arow = map ? (long long)(map[row] / div) : row;
+  const f32x4_t *src = reinterpret_cast<const f32x4_t *>(A + arow * lda + blk * 32);
   float a[32];
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
@@ -166,17 +170,17 @@ __global__ __launch_bounds__(256) void mx6_split_kernel(const float *__restrict_
 
 size_t mx8_split_bytes(long long rows, int K) { return (size_t)rows * K * 3 + (size_t)rows * (K / 32) * 3; }
 
-hipError_t launch_mx_split(bool fp6, const float *A, long long lda, int rows, int K, uint8_t *ws,
-                           hipStream_t st) {
+hipError_t launch_mx_split(bool fp6, const float *A, long long lda, int rows, int K, const int32_t *map, int div,
+                           uint8_t *ws, hipStream_t st) {
   const long long n = (long long)rows * (K / 32);
   uint8_t *q = ws;
   uint8_t *sc = ws + (size_t)rows * K * 3;
   if (fp6)
-    hipLaunchKernelGGL(mx6_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, lda, rows, K, q,
-                       sc);
+    hipLaunchKernelGGL(mx6_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, lda, rows, K, map,
+                       div, q, sc);
   else
-    hipLaunchKernelGGL(mx8_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, lda, rows, K, q,
-                       sc);
+    hipLaunchKernelGGL(mx8_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, A, lda, rows, K, map,
+                       div, q, sc);
   return hipGetLastError();
 }
 

@@ -73,17 +73,22 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   }
 
   // ---- activation rows this thread stages: token (tid >> 4) + RPP i, octet tid & 15
+  // Gathered rows index A from its start (the boundary keeps A below 2^31
+  // bytes then); rows in sorted order are addressed from the chunk's first
+  // row, so the number of sorted rows is not limited by 32-bit offsets.
   const int a_oct = tid & 15;
   const int esz = (AF == A_BF16) ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.A, 0x7FFFFFF0u);
+  const char *abase = static_cast<const char *>(g.A) + (g.a_map ? 0LL : (long long)row0 * g.lda * esz);
+  const long long abytes = (g.a_map ? g.a_rows : (long long)nrows) * g.lda * esz;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(abase, (uint32_t)min(abytes, 0x7FFFFFF0LL));
   uint32_t aoff[NPASS];
   bool alive[NPASS];
 #pragma unroll
   for (int i = 0; i < NPASS; ++i) {
     const int r = (tid >> 4) + RPP * i;
     alive[i] = r < nrows;
-    const int p = row0 + min(r, nrows - 1);
-    const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
+    const int rr = min(r, nrows - 1);
+    const long long arow = g.a_map ? (long long)(g.a_map[row0 + rr] / g.a_div) : (long long)rr;
     aoff[i] = (uint32_t)((arow * g.lda + a_oct * 8) * esz);
   }
 

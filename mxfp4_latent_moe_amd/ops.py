@@ -53,9 +53,10 @@ def permute(shape, topk_ids, offsets, sorted_pair, pair_pos, active, ws, stream=
 
 def grouped_gemm(shape, op, P, offsets, sorted_pair, A, w_packed, w_scale, w3_packed, w3_scale,
                  pair_weight, C, ws, stream=None):
+    """mxfp4_grouped_gemm; a_rows is A's row count."""
     a_dtype = MOE_DT_BF16 if A.dtype in (torch.bfloat16, torch.int16, torch.uint16) else MOE_DT_F32
     check("mxfp4_grouped_gemm",
-          load().mxfp4_grouped_gemm(shape, op, P, _p(offsets), _p(sorted_pair), _p(A), a_dtype,
+          load().mxfp4_grouped_gemm(shape, op, P, _p(offsets), _p(sorted_pair), _p(A), A.shape[0], a_dtype,
                                     _p(w_packed), _p(w_scale), _p(w3_packed), _p(w3_scale),
                                     _p(pair_weight), _p(C), _p(ws), ws.numel(), _s(stream)))
 

@@ -166,33 +166,43 @@ class ExpertCache:
 
 
 def routed_experts(z: np.ndarray, ids: np.ndarray, get_expert, n_experts: int,
-                   beta: float = BETA, beta_lin: float = BETA_LIN, keep: bool = False) -> dict:
+                   beta: float = BETA, beta_lin: float = BETA_LIN, keep: bool = False, map_fn=map) -> dict:
     """Expert outputs for every pair, laid out in expert-sorted order.
 
     Returns Y_pair [T, k, L] (un-weighted expert output of each pair) and,
-    with keep=True, H_sorted / Y_sorted in sorted-pair order plus the
-    permutation.
+    with keep=True, H_sorted / Y_sorted in sorted-pair order, H_pair
+    [T, k, I] in pair order, plus the permutation.  The experts are
+    independent; map_fn (default: the builtin map) applies the per-expert
+    step to the active experts, so a caller may hand it a thread pool's map
+    without changing any arithmetic.
     """
     T, k = ids.shape
     perm = permute(ids, n_experts)
     L = z.shape[1]
     Y_pair = np.zeros((T * k, L))
-    H_sorted = None
+    H_sorted = H_pair = None
     Y_sorted = np.zeros((T * k, L)) if keep else None
     offs, sp = perm["offsets"], perm["sorted_pair"]
-    for e in perm["active"]:
+
+    def one_expert(e):
         rows = sp[offs[e]:offs[e + 1]]
         H, Y = expert_mlp(z[rows // k], get_expert(e), beta, beta_lin)
+        return e, rows, H, Y
+
+    for e, rows, H, Y in map_fn(one_expert, perm["active"]):
         Y_pair[rows] = Y
         if keep:
             if H_sorted is None:
                 H_sorted = np.zeros((T * k, H.shape[1]))
+                H_pair = np.zeros((T * k, H.shape[1]))
             H_sorted[offs[e]:offs[e + 1]] = H
+            H_pair[rows] = H
             Y_sorted[offs[e]:offs[e + 1]] = Y
     out = {"Y_pair": Y_pair.reshape(T, k, L), "perm": perm}
     if keep:
         out["H_sorted"] = H_sorted
         out["Y_sorted"] = Y_sorted
+        out["H_pair"] = H_pair.reshape(T, k, -1)
     return out
 
 
@@ -227,17 +237,18 @@ def shared_experts(x_bits, sh_gate_bits, sh_up_bits, sh_down_bits, n_shared: int
 
 
 def layer_forward(x_bits, dense: dict, bias, get_expert, shape, eps: float = RMS_EPS,
-                  beta: float = BETA, beta_lin: float = BETA_LIN, keep: bool = False) -> dict:
+                  beta: float = BETA, beta_lin: float = BETA_LIN, keep: bool = False, map_fn=map) -> dict:
     """One forward pass of the layer for the given token rows.
 
     dense: w_router, w_down, w_up, gamma, sh_gate, sh_up, sh_down (bf16 bits);
     get_expert(e) -> dequantised {w1, w3, w2}.  Every output row depends only
     on its own input row, so any subset of tokens can be evaluated on its own
-    (the permutation diagnostics then refer to that subset).
+    (the permutation diagnostics then refer to that subset).  map_fn as for
+    routed_experts.
     """
     r = route(x_bits, dense["w_router"], bias, shape.top_k)
     z = latent_down(x_bits, dense["w_down"])
-    re = routed_experts(z, r["ids"], get_expert, shape.n_experts, beta, beta_lin, keep=keep)
+    re = routed_experts(z, r["ids"], get_expert, shape.n_experts, beta, beta_lin, keep=keep, map_fn=map_fn)
     y = combine(re["Y_pair"], r["weights"])
     y_n = rmsnorm(y, dense["gamma"], eps)
     routed = up_proj(y_n, dense["w_up"])
@@ -249,21 +260,6 @@ def layer_forward(x_bits, dense: dict, bias, get_expert, shape, eps: float = RMS
         out["H_sorted"] = re["H_sorted"]
         out["Y_sorted"] = re["Y_sorted"]
         out["Y_pair"] = re["Y_pair"]
+        out["H_pair"] = re["H_pair"]
     return out
 
-
-def grouped_microbench(A_bits, counts, get_expert, segments=None,
-                       beta: float = BETA, beta_lin: float = BETA_LIN) -> dict:
-    """Isolated grouped expert MLP on already-permuted rows: expert e owns rows
-    offsets[e]..offsets[e+1] of A (bf16 bits [P, L]); returns H and Y per
-    requested segment (default all) as {e: (row0, H, Y)}."""
-    counts = np.asarray(counts, dtype=np.int64)
-    offsets = np.zeros(counts.size + 1, dtype=np.int64)
-    np.cumsum(counts, out=offsets[1:])
-    segs = np.nonzero(counts)[0] if segments is None else segments
-    res = {}
-    for e in segs:
-        r0, r1 = offsets[e], offsets[e + 1]
-        H, Y = expert_mlp(bf16_to_f64(A_bits[r0:r1]), get_expert(e), beta, beta_lin)
-        res[int(e)] = (int(r0), H, Y)
-    return res

@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
     for fn in _declared():
         assert fn in exported, fn
         assert hasattr(lib, fn)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert b"workspace" in lib.moe_strerror(_lib.MOE_EWORKSPACE)
 
 
@@ -124,9 +124,9 @@ def test_grouped_gemm_validation(lib):
     G, D = _lib.MOE_OP_GATEUP_SITU, _lib.MOE_OP_DOWN
     f32 = _lib.MOE_DT_F32
 
-    def call(op=G, P_=P, off=FAKE, sp=FAKE, A=FAKE, dt=f32, wp=FAKE, wsc=FAKE, w3p=FAKE, w3s=FAKE, pw=None,
-             C=FAKE, wsb=ws):
-        return lib.mxfp4_grouped_gemm(s, op, P_, off, sp, A, dt, wp, wsc, w3p, w3s, pw, C, FAKE, wsb, None)
+    def call(op=G, P_=P, off=FAKE, sp=FAKE, A=FAKE, ar=P // 16, dt=f32, wp=FAKE, wsc=FAKE, w3p=FAKE, w3s=FAKE,
+             pw=None, C=FAKE, wsb=ws):
+        return lib.mxfp4_grouped_gemm(s, op, P_, off, sp, A, ar, dt, wp, wsc, w3p, w3s, pw, C, FAKE, wsb, None)
 
     assert call(op=5) == _lib.MOE_EINVAL
     assert call(dt=9) == _lib.MOE_EINVAL
@@ -138,7 +138,16 @@ def test_grouped_gemm_validation(lib):
     assert call(A=FAKE + 4) == _lib.MOE_EINVAL
     assert call(wsc=FAKE + 1) == _lib.MOE_EINVAL
     assert call(wsb=ws - 1) == _lib.MOE_EWORKSPACE
-    assert call(op=D, w3p=None, w3s=None, wsb=16) == _lib.MOE_EWORKSPACE
+    assert call(op=D, w3p=None, w3s=None, ar=P, wsb=16) == _lib.MOE_EWORKSPACE
+    # rows of A: at least one; at least P when A holds the sorted rows itself
+    assert call(ar=0) == _lib.MOE_EINVAL
+    assert call(sp=None, ar=P - 1) == _lib.MOE_EINVAL
+    assert call(op=D, w3p=None, w3s=None, ar=P - 1) == _lib.MOE_EINVAL
+    # gathered rows are addressed with 32-bit offsets: A below 2^31 bytes
+    lat = s.latent
+    big = -(-(1 << 31) // (lat * 4))  # smallest row count with 2^31 bytes or more
+    assert call(ar=big) == _lib.MOE_ENOTSUP
+    assert call(ar=big - 1, wsb=ws - 1) == _lib.MOE_EWORKSPACE
 
 
 def test_combine_and_shared_validation(lib):

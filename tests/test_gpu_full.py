@@ -3,8 +3,11 @@
 The whole layer runs on the GPU for every token of each workload, in the
 launch configuration the benchmark times.  The float64 oracle checks: expert
 ids and the permutation for every token (exact outside near-ties), z for every
-token, and the full layer output, H and Y for sampled tokens (the oracle
-evaluates one token at a time; each output row depends only on its token).
+token up to T=256, and the full layer output plus H and Y of every pair for
+all 16 decode tokens, and for 64 tokens at T=256 and T=4096 chosen so that
+their pairs fall in chunks with every count of active token tiles and in a
+second chunk of a long segment (each output row depends only on its token, so
+the oracle evaluates just those tokens).
 """
 import numpy as np
 import pytest
@@ -13,8 +16,8 @@ import torch
 import synth
 from synth.device import to_dev, upload_tokens, upload_weights
 from oracle import layer
-from gpu_common import (TOL, ZIPF_BIAS, check_permutation, check_routing, expert_cache, rel_max_err,
-                        say)
+from gpu_common import (TOL, ZIPF_BIAS, check_permutation, check_routing, expert_cache, oracle_layer_threaded,
+                        oracle_threads, pick_tokens, rel_max_err, say)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = "cuda"
@@ -48,39 +51,96 @@ def _run_layer(mx, k3, wl, bias_np=None, operand_mode=0, **schedule):
     return {k: v.cpu().numpy() for k, v in bufs.items() if k not in ("ws",)}
 
 
-def _full_check(mx, k3, wl, bias, sample, tag, operand_mode=0, inter_tol=1e-4):
+# oracle results per (workload, sampled tokens): the three prefill operand
+# modes check the same tokens against one oracle run
+_ORACLE = {}
+# 16-token tiles per chunk of the prefill kernels
+CHUNK_ROWS = 96
+N_SAMPLE = 64
+
+
+def _routing_ref(k3, wl, bias):
+    key = ("route", wl.name)
+    if key not in _ORACLE:
+        _ORACLE[key] = layer.route(synth.gen_tokens(wl), k3["dense"]["w_router"], bias, wl.shape.top_k)
+    return _ORACLE[key]
+
+
+def _sample_for(k3, wl, bias):
+    """All tokens up to 16; else N_SAMPLE tokens covering every tile count of a chunk."""
+    if wl.tokens <= 16:
+        return np.arange(wl.tokens)
+    ref = _routing_ref(k3, wl, bias)
+    return pick_tokens(ref["ids"], ref["gap"], wl.shape.n_experts, CHUNK_ROWS, N_SAMPLE)
+
+
+def _oracle_for(k3, wl, bias, sample):
+    key = (wl.name, tuple(sample.tolist()))
+    if key not in _ORACLE:
+        say(f"oracle: layer for {sample.size} tokens of {wl.name} ({oracle_threads()} threads)")
+        x_bits = synth.gen_tokens(wl)
+        _ORACLE[key] = oracle_layer_threaded(wl, x_bits[sample], k3["dense"], bias)
+    return _ORACLE[key]
+
+
+def _full_check(mx, k3, wl, bias, tag, operand_mode=0, inter_tol=1e-4):
     say(f"case: {tag} (T={wl.tokens}) full layer on GPU")
     g = _run_layer(mx, k3, wl, None if wl.bias_mode == "normal" else bias, operand_mode)
     x_bits = synth.gen_tokens(wl)
     d = k3["dense"]
     say(f"case: {tag} oracle routing for all tokens")
-    ref = layer.route(x_bits, d["w_router"], bias, wl.shape.top_k)
+    ref = _routing_ref(k3, wl, bias)
     excl = check_routing(g["topk_ids"], g["topk_w"], ref)
     same = (g["topk_ids"] == ref["ids"]).all(axis=1)
     say(f"{tag}: {excl.size} near-tie tokens excluded, {int((~same).sum())} of them with a different set")
-    # outputs are compared only where the GPU chose the oracle's expert set
-    sample = np.array([t for t in sample if same[t]])
     check_permutation(g, ref["ids"], wl.shape.n_experts, excl)
+    sample = _sample_for(k3, wl, bias)
+    # outputs are compared where the GPU chose the oracle's expert set: every
+    # sampled token but a near-tie one (the prefill-size samples hold none)
+    keep = same[sample]
+    assert keep.sum() >= sample.size - np.isin(sample, excl).sum() and keep.sum() >= min(wl.tokens - excl.size,
+                                                                                         N_SAMPLE)
     zs = sample if wl.tokens > 256 else np.arange(wl.tokens)
     z_ref = layer.latent_down(x_bits[zs], d["w_down"])
     assert rel_max_err(g["z"][zs], z_ref) < 1e-5
-    say(f"case: {tag} oracle layer for tokens {list(sample)}")
-    r = layer.layer_forward(x_bits[sample], d, bias, k3["cache"], wl.shape, keep=True)
-    err = rel_max_err(g["out"][sample], r["out"])
-    say(f"{tag}: max|gpu-oracle|/rms over sampled tokens = {err:.3e} (excluded near-ties: {excl.size})")
+    r = _oracle_for(k3, wl, bias, sample)
+    err = rel_max_err(g["out"][sample[keep]], r["out"][keep])
+    ex = r["perm"]["counts"]
+    say(f"{tag}: max|gpu-oracle|/rms over {int(keep.sum())} tokens ({int((ex > 0).sum())} experts) = {err:.3e} "
+        f"(excluded near-ties: {excl.size})")
     assert err <= TOL
-    # the per-pair intermediates of the sampled tokens
+    # every pair of the compared tokens: H and Y rows at the GPU's sorted positions
     k = wl.shape.top_k
-    pp = g["pair_pos"].reshape(-1, k)[sample]
-    Y_pair = r["Y_pair"]  # [s, k, L] oracle, unweighted
-    assert rel_max_err(g["Y"][pp.reshape(-1)], Y_pair.reshape(-1, Y_pair.shape[-1])) < inter_tol
+    pp = g["pair_pos"].reshape(-1, k)[sample[keep]].reshape(-1)
+    errH = rel_max_err(g["H"][pp], r["H_pair"][keep].reshape(pp.size, -1))
+    errY = rel_max_err(g["Y"][pp], r["Y_pair"][keep].reshape(pp.size, -1))
+    say(f"{tag}: {pp.size} pairs, H {errH:.3e}, Y {errY:.3e}")
+    assert errH < inter_tol and errY < inter_tol
+    # at prefill sizes the pairs cover every count of active token tiles that
+    # the layer's chunks have, and a chunk past a segment's first
+    if wl.tokens * k / wl.shape.n_experts >= 2:
+        offs = g["offsets"]
+
+        def tile_counts(rows):
+            e_of = np.searchsorted(offs, rows, side="right") - 1
+            row_in = rows - offs[e_of]
+            chunk_len = np.minimum(CHUNK_ROWS, offs[e_of + 1] - offs[e_of] - row_in // CHUNK_ROWS * CHUNK_ROWS)
+            return (chunk_len + 15) // 16, row_in
+
+        covered, row_in = tile_counts(pp)
+        existing, _ = tile_counts(np.arange(wl.tokens * k))
+        say(f"{tag}: active-tile counts covered {sorted(set(covered.tolist()))} of {sorted(set(existing.tolist()))}; "
+            f"rows past a first chunk: {int((row_in >= CHUNK_ROWS).sum())}")
+        assert set(covered.tolist()) == set(existing.tolist())
+        if (np.diff(offs) > CHUNK_ROWS).any():
+            assert (row_in >= CHUNK_ROWS).any()
     return err
 
 
 def test_decode_T16(mx, k3):
     wl = synth.workload("decode")
     bias = synth.gen_bias(wl)
-    err = _full_check(mx, k3, wl, bias, np.array([0, 7, 15]), "decode")
+    err = _full_check(mx, k3, wl, bias, "decode")
     assert err < 1e-3
 
 
@@ -103,13 +163,13 @@ def test_schedules_bitwise_equal(mx, k3, wl_name):
 def test_batched_decode_T256_zipf(mx, k3):
     wl = synth.workload("batched_decode")
     bias = synth.gen_bias(wl, ZIPF_BIAS)
-    _full_check(mx, k3, wl, bias, np.array([3, 128, 255]), "batched_decode")
+    _full_check(mx, k3, wl, bias, "batched_decode")
 
 
 def test_prefill_T4096(mx, k3):
     wl = synth.workload("prefill")
     bias = synth.gen_bias(wl)
-    _full_check(mx, k3, wl, bias, np.array([0, 2049, 4095]), "prefill")
+    _full_check(mx, k3, wl, bias, "prefill")
 
 
 def test_prefill_T4096_mx8x3(mx, k3):
@@ -118,8 +178,7 @@ def test_prefill_T4096_mx8x3(mx, k3):
     wl = synth.workload("prefill")
     bias = synth.gen_bias(wl)
     # three fp8 terms leave about 2^-12 of each 32-block's maximum: intermediates within 2e-3
-    err = _full_check(mx, k3, wl, bias, np.array([1, 1500, 4094]), "prefill mx8x3", _lib.MOE_OPND_MX8X3,
-                      inter_tol=2e-3)
+    err = _full_check(mx, k3, wl, bias, "prefill mx8x3", _lib.MOE_OPND_MX8X3, inter_tol=2e-3)
     assert err < 2e-3
 
 
@@ -128,8 +187,7 @@ def test_prefill_T4096_mx6x3(mx, k3):
     from mxfp4_latent_moe_amd import _lib
     wl = synth.workload("prefill")
     bias = synth.gen_bias(wl)
-    err = _full_check(mx, k3, wl, bias, np.array([2, 2500, 4093]), "prefill mx6x3", _lib.MOE_OPND_MX6X3,
-                      inter_tol=2e-3)
+    err = _full_check(mx, k3, wl, bias, "prefill mx6x3", _lib.MOE_OPND_MX6X3, inter_tol=2e-3)
     assert err < 2e-3
 
 
@@ -174,32 +232,38 @@ def test_microbench_grouped_gemm(mx, k3):
     assert max(errs) <= TOL
 
 
-def test_expert_slice_partition_invariance(mx, k3):
+@pytest.mark.parametrize("wl_name,mode,n_slice", [("decode", 0, 112), ("prefill", 0, 16),
+                                                   ("prefill", 3, 112), ("prefill", 3, 16)])
+def test_expert_slice_partition_invariance(mx, k3, wl_name, mode, n_slice):
     """One GPU's share under expert parallelism: the grouped GEMMs run over a
-    contiguous 112-expert slice (weights, offsets and rows of that slice only)
-    give bit-identical H and Y rows to the full 896-expert call."""
+    contiguous slice of experts (weights, offsets and sorted rows of that slice
+    only, z of all T tokens) give bit-identical H and Y rows to the full
+    896-expert call.  Slices of 112 experts are the 8-GPU split; at prefill a
+    16-expert slice has fewer pairs than tokens, so the MX modes' activation
+    split then gathers the slice's rows itself."""
     from mxfp4_latent_moe_amd import ops
-    wl = synth.workload("decode")
+    wl = synth.workload(wl_name)
     sh = wl.shape
-    say("case: decode layer, then each of the 8 expert slices of 112 experts")
-    g = _run_layer(mx, k3, wl)
+    say(f"case: {wl_name} layer (operand mode {mode}), then expert slices of {n_slice}")
+    g = _run_layer(mx, k3, wl, operand_mode=mode)
     w = k3["w"]
     offsets = g["offsets"]
-    n_slice = sh.n_experts // 8
-    for e0 in range(0, sh.n_experts, n_slice):
+    z = to_dev(g["z"], DEV)
+    starts = range(0, sh.n_experts, n_slice) if n_slice * 8 >= sh.n_experts else (0, 448, sh.n_experts - n_slice)
+    for e0 in starts:
         r0, r1 = int(offsets[e0]), int(offsets[e0 + n_slice])
         if r1 == r0:
             continue
         sub = synth.LayerShape(sh.hidden, sh.latent, n_slice, sh.top_k, sh.inter, sh.n_shared, sh.shared_inter)
-        s = mx.shape_of(sub)
+        s = mx.shape_of(sub, mode)
         P = r1 - r0
         off = to_dev((offsets[e0:e0 + n_slice + 1] - r0).astype(np.int32), DEV)
         sp = to_dev(g["sorted_pair"][r0:r1].astype(np.int32), DEV)
-        z = to_dev(g["z"], DEV)
         ws = torch.empty(ops.workspace_bytes(s, ops.MOE_FN_GROUPED_GEMM, P), dtype=torch.uint8, device=DEV)
         H = torch.empty((P, sh.inter), dtype=torch.float32, device=DEV)
         Y = torch.empty((P, sh.latent), dtype=torch.float32, device=DEV)
         sl = slice(e0, e0 + n_slice)
+        say(f"  slice {e0}..{e0 + n_slice - 1}: {P} rows, z has {wl.tokens}")
         ops.grouped_gemm(s, ops.MOE_OP_GATEUP_SITU, P, off, sp, z, w["w1_packed"][sl], w["w1_scale"][sl],
                          w["w3_packed"][sl], w["w3_scale"][sl], None, H, ws)
         ops.grouped_gemm(s, ops.MOE_OP_DOWN, P, off, sp, H, w["w2_packed"][sl], w["w2_scale"][sl], None, None,
@@ -207,3 +271,78 @@ def test_expert_slice_partition_invariance(mx, k3):
         torch.cuda.synchronize()
         assert (H.cpu().numpy() == g["H"][r0:r1]).all(), e0
         assert (Y.cpu().numpy() == g["Y"][r0:r1]).all(), e0
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_grouped_gemm_rows_past_32bit_offsets(mx, k3, mode):
+    """180,000 sorted rows of fp32 activations: the gate/up input (2.58 GB) and
+    the down input H (2.21 GB) both pass 2^31 bytes, which the kernels address
+    from each chunk's first row.  Rows of the first, a middle and the last
+    experts against the oracle."""
+    from mxfp4_latent_moe_amd import ops
+    wl = synth.workload("microbench")
+    sh = wl.shape
+    E = sh.n_experts
+    counts = np.full(E, 200, np.int64)
+    counts[E - 1] += 800
+    P = int(counts.sum())
+    assert P == 180_000 and P * sh.latent * 4 > 2 ** 31 and P * sh.inter * 4 > 2 ** 31
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    say(f"case: {P} sorted rows, fp32 activations, operand mode {mode}")
+    A_bits = synth.gen_microbench_activations(wl, P)
+    A = torch.from_numpy(A_bits.view(np.int16)).to(DEV).view(torch.bfloat16).float()
+    s = mx.shape_of(sh, mode)
+    w = k3["w"]
+    ws = torch.empty(ops.workspace_bytes(s, ops.MOE_FN_GROUPED_GEMM, P), dtype=torch.uint8, device=DEV)
+    H = torch.empty((P, sh.inter), dtype=torch.float32, device=DEV)
+    Y = torch.empty((P, sh.latent), dtype=torch.float32, device=DEV)
+    off_d = to_dev(offsets, DEV)
+    ops.grouped_gemm(s, ops.MOE_OP_GATEUP_SITU, P, off_d, None, A, w["w1_packed"], w["w1_scale"], w["w3_packed"],
+                     w["w3_scale"], None, H, ws)
+    ops.grouped_gemm(s, ops.MOE_OP_DOWN, P, off_d, None, H, w["w2_packed"], w["w2_scale"], None, None, None, Y, ws)
+    torch.cuda.synchronize()
+    del A
+    tol = 1e-4 if mode == 0 else 2e-3
+    for e in (0, E // 2, E - 2, E - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        rows = np.r_[r0:r0 + 24, r1 - 24:r1]
+        Hr, Yr = layer.expert_mlp(layer.bf16_to_f64(A_bits[rows]), k3["cache"](e))
+        Hg = H[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        Yg = Y[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        eh, ey = rel_max_err(Hg, Hr), rel_max_err(Yg, Yr)
+        say(f"  expert {e} rows {r0}..{r1 - 1}: H {eh:.3e}, Y {ey:.3e}")
+        assert eh < tol and ey < tol
+
+
+@pytest.mark.parametrize("wl_name", ["decode", "prefill"])
+def test_graph_capture_replays_full_shape(mx, k3, wl_name):
+    """The full-shape layer captured once in a HIP graph (at decode the
+    persistent grouped kernel with its occupancy-sized grid and device-side
+    item count, at prefill the tiled kernels); three replays with eager work
+    in between, each bitwise equal to the eager result."""
+    wl = synth.workload(wl_name)
+    say(f"case: {wl_name} (T={wl.tokens}) layer captured in a HIP graph, 3 replays")
+    layer_ = mx.LatentMoE(mx.shape_of(wl.shape), k3["w"], DEV)
+    x = upload_tokens(wl, DEV)
+    eager = {k: v.clone() for k, v in layer_.forward(x).items() if k not in ("ws", "ws_shared")}
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer_.forward(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        bufs = layer_.forward(x)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for k in ("out", "H", "Y", "topk_ids", "z", "offsets"):
+            bufs[k].zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("topk_ids", "topk_w", "z", "offsets", "sorted_pair", "H", "Y", "out"):
+            assert torch.equal(bufs[k], eager[k]), (i, k)
+    del graph

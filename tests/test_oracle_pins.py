@@ -328,3 +328,25 @@ def test_shared_experts_concatenated_glu_identity():
     # and it is not a single expert's output
     single = layer.shared_experts(x, g[:Is], u[:Is], dn[:, :Is], 1, Is)
     assert np.abs(single - ref).max() > 1e-3
+
+
+def test_threaded_expert_map_and_pair_layout():
+    """The per-expert step may run under a thread pool's map: same result bit for
+    bit as the serial loop.  H_pair / Y_pair hold each pair's rows in pair order,
+    the rows H_sorted / Y_sorted hold at that pair's sorted position."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl, x, d, b, st = _tiny()
+    sh = wl.shape
+    cache = layer.ExpertCache(lambda e: {k: v[e] for k, v in st.items()})
+    r = layer.layer_forward(x, d, b, cache, sh, keep=True)
+    with ThreadPoolExecutor(4) as ex:
+        r2 = layer.layer_forward(x, d, b, cache, sh, keep=True, map_fn=ex.map)
+    for key in ("out", "H_sorted", "Y_sorted", "H_pair", "Y_pair"):
+        assert np.array_equal(r[key], r2[key]), key
+    pos = r["perm"]["pair_pos"]
+    k = sh.top_k
+    assert np.array_equal(r["H_pair"].reshape(-1, sh.inter), r["H_sorted"][pos])
+    assert np.array_equal(r["Y_pair"].reshape(-1, sh.latent), r["Y_sorted"][pos])
+    # the pair order is p = t*k + j: token t's slot j
+    t, j = 5, 2
+    assert np.array_equal(r["H_pair"][t, j], r["H_sorted"][pos[t * k + j]])
