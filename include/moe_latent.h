@@ -150,6 +150,25 @@ int moe_route_capped(const moe_shape *shape, int T, const uint16_t *x, const uin
                      int32_t *topk_ids, float *topk_w, float *z, float *gap, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* moe_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments and outputs are moe_route's, without the workspace: the call uses
+ * a fixed per-device scratch array of MOE_ROUTE_NOALLOC_SCRATCH_BYTES that the
+ * library holds from its first use on a device until the process ends, and it
+ * calls no allocating routine.  Its first call on a device looks up that
+ * device's copy of the array (a host-side query, no allocation).
+ * Every call on one GPU shares the array and leaves its last contents in it
+ * (nothing in it needs to start at zero): calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must not be made.
+ * Size limit: moe_workspace_bytes(shape, MOE_FN_ROUTE, T) must not exceed
+ * MOE_ROUTE_NOALLOC_SCRATCH_BYTES (at K3 shapes: T <= 64, the decode sizes).
+ * Errors: those of moe_route; MOE_EWORKSPACE when T needs more scratch than
+ * the array holds. */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_route_noalloc(const moe_shape *shape, int T, const uint16_t *x, const uint16_t *w_router,
+                      const float *bias, const uint16_t *w_down, int32_t *topk_ids, float *topk_w,
+                      float *z, float *gap, void *stream);
+
 /* Token permutation: stable counting sort of the pairs p = t*k + j by expert.
  * Follows: kimi-k3-mlx README, REAP section, two-bank paragraph (pairs sorted
  * by expert index give each expert a contiguous slice).

@@ -16,12 +16,13 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP, MOE_EINTERNAL = 0, -1
 MOE_OPND_BF16X2, MOE_OPND_BF16, MOE_OPND_MX8X3, MOE_OPND_MX6X3 = 0, 1, 2, 3
 MOE_OP_GATEUP_SITU, MOE_OP_DOWN = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_ROUTE_NOALLOC_SCRATCH_BYTES = 8 << 20
 (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP, MOE_FN_SHARED_FFN,
  MOE_FN_REAP_SALIENCY, MOE_FN_COMBINE_NORM_UP_REAP) = range(7)
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute",
            "mxfp4_grouped_gemm", "moe_combine_norm_up", "shared_expert_ffn", "moe_reap_saliency",
-           "moe_combine_norm_up_reap", "moe_route_capped")
+           "moe_combine_norm_up_reap", "moe_route_capped", "moe_route_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -71,6 +72,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.shared_expert_ffn.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.moe_reap_saliency.restype = i32
     lib.moe_reap_saliency.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.moe_route_noalloc.restype = i32
+    lib.moe_route_noalloc.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_route_capped.restype = i32
     lib.moe_route_capped.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine_norm_up_reap.restype = i32

@@ -214,7 +214,32 @@ int guarded(F &&f) {
   }
 }
 
+// ---- the fixed routing scratch of moe_route_noalloc: one copy per device,
+// alive until the process ends.  Host code never uses the array's name as an
+// address; it uses the device address hipGetSymbolAddress returned for the
+// current device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = MOE_ROUTE_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device.
+static int scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= 64) return MOE_ENOTSUP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 // Router, top-k (capped when `promoted` is given) and the latent projection.
 static int route_impl(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_router, const float *bias,
@@ -327,6 +352,22 @@ int moe_route(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_ro
               float *gap, void *ws, size_t ws_bytes, void *stream) {
   return guarded([&]() -> int {
     return route_impl(s, T, x, w_router, bias, w_down, nullptr, 0, topk_ids, topk_w, z, gap, ws, ws_bytes, stream);
+  });
+}
+
+int moe_route_noalloc(const moe_shape *s, int T, const uint16_t *x, const uint16_t *w_router, const float *bias,
+                      const uint16_t *w_down, int32_t *topk_ids, float *topk_w, float *z, float *gap, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (T <= 0) return MOE_EINVAL;
+    // the same workspace layout moe_route uses, in the fixed scratch
+    if (route_ws(s, T).total > NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    void *ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    return route_impl(s, T, x, w_router, bias, w_down, nullptr, 0, topk_ids, topk_w, z, gap, ws,
+                      NOALLOC_SCRATCH_BYTES, stream);
   });
 }
 

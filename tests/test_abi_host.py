@@ -231,3 +231,14 @@ def test_route_capped_validation(lib):
     a = list(args)
     a[12] = ws - 1
     assert lib.moe_route_capped(s, *a) == _lib.MOE_EWORKSPACE
+
+
+def test_route_noalloc_validation(lib):
+    """Sizes past the fixed scratch are rejected before any device work."""
+    s = _shape()
+    assert lib.moe_workspace_bytes(s, _lib.MOE_FN_ROUTE, 64) <= _lib.MOE_ROUTE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_workspace_bytes(s, _lib.MOE_FN_ROUTE, 65) > _lib.MOE_ROUTE_NOALLOC_SCRATCH_BYTES
+    args = (FAKE,) * 9 + (None,)
+    assert lib.moe_route_noalloc(s, 65, *args) == _lib.MOE_EWORKSPACE
+    assert lib.moe_route_noalloc(s, 0, *args) == _lib.MOE_EINVAL
+    assert lib.moe_route_noalloc(None, 16, *args) == _lib.MOE_EINVAL
