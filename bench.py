@@ -255,6 +255,57 @@ def summarize_pmc(fetch_dir, write_dir):
     print(f"traffic_bytes_per_launch: {traffic:.0f}")
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_BUSY_CU_CYCLES TCC_HIT TCC_MISS")
+SIMDS = 1024   # 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def summarize_mfma(d, cmd):
+    """One --pmc run with MFMA_COUNTERS -> per-kernel MFMA work and utilisation.
+
+    Per dispatch, averaged over the kernel's dispatches: duration from the
+    dispatch timestamps; executed MFMA FLOPs = 512 x the MOPS counters (the
+    counters count MFMA math operations in units of 512); MFMA busy = the SIMDs'
+    MFMA-busy cycles over (GPU-active cycles of one XCD x 1024 SIMDs), the
+    counter's summed-over-XCD GRBM_GUI_ACTIVE divided by 8; L2 hit rate."""
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not f:
+        sys.exit(f"no counter_collection.csv under {d}")
+    per = {}
+    for r in csv.DictReader(open(f[0])):
+        k = _short(r["Kernel_Name"])
+        disp = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+        disp[r["Counter_Name"]] = float(r["Counter_Value"])
+        disp["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    print("# MFMA work and utilisation per kernel, prefill T=4096 at full K3 shapes")
+    print("# made by:")
+    print(f"#   cd /tmp && timeout -s KILL 180 rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d <D> -o run -- "
+          f"python3 <repo>/bench.py {cmd}")
+    print("#   python3 bench.py --summarize-mfma <D> --summary-cmd '<the bench.py arguments>'")
+    print("# exec_tflop: executed MFMA FLOPs per dispatch (512 x MOPS, all types); mfma_busy: MFMA-busy SIMD cycles / "
+          "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)")
+    print("# clk_ghz: GRBM_GUI_ACTIVE / 8 per microsecond of the dispatch (the engine clock the counters saw)")
+    print(f"{'kernel':56s} {'calls':>5s} {'avg_us':>9s} {'exec_tflop':>10s} {'exec_tf/s':>9s} {'mfma_busy':>9s} "
+          f"{'l2_hit':>7s} {'clk_ghz':>7s}")
+    for k, disps in per.items():
+        ds = list(disps.values())
+        n = len(ds)
+        if n == 0 or "SQ_VALU_MFMA_BUSY_CYCLES" not in ds[0]:
+            continue
+        avg = lambda key: sum(x.get(key, 0.0) for x in ds) / n  # noqa: E731
+        us = avg("_us")
+        flop = 512.0 * (avg("SQ_INSTS_VALU_MFMA_MOPS_BF16") + avg("SQ_INSTS_VALU_MFMA_MOPS_F8")
+                        + avg("SQ_INSTS_VALU_MFMA_MOPS_F6F4"))
+        if flop == 0:
+            continue
+        active = avg("GRBM_GUI_ACTIVE") / XCDS
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (active * SIMDS) if active else 0.0
+        hit, miss = avg("TCC_HIT"), avg("TCC_MISS")
+        print(f"{k[:56]:56s} {n:5d} {us:9.1f} {flop / 1e12:10.4f} {flop / (us * 1e-6) / 1e12:9.1f} "
+              f"{100 * busy:8.1f}% {100 * hit / max(1.0, hit + miss):6.1f}% {active / us / 1e3:7.2f}")
+
+
 def cpu_baseline(synth, wl, n_tokens, bias=None):
     """The float64 oracle as it stands, on the first n_tokens tokens of the workload.
 
@@ -548,12 +599,17 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true", help="run a known-size copy for counter scaling")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--summary-cmd", default="", help="the profiled bench.py arguments, for the summary header")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.summary_cmd)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU expert parallelism "

@@ -282,6 +282,8 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
   float *C = g.splits > 1 ? g.partial + (long long)split * rows * (PAIR ? 2 * N : N) : g.C;
   const long long ldc = g.splits > 1 ? (PAIR ? 2 * N : N) : g.ldc;
   const bool acc_in = g.splits == 1 && g.accumulate;
+  // 16-byte stores need every row to start 16-byte aligned
+  const bool vec_ok = (ldc & 3) == 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int t = t0 + tokrow0 + 32 * b + l32;
@@ -317,11 +319,19 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
         for (int a = 0; a < 4; ++a) {
           const int col = n0 + 128 * wn + 32 * a + 8 * q + 4 * lh;
           if (col >= N) continue;
-          f32x4_t v;
+          if (vec_ok && col + 3 < N) {
+            f32x4_t v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[a][b][4 * q + r];
-          if (acc_in) v += *reinterpret_cast<const f32x4_t *>(crow + col);
-          *reinterpret_cast<f32x4_t *>(crow + col) = v;
+            for (int r = 0; r < 4; ++r) v[r] = acc[a][b][4 * q + r];
+            if (acc_in) v += *reinterpret_cast<const f32x4_t *>(crow + col);
+            *reinterpret_cast<f32x4_t *>(crow + col) = v;
+          } else {
+            // the last group of a row whose length is not a multiple of 4 (the
+            // router at an expert count that is not), or rows not 16-byte aligned
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (col + r < N) crow[col + r] = acc_in ? crow[col + r] + acc[a][b][4 * q + r] : acc[a][b][4 * q + r];
+          }
         }
       }
     }

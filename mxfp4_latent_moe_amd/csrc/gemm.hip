@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void ws_gemm_kernel(GemmArgs g) {
         for (int r = 0; r < 4; ++r) v[r] *= rs;
       }
       float *cp = g.C + orow * g.ldc + col0;
-      if (col0 + 3 < N) {
+      if (col0 + 3 < N && (g.ldc & 3) == 0) {
         f32x4_t o = {v[0], v[1], v[2], v[3]};
         if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
         *reinterpret_cast<f32x4_t *>(cp) = o;

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(GemmArgs g) {
     if (g.splits > 1) {
       const int ncols = PAIR ? 2 * N : N;
       float *pp = g.partial + ((long long)split * g.partial_rows + orow) * ncols;
-      if (col0 + 3 < N) {
+      if (col0 + 3 < N && (N & 3) == 0) {
         *reinterpret_cast<f32x4_t *>(pp + col0) = acc[m];
         if constexpr (PAIR) *reinterpret_cast<f32x4_t *>(pp + N + col0) = acc[m + MT];
       } else {
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) void stream_gemm_kernel(GemmArgs g) {
       for (int r = 0; r < 4; ++r) v[r] *= rs;
     }
     float *cp = g.C + orow * g.ldc + col0;
-    if (col0 + 3 < N) {
+    if (col0 + 3 < N && (g.ldc & 3) == 0) {
       f32x4_t o = {v[0], v[1], v[2], v[3]};
       if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
       *reinterpret_cast<f32x4_t *>(cp) = o;

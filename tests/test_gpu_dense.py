@@ -59,17 +59,22 @@ def test_shared_expert_ffn_tiled(mx, mode, tol):
     assert err <= tol
 
 
-def test_route_tiled(mx):
-    """Router logits + top-k and the latent projection z at T = 1100."""
+@pytest.mark.parametrize("E,T", [(64, 1100), (62, 1100), (242, 1100), (62, 300), (242, 40)])
+def test_route_tiled(mx, E, T):
+    """Router logits + top-k and the latent projection z: at T = 1100 on the
+    tiled kernel, at T = 300 and 40 on the mid-size and streaming kernels.
+    Expert counts that are not a multiple of 4 leave a ragged group of logit
+    columns at the end of every row."""
     from mxfp4_latent_moe_amd import _lib, ops
     dev = torch.device("cuda:0")
-    s = MID_SHAPE
-    T = MID.tokens
-    x_bits = synth.gen_tokens(MID)
-    d = synth.gen_dense(MID)
-    bias = synth.gen_bias(MID)
+    s = synth.LayerShape(MID_SHAPE.hidden, MID_SHAPE.latent, E, MID_SHAPE.top_k, MID_SHAPE.inter,
+                         MID_SHAPE.n_shared, MID_SHAPE.shared_inter)
+    wl = synth.Workload(f"mid{T}e{E}", 12, s, T, 12, 0.02, 0.1, "normal", 119, 121)
+    x_bits = synth.gen_tokens(wl)
+    d = synth.gen_dense(wl)
+    bias = synth.gen_bias(wl)
     say(f"case: moe_route T={T} H={s.hidden} E={s.n_experts} L={s.latent}")
-    sh = _shape(mx, 0)
+    sh = mx.make_shape(s.hidden, s.latent, s.n_experts, s.top_k, s.inter, s.n_shared, s.shared_inter)
     ws = torch.empty(ops.workspace_bytes(sh, _lib.MOE_FN_ROUTE, T), dtype=torch.uint8, device=dev)
     ids = torch.empty((T, s.top_k), dtype=torch.int32, device=dev)
     w = torch.empty((T, s.top_k), dtype=torch.float32, device=dev)

@@ -346,3 +346,66 @@ def test_graph_capture_replays_full_shape(mx, k3, wl_name):
         for k in ("topk_ids", "topk_w", "z", "offsets", "sorted_pair", "H", "Y", "out"):
             assert torch.equal(bufs[k], eager[k]), (i, k)
     del graph
+
+
+def _pruned_weights(w, keep_np):
+    """The layer's weights renumbered to the kept experts: new expert i is old
+    expert keep[i]; router rows, bias and expert stacks reordered alike."""
+    keep = torch.from_numpy(keep_np.astype(np.int64)).to(DEV)
+    wp = dict(w)
+    for key in ("w_router", "bias", "w1_packed", "w1_scale", "w3_packed", "w3_scale", "w2_packed", "w2_scale"):
+        wp[key] = w[key].index_select(0, keep).contiguous()
+    return wp
+
+
+@pytest.mark.parametrize("wl_name", ["decode", "prefill"])
+def test_runtime_pruning_renumbered_subset(mx, k3, wl_name):
+    """Runtime pruning (kimi-k3-mlx README, REAP section, prune-apply paragraph):
+    a layer renumbered to a kept subset of E' = 242 experts equals the full
+    896-expert layer whose dropped experts carry a -inf correction bias.  The
+    expert sets match for every token outside near-ties; the sorted rows, H and
+    Y of matching tokens are bitwise equal (z and every expert segment are the
+    same); routing weights and the output agree to rounding (the router's
+    split-K schedule depends on E, so logits may differ in the last bit).  An
+    identity prune (every expert kept in order) is a bitwise no-op."""
+    wl = synth.workload(wl_name)
+    sh = wl.shape
+    E = sh.n_experts
+    bias = synth.gen_bias(wl)
+    keep = np.sort(np.random.default_rng(11).choice(E, 242, replace=False))
+    dropped = np.setdiff1d(np.arange(E), keep)
+    bias_inf = bias.copy()
+    bias_inf[dropped] = -np.inf
+    say(f"case: {wl_name} (T={wl.tokens}) full layer with -inf bias on {dropped.size} experts vs E'=242")
+    full = _run_layer(mx, k3, wl, bias_inf)
+    w = dict(k3["w"])
+    w["bias"] = to_dev(bias, DEV)
+    sub = synth.LayerShape(sh.hidden, sh.latent, keep.size, sh.top_k, sh.inter, sh.n_shared, sh.shared_inter)
+    moe = mx.LatentMoE(mx.shape_of(sub), _pruned_weights(w, keep), DEV)
+    x = upload_tokens(wl, DEV)
+    g = {k: v.cpu().numpy() for k, v in moe.forward(x).items() if k not in ("ws", "ws_shared")}
+    torch.cuda.synchronize()
+    ids = keep[g["topk_ids"]]
+    assert (np.diff(ids, axis=1) > 0).all()  # renumbering keeps ids ascending
+    clear = full["gap"] >= 1e-5
+    same = (ids == full["topk_ids"]).all(axis=1)
+    assert same[clear].all(), np.nonzero(clear & ~same)[0][:10]
+    np.testing.assert_allclose(g["topk_w"][same], full["topk_w"][same], rtol=2e-6, atol=1e-8)
+    assert np.array_equal(g["z"], full["z"])
+    k = sh.top_k
+    pairs = (np.nonzero(same)[0][:, None] * k + np.arange(k)).reshape(-1)
+    pf, pg = full["pair_pos"][pairs], g["pair_pos"][pairs]
+    assert np.array_equal(g["H"][pg], full["H"][pf]) and np.array_equal(g["Y"][pg], full["Y"][pf])
+    if same.all():
+        assert np.array_equal(g["sorted_pair"], full["sorted_pair"])
+        assert np.array_equal(g["offsets"], full["offsets"][np.r_[keep, E]])
+    err = rel_max_err(g["out"][same], full["out"][same])
+    say(f"{wl_name}: {int(same.sum())} of {wl.tokens} tokens with the same set; out max rel diff {err:.2e}, "
+        f"bitwise {np.array_equal(g['out'][same], full['out'][same])}")
+    assert err < 1e-5
+    if wl_name == "decode":
+        ident = mx.LatentMoE(mx.shape_of(sh), _pruned_weights(w, np.arange(E)), DEV)
+        gi = {k_: v.cpu().numpy() for k_, v in ident.forward(x).items() if k_ not in ("ws", "ws_shared")}
+        base = _run_layer(mx, k3, wl)
+        for key in ("topk_ids", "topk_w", "z", "sorted_pair", "H", "Y", "out"):
+            assert np.array_equal(gi[key], base[key]), key
