@@ -19,6 +19,10 @@ from .inputs import (  # noqa: F401
     gen_gamma_random,
     gen_expert,
     gen_expert_stack,
+    gen_expert_affine2,
+    gen_expert_affine2_stack,
+    gen_expert_paired,
+    AFFINE_GROUP,
     gen_tokens,
     gen_bias,
     gen_microbench_counts,

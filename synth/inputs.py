@@ -34,6 +34,9 @@ T_SH_GATE, T_SH_UP, T_SH_DOWN = 6, 7, 8
 T_W1P, T_W1S, T_W3P, T_W3S, T_W2P, T_W2S = 10, 11, 12, 13, 14, 15
 T_ZIPF_PERM, T_MB_COUNTS, T_MB_A = 20, 21, 22
 T_GAMMA = 23
+# affine 2-bit bank: packed codes, bf16 scales, bf16 biases of w1, w3, w2
+T_Q1P, T_Q1S, T_Q1B, T_Q3P, T_Q3S, T_Q3B, T_Q2P, T_Q2S, T_Q2B = 30, 31, 32, 33, 34, 35, 36, 37, 38
+T_PAIRED = 39
 _WSET_DOMAIN = 1000
 
 
@@ -284,3 +287,67 @@ def gen_microbench_activations(wl: Workload, rows: int | None = None) -> np.ndar
     """A: bf16 bits [P, L] of N(0, 1), already in expert-sorted row order."""
     P = wl.tokens * wl.shape.top_k if rows is None else rows
     return _normal_bf16(_stream(wl.cfg_id, T_MB_A), (P, wl.shape.latent), 1.0, chunk_rows=2048)
+
+
+_QTIDS = {"w1": (T_Q1P, T_Q1S, T_Q1B), "w3": (T_Q3P, T_Q3S, T_Q3B), "w2": (T_Q2P, T_Q2S, T_Q2B)}
+AFFINE_GROUP = 64
+
+
+def gen_expert_affine2(wl: Workload, e: int, which: str):
+    """One expert matrix of the affine 2-bit bank: packed u8 [N, K/4] (raw
+    PCG64 bytes, so every 2-bit code is uniform over 0..3), bf16 scales and
+    biases [N, K/64].  scale = 2^-7 * U[0.5, 1.5), bias = -1.5 * scale *
+    U[0.8, 1.2) (each rounded to bf16): the grid scale * q + bias then spans
+    about [-1.5, 1.5] scales, the magnitude of the MXFP4 experts' weights."""
+    N, K = _expert_dims(wl.shape, which)
+    d = _WSET_DOMAIN + wl.wset
+    tp, ts, tb = _QTIDS[which]
+    nbytes = N * K // 4
+    raw = np.random.PCG64(_stream(d, tp, e)).random_raw((nbytes + 7) // 8).view(np.uint8)[:nbytes].reshape(N, K // 4)
+    G = K // AFFINE_GROUP
+    sc = np.float32(2.0 ** -7) * _rng(_stream(d, ts, e)).uniform(0.5, 1.5, size=(N, G)).astype(np.float32)
+    sc_bits = f32_to_bf16_bits(sc)
+    sc_r = bf16_bits_to_f32(sc_bits)
+    bi = np.float32(-1.5) * sc_r * _rng(_stream(d, tb, e)).uniform(0.8, 1.2, size=(N, G)).astype(np.float32)
+    return raw, sc_bits, f32_to_bf16_bits(bi)
+
+
+def gen_expert_affine2_stack(wl: Workload, experts) -> dict:
+    """Stacked affine-bank tensors {w1,w3,w2}_{packed,scale,bias} for the listed experts."""
+    ids = list(experts)
+    out = {}
+    for w in ("w1", "w3", "w2"):
+        N, K = _expert_dims(wl.shape, w)
+        out[w + "_packed"] = np.empty((len(ids), N, K // 4), np.uint8)
+        out[w + "_scale"] = np.empty((len(ids), N, K // AFFINE_GROUP), np.uint16)
+        out[w + "_bias"] = np.empty((len(ids), N, K // AFFINE_GROUP), np.uint16)
+
+    def job(i):
+        for w in ("w1", "w3", "w2"):
+            p, s_, b = gen_expert_affine2(wl, ids[i], w)
+            out[w + "_packed"][i], out[w + "_scale"][i], out[w + "_bias"][i] = p, s_, b
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(len(ids))))
+    return out
+
+
+def gen_expert_paired(wl: Workload, e: int, which: str) -> dict:
+    """The same weight matrix in both bank formats.  Every element is
+    c * 2^(x - 127) with c in {0, 0.5, 1, 1.5} (e2m1 codes 0..3) and one
+    exponent x in [exp_lo, exp_hi] per group of 64; MXFP4: those codes with
+    e8m0 scale x for both 32-blocks of the group; affine 2-bit: code q = c / 0.5
+    (the same code value), scale 2^(x - 128) as a bf16 (exponent field x - 1,
+    no mantissa), bias 0.  Returns {fp4_packed, fp4_scale, q2_packed,
+    q2_scale, q2_bias}."""
+    N, K = _expert_dims(wl.shape, which)
+    d = _WSET_DOMAIN + wl.wset
+    rng = _rng(_stream(d, T_PAIRED, e * 3 + {"w1": 0, "w3": 1, "w2": 2}[which]))
+    codes = rng.integers(0, 4, size=(N, K), dtype=np.uint8)
+    x = rng.integers(wl.exp_lo, wl.exp_hi + 1, size=(N, K // AFFINE_GROUP), dtype=np.uint8)
+    fp4 = (codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    q2 = (codes[:, 0::4] | (codes[:, 1::4] << np.uint8(2)) | (codes[:, 2::4] << np.uint8(4))
+          | (codes[:, 3::4] << np.uint8(6))).astype(np.uint8)
+    return {"fp4_packed": fp4, "fp4_scale": np.repeat(x, 2, axis=1),
+            "q2_packed": q2, "q2_scale": ((x.astype(np.uint16) - 1) << np.uint16(7)).astype(np.uint16),
+            "q2_bias": np.zeros((N, K // AFFINE_GROUP), np.uint16)}
