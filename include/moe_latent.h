@@ -80,6 +80,12 @@ extern "C" {
 #define MOE_FN_SHARED_FFN 4
 #define MOE_FN_REAP_SALIENCY 5
 #define MOE_FN_COMBINE_NORM_UP_REAP 6
+#define MOE_FN_GROUPED_GEMM_TWO_BANK 7
+
+/* weight formats of an expert bank (moe_grouped_gemm_two_bank) */
+#define MOE_WF_MXFP4 0   /* e2m1 codes packed [E, N, K/2] (low nibble first), e8m0 scales u8 [E, N, K/32] */
+#define MOE_WF_AFFINE2 1 /* 2-bit codes packed [E, N, K/4] (element 4b+i in bits 2i..2i+1 of byte b),
+                            bf16 scales and biases [E, N, K/64]: w = scale * q + bias */
 
 typedef struct {
   int32_t hidden;       /* H: residual width (7168 for K3) */
@@ -229,6 +235,56 @@ int mxfp4_grouped_gemm(const moe_shape *shape, int op, int P, const int32_t *exp
                        const uint8_t *w_packed, const uint8_t *w_scale, const uint8_t *w3_packed,
                        const uint8_t *w3_scale, const float *pair_weight, float *C, void *ws,
                        size_t ws_bytes, void *stream);
+
+/* One bank of expert weights for moe_grouped_gemm_two_bank.  All pointers are
+ * device pointers; tensors are stacked over the bank's experts, its first
+ * expert at index 0.  MXFP4 banks: packed/scale as for mxfp4_grouped_gemm,
+ * bias NULL.  AFFINE2 banks: packed u8, scale and bias bf16 bits, all 16-byte
+ * aligned.  packed/scale/bias hold w1 (gate) for MOE_OP_GATEUP_SITU and w2
+ * (down) for MOE_OP_DOWN; packed3/scale3/bias3 hold w3 (up) for
+ * MOE_OP_GATEUP_SITU and are NULL for MOE_OP_DOWN. */
+typedef struct {
+  int32_t format;    /* MOE_WF_MXFP4 or MOE_WF_AFFINE2 */
+  int32_t n_experts; /* experts in the bank (may be 0) */
+  const uint8_t *packed;
+  const void *scale;
+  const uint16_t *bias;
+  const uint8_t *packed3;
+  const void *scale3;
+  const uint16_t *bias3;
+} moe_expert_bank;
+
+/* Grouped expert GEMM over one sorted pair list with the experts split into two
+ * weight banks.
+ * Follows: kimi-k3-mlx README, REAP section, graded-plan and two-bank
+ * paragraphs (the graded plan keeps the most salient experts in MXFP4 and
+ * stores the middle ones at a lower width; MLX holds one width per tensor, so
+ * the two widths sit in two banks; once the pairs are sorted by expert index,
+ * the bank that owns a contiguous range of expert indices owns a contiguous
+ * slice of the sorted rows, so each bank computes only its own rows; the
+ * split point depends on the routing), and Tiers section (the 2-bit affine
+ * tier: 2.50 bits per weight).
+ * Bank A owns experts 0 .. bank_a->n_experts - 1, bank B the rest
+ * (bank_a->n_experts + bank_b->n_experts == shape->n_experts).  The split point
+ * of the sorted rows, expert_offsets[bank_a->n_experts], is read on the device:
+ * no call waits on the host.  Every other argument, and the result, are as for
+ * mxfp4_grouped_gemm: with both banks in one format holding the same experts,
+ * H and Y equal mxfp4_grouped_gemm's bit for bit.
+ * Affine weights: the codes enter the bf16 MFMA as exact integers q, each
+ * 64-element group's fp32 partial sum is multiplied by that group's scale, and
+ * the bias part enters as the biases times the per-group sums of the
+ * activations in bf16 hi + lo.
+ * Limits (else MOE_ENOTSUP): operand modes BF16X2 and BF16 only; with an
+ * affine bank, K (latent for gate/up, inter for down) a multiple of 512 and at
+ * most 4096, and at decode-sized segments (P < 2 E) K >= 1536.
+ * Workspace: moe_workspace_bytes(shape, MOE_FN_GROUPED_GEMM_TWO_BANK, P).
+ * Errors: those of mxfp4_grouped_gemm; MOE_EINVAL for a null bank, an unknown
+ * format, expert counts that do not add up to n_experts, a missing or extra
+ * tensor for the format and op, or a misaligned tensor. */
+int moe_grouped_gemm_two_bank(const moe_shape *shape, int op, int P, const int32_t *expert_offsets,
+                              const int32_t *sorted_pair, const void *A, int a_rows, int a_dtype,
+                              const moe_expert_bank *bank_a, const moe_expert_bank *bank_b,
+                              const float *pair_weight, float *C, void *ws, size_t ws_bytes, void *stream);
 
 /* Weighted combine, RMSNorm on the combined latent, up projection.
  * Follows: kimi-k3-mlx README, REAP section caveat paragraph (RMSNorm is

@@ -18,11 +18,13 @@ MOE_OP_GATEUP_SITU, MOE_OP_DOWN = 0, 1
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_ROUTE_NOALLOC_SCRATCH_BYTES = 8 << 20
 (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP, MOE_FN_SHARED_FFN,
- MOE_FN_REAP_SALIENCY, MOE_FN_COMBINE_NORM_UP_REAP) = range(7)
+ MOE_FN_REAP_SALIENCY, MOE_FN_COMBINE_NORM_UP_REAP, MOE_FN_GROUPED_GEMM_TWO_BANK) = range(8)
+MOE_WF_MXFP4, MOE_WF_AFFINE2 = 0, 1
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute",
            "mxfp4_grouped_gemm", "moe_combine_norm_up", "shared_expert_ffn", "moe_reap_saliency",
-           "moe_combine_norm_up_reap", "moe_route_capped", "moe_route_noalloc")
+           "moe_combine_norm_up_reap", "moe_route_capped", "moe_route_noalloc",
+           "moe_grouped_gemm_two_bank")
 
 
 class MoeShape(ctypes.Structure):
@@ -31,6 +33,14 @@ class MoeShape(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32),
         ("shared_inter", ctypes.c_int32), ("beta", ctypes.c_float), ("beta_lin", ctypes.c_float),
         ("rms_eps", ctypes.c_float), ("operand_mode", ctypes.c_int32),
+    ]
+
+
+class MoeExpertBank(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+        ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("packed3", ctypes.c_void_p), ("scale3", ctypes.c_void_p), ("bias3", ctypes.c_void_p),
     ]
 
 
@@ -72,6 +82,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.shared_expert_ffn.argtypes = [sp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.moe_reap_saliency.restype = i32
     lib.moe_reap_saliency.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    bp = ctypes.POINTER(MoeExpertBank)
+    lib.moe_grouped_gemm_two_bank.restype = i32
+    lib.moe_grouped_gemm_two_bank.argtypes = [sp, i32, i32, vp, vp, vp, i32, i32, bp, bp, vp, vp, vp, sz, vp]
     lib.moe_route_noalloc.restype = i32
     lib.moe_route_noalloc.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_route_capped.restype = i32

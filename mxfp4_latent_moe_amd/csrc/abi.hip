@@ -98,6 +98,25 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
   return w;
 }
 
+// two-bank call: a chunk list and count per bank, then the split-K partials
+struct TwoBankWs {
+  size_t chunks[2], count[2], partial, total;
+  GemmPlan plan;
+};
+TwoBankWs two_bank_ws(const moe_shape *s, int P, bool gateup) {
+  TwoBankWs w{};
+  w.plan = gateup ? plan_grouped(P, s->n_experts, s->inter, s->latent, true)
+                  : plan_grouped(P, s->n_experts, s->latent, s->inter, false);
+  const size_t list = align_up((size_t)w.plan.max_chunks * 16);
+  w.chunks[0] = 0;
+  w.count[0] = list;
+  w.chunks[1] = w.count[0] + ALIGN;
+  w.count[1] = w.chunks[1] + list;
+  w.partial = w.count[1] + ALIGN;
+  w.total = w.partial + align_up(w.plan.partial_bytes);
+  return w;
+}
+
 // bf16 planes of fp32 activations for the dense tiled kernel (hi, then lo)
 size_t planes_bytes(const GemmPlan &pl, int rows, int K, int afmt) {
   if (pl.variant != 4 || afmt == A_BF16) return 0;
@@ -343,6 +362,10 @@ size_t moe_workspace_bytes(const moe_shape *s, int fn, int n) {
       return shared_ws(s, n).total;
     case MOE_FN_REAP_SALIENCY: return align_up((size_t)n * sizeof(float));
     case MOE_FN_COMBINE_NORM_UP_REAP: return combine_reap_ws(s, n);
+    case MOE_FN_GROUPED_GEMM_TWO_BANK: {
+      const size_t a = two_bank_ws(s, n, true).total, b = two_bank_ws(s, n, false).total;
+      return a > b ? a : b;
+    }
     default: return 0;
   }
 }
@@ -495,6 +518,134 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
       a.grid_logical = (int)pl.grid_logical;
     }
     if (launch_gemm(pl, W_MXFP4, afmt, gateup, a, st) != hipSuccess) return MOE_EHIP;
+    if (w.plan.splits > 1) {
+      FinalizeArgs f{};
+      f.partial = a.partial;
+      f.splits = w.plan.splits;
+      f.rows = P;
+      f.N = N;
+      f.pair = gateup ? 1 : 0;
+      f.C = C;
+      f.ldc = N;
+      f.accumulate = 0;
+      f.rscale = pair_weight;
+      f.rscale_map = pair_weight ? sorted_pair : nullptr;
+      f.beta = s->beta;
+      f.beta_lin = s->beta_lin;
+      if (launch_finalize(f, st) != hipSuccess) return MOE_EHIP;
+    }
+    return MOE_OK;
+  });
+}
+
+int moe_grouped_gemm_two_bank(const moe_shape *s, int op, int P, const int32_t *expert_offsets,
+                              const int32_t *sorted_pair, const void *A, int a_rows, int a_dtype,
+                              const moe_expert_bank *bank_a, const moe_expert_bank *bank_b,
+                              const float *pair_weight, float *C, void *ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() -> int {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (op != MOE_OP_GATEUP_SITU && op != MOE_OP_DOWN) return MOE_EINVAL;
+    if (a_dtype != MOE_DT_F32 && a_dtype != MOE_DT_BF16) return MOE_EINVAL;
+    if (P <= 0 || !expert_offsets || !A || !C || !ws || !bank_a || !bank_b) return MOE_EINVAL;
+    const bool gateup = op == MOE_OP_GATEUP_SITU;
+    const bool gathered = gateup && sorted_pair != nullptr;
+    if (a_rows < 1 || (!gathered && a_rows < P)) return MOE_EINVAL;
+    const int N = gateup ? s->inter : s->latent;
+    const int K = gateup ? s->latent : s->inter;
+    if (gathered && (long long)a_rows * K * (a_dtype == MOE_DT_BF16 ? 2 : 4) >= (1LL << 31)) return MOE_ENOTSUP;
+    if (gateup && pair_weight) return MOE_EINVAL;
+    if (pair_weight && !sorted_pair) return MOE_EINVAL;
+    if (!aligned16(A) || !aligned16(C) || !aligned16(ws)) return MOE_EINVAL;
+    const moe_expert_bank *banks[2] = {bank_a, bank_b};
+    bool any_affine = false;
+    for (const moe_expert_bank *b : banks) {
+      if (b->format != MOE_WF_MXFP4 && b->format != MOE_WF_AFFINE2) return MOE_EINVAL;
+      if (b->n_experts < 0) return MOE_EINVAL;
+      if (b->n_experts == 0) continue;
+      const bool aff = b->format == MOE_WF_AFFINE2;
+      any_affine |= aff;
+      if (!b->packed || !b->scale || (aff != (b->bias != nullptr))) return MOE_EINVAL;
+      if (gateup && (!b->packed3 || !b->scale3 || (aff != (b->bias3 != nullptr)))) return MOE_EINVAL;
+      if (!gateup && (b->packed3 || b->scale3 || b->bias3)) return MOE_EINVAL;
+      const uintptr_t salign = aff ? 15u : 3u;
+      if (!aligned16(b->packed) || (reinterpret_cast<uintptr_t>(b->scale) & salign) || (b->bias && !aligned16(b->bias)) ||
+          (b->packed3 && !aligned16(b->packed3)) || (b->scale3 && (reinterpret_cast<uintptr_t>(b->scale3) & salign)) ||
+          (b->bias3 && !aligned16(b->bias3)))
+        return MOE_EINVAL;
+    }
+    if ((long long)bank_a->n_experts + bank_b->n_experts != s->n_experts) return MOE_EINVAL;
+    // the affine path runs with bf16 operands, on rows whose 64-element groups
+    // come in whole 16-byte runs of biases
+    if (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16) return MOE_ENOTSUP;
+    const TwoBankWs w = two_bank_ws(s, P, gateup);
+    if (any_affine) {
+      if (K % 512 || K > 4096) return MOE_ENOTSUP;
+      // the decode kernel keeps an item's biases in flight across at most one item boundary
+      if (w.plan.variant != 2 && w.plan.variant != 3) return MOE_ENOTSUP;
+      if (w.plan.variant == 2 && K / 128 < 12) return MOE_ENOTSUP;
+    }
+    if (ws_bytes < w.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    GemmArgs a{};
+    a.A = A;
+    a.lda = K;
+    a.a_map = gathered ? sorted_pair : nullptr;
+    a.a_div = s->top_k;
+    a.a_rows = a_rows;
+    a.N = N;
+    a.K = K;
+    a.C = C;
+    a.ldc = N;
+    a.accumulate = 0;
+    a.rscale = pair_weight;
+    a.rscale_map = pair_weight ? sorted_pair : nullptr;
+    a.dense_rows = 0;
+    a.n_blocks = w.plan.n_blocks;
+    a.splits = w.plan.splits;
+    a.partial = reinterpret_cast<float *>(wsp(ws, w.partial));
+    a.partial_rows = P;
+    a.beta = s->beta;
+    a.beta_lin = s->beta_lin;
+    const int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
+    // bank A owns experts [0, E_a), bank B [E_a, E): each bank's chunks come from
+    // its slice of the offsets on the device, so its sorted rows are found with
+    // no host round trip
+    int e0 = 0;
+    for (int bi = 0; bi < 2; ++bi) {
+      const moe_expert_bank *b = banks[bi];
+      const int ne = b->n_experts;
+      if (ne == 0) continue;
+      const bool aff = b->format == MOE_WF_AFFINE2;
+      int32_t *chunks = reinterpret_cast<int32_t *>(wsp(ws, w.chunks[bi]));
+      int32_t *count = reinterpret_cast<int32_t *>(wsp(ws, w.count[bi]));
+      if (launch_plan_chunks(expert_offsets + e0, ne, w.plan.chunk_rows, chunks, count, st) != hipSuccess)
+        return MOE_EHIP;
+      GemmArgs ab = a;
+      ab.W0 = b->packed;
+      ab.W1 = b->packed3;
+      ab.S0 = static_cast<const uint8_t *>(b->scale);
+      ab.S1 = static_cast<const uint8_t *>(b->scale3);
+      ab.B0 = b->bias;
+      ab.B1 = b->bias3;
+      ab.w_estride = (long long)N * (K / (aff ? 4 : 2));
+      ab.s_estride = aff ? (long long)N * (K / 64) * 2 : (long long)N * (K / 32);
+      ab.chunks = chunks;
+      ab.chunk_count = count;
+      GemmPlan pl = w.plan;
+      if (pl.variant == 3) {
+        // the tiled kernel's affine variant covers fewer weight rows per work-group
+        const int rows_wg = prefill_rows_per_wg_fmt(gateup, aff ? W_AFF2 : W_MXFP4);
+        pl.n_blocks = (N + rows_wg - 1) / rows_wg;
+        ab.n_blocks = pl.n_blocks;
+      }
+      pl.max_chunks = P / pl.chunk_rows + (ne < P ? ne : P);
+      pl.grid_logical = (long long)pl.max_chunks * pl.n_blocks * pl.splits;
+      ab.grid_logical = (int)pl.grid_logical;
+      if (launch_gemm(pl, aff ? W_AFF2 : W_MXFP4, afmt, gateup, ab, st) != hipSuccess) return MOE_EHIP;
+      e0 += ne;
+    }
     if (w.plan.splits > 1) {
       FinalizeArgs f{};
       f.partial = a.partial;

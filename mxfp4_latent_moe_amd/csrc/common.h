@@ -46,6 +46,36 @@ MOE_DEV bf16x8_t fp4x8_to_bf16(uint32_t q, float scale) {
 
 MOE_DEV float e8m0_to_float(uint32_t e) { return __uint_as_float(e << 23); }
 
+// Affine 2-bit codes (element i of a dword in bits 2i .. 2i+1) as exact bf16
+// integers q through the fp4 convert: masked into the low half of a nibble,
+// code q reads as the e2m1 value q / 2, and the convert's scale 2 (a power of
+// two: the convert takes only the exponent of its scale) gives q.
+// y = d & 0x33333333 holds codes 4b and 4b+2 in byte b, z = (d >> 2) &
+// 0x33333333 codes 4b+1 and 4b+3.  Bytes B and B+1 of y and z give the eight
+// codes 4B .. 4B+7 in the order 0, 2, 1, 3, 4, 6, 5, 7 (relative to 4B); the
+// activations are staged in that same order, so the products pair up.
+template <int B>
+MOE_DEV bf16x8_t aff2x8_to_bf16(uint32_t y, uint32_t z) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y, 2.0f, B);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(z, 2.0f, B);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y, 2.0f, B + 1);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(z, 2.0f, B + 1);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+// Slot i of an octet of activations staged for affine weights holds element
+// aff2_perm(i) of the octet (the order aff2x8_to_bf16 produces).
+MOE_DEV constexpr int aff2_perm(int i) { return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1); }
+// Affine K layout of one 128-wide K step (two 64-element groups h): MFMA
+// instruction j = 2h + jj covers group h only; in it, lane group kg takes the
+// 8 elements 64h + 16kg + 8jj .. +7, i.e. half jj of the step's dword 4h + kg
+// of codes, and the activations of octet 8h + 2kg + jj.
+MOE_DEV constexpr int aff2_octet(int h, int kg, int jj) { return 8 * h + 2 * kg + jj; }
+// fp32 value of the bf16 in the low 16 bits of a pattern
+MOE_DEV float bf16_lo_to_float(uint32_t bits) { return __uint_as_float(bits << 16); }
+
 // tanh in fp32 from two identities: the odd Taylor series of tanh (Bernoulli-
 // number coefficients, terms to x^11) for |x| < 0.4, where the first omitted
 // term is below 1e-7 of the value, and tanh|x| = (1 - e) / (1 + e) with
@@ -90,6 +120,9 @@ MOE_DEV u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t sof
 }
 MOE_DEV uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+MOE_DEV u32x2_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
 
 // Work-item decode shared by the GEMM kernels.  The grid is sized for the

@@ -463,7 +463,7 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
 hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
                        hipStream_t st) {
   const long long grid = (pl.grid_logical + 7) / 8 * 8;
-  if (pl.variant == 2) return launch_grouped_stream(afmt, pair, a, st);
+  if (pl.variant == 2) return launch_grouped_stream(wfmt, afmt, pair, a, st);
   if (pl.variant == 3) return launch_prefill_gemm(wfmt, afmt, pair, a, grid, st);
   if (pl.variant == 4) {
     // activations arrive as bf16 planes (the caller splits fp32 ones)

@@ -8,7 +8,9 @@
 namespace moe {
 
 // weight formats, activation formats
-enum { W_BF16 = 0, W_MXFP4 = 1 };
+// W_AFF2: affine 2-bit codes [E][N][K/4] (element 4b + i in bits 2i..2i+1 of
+// byte b), bf16 scales and biases [E][N][K/64]: w = scale * q + bias
+enum { W_BF16 = 0, W_MXFP4 = 1, W_AFF2 = 2 };
 enum { A_BF16 = 0, A_F32_SPLIT = 1, A_F32_ROUND = 2, A_MX8X3 = 3, A_MX6X3 = 4 };
 
 // Weight-stationary GEMM: C[row, n] (+)= sum_k A[row, k] * W[n, k] over a
@@ -21,7 +23,8 @@ struct GemmArgs {
   int a_div;
   long long a_rows;       // rows of A (grouped calls; gathered reads stay below it)
   const void *W0, *W1;    // weights [E][N][K] bf16 or packed [E][N][K/2]; W1 for SiTU pairs
-  const uint8_t *S0, *S1; // e8m0 scales [E][N][K/32] (MXFP4)
+  const uint8_t *S0, *S1; // e8m0 scales [E][N][K/32] (MXFP4), bf16 scales [E][N][K/64] (W_AFF2)
+  const uint16_t *B0, *B1; // bf16 biases [E][N][K/64] (W_AFF2)
   long long w_estride;    // per-expert stride of W (elements for bf16, bytes for packed)
   long long s_estride;    // per-expert stride of S in bytes
   int N, K;
@@ -100,8 +103,9 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
 int stream_rows_per_wg(int wfmt, bool pair);
 int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
-hipError_t launch_grouped_stream(int afmt, bool pair, const GemmArgs &a, hipStream_t st);
+hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st);
 int prefill_rows_per_wg(bool pair);
+int prefill_rows_per_wg_fmt(bool pair, int wfmt);
 int prefill_mx_rows_per_wg(bool pair);
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st);

@@ -19,6 +19,8 @@
 // The item body is specialised on the number of active 16-token tiles, so the
 // K loop is straight-line code and token tiles past the chunk's last row cost
 // nothing.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +31,7 @@ constexpr int KSTEP = 128;
 
 // One work item with NTA active 16-token tiles (the K loop has no branches).
 template <int WF, int AF, bool PAIR, int NTA, int MT, int NW>
-__device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int expert, int row0,
+__device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, float *gsum, int expert, int row0,
                                         int nrows, int nb) {
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;  // LDS planes (hi, lo)
   constexpr int NMAT = PAIR ? 2 : 1;
@@ -53,22 +55,31 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   // ---- weight rows of this wave: buffer resources per matrix, offsets per tile.
   // MXFP4: lane group kg's 16 bytes of a 128-wide K step are its 32 codes (one
   // scale group); bf16: its 64 bytes (32 values), one 16-byte load per sub-step.
+  // Affine 2-bit weights: the codes enter the MFMA as exact integers, each
+  // instruction inside one 64-element group (aff2_octet: a lane loads dwords
+  // kg and 4 + kg of a step's codes); a group's two instructions sum into a
+  // temporary that is added times the group's scale of each output row, and
+  // the bias part is one more product at the end of the item.
   constexpr bool FP4 = WF == W_MXFP4;
-  static_assert(FP4, "MXFP4 weights only");
-  const uint32_t row_bytes = FP4 ? K / 2 : K * 2, srow_bytes = FP4 ? K / 32 : 0;
+  constexpr bool AFF = WF == W_AFF2;
+  static_assert(FP4 || AFF, "MXFP4 or affine 2-bit weights");
+  const int ngroups = K / 64;
+  const uint32_t row_bytes = FP4 ? K / 2 : K / 4, srow_bytes = FP4 ? K / 32 : ngroups * 2;
+  constexpr uint32_t STEP_BYTES = FP4 ? 64u : 32u;
+  typedef typename std::conditional<FP4, u32x4_t, u32x2_t>::type WQ;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) {
     const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0) + expert * g.w_estride;
     wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
-    if constexpr (FP4) sr[mat] = make_rsrc((mat ? g.S1 : g.S0) + expert * g.s_estride, (uint32_t)N * srow_bytes);
+    sr[mat] = make_rsrc((mat ? g.S1 : g.S0) + expert * g.s_estride, (uint32_t)N * srow_bytes);
   }
   const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
   uint32_t woff[NTILE], soff[NTILE];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
     const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
-    woff[t] = (uint32_t)n * row_bytes + kg * (FP4 ? 16 : 64);
+    woff[t] = (uint32_t)n * row_bytes + kg * (FP4 ? 16 : 4);
     soff[t] = (uint32_t)n * srow_bytes;
   }
 
@@ -92,7 +103,7 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     aoff[i] = (uint32_t)((arow * g.lda + a_oct * 8) * esz);
   }
 
-  u32x4_t wq[2][NTILE];    // codes of one K step per stage
+  WQ wq[2][NTILE];          // codes of one K step per stage
   uint32_t wsc[2][NTILE];
   u32x4_t aq[NPASS][AW];
 
@@ -101,7 +112,12 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     s = min(s, nks - 1);
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-      wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * 64u);
+      if constexpr (FP4) {
+        wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * STEP_BYTES);
+      } else {
+        wq[b][t] = u32x2_t{buf_load4(wr[t / MT], woff[t], (uint32_t)s * STEP_BYTES),
+                           buf_load4(wr[t / MT], woff[t] + 16u, (uint32_t)s * STEP_BYTES)};
+      }
       wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
     }
   };
@@ -116,31 +132,57 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
   };
   // swizzled LDS slot of (octet, token): octet-major, token XOR octet
   auto slot = [](int oct, int tok) { return (oct * CT + (tok ^ oct)) * 8; };
-  auto store_a = [&](int b) {
+  // step sa's activations into LDS stage b; for affine weights in the
+  // convert's element order, with each row's two 64-element group sums of the
+  // staged values written to gsum[group][row]
+  auto store_a = [&](int b, int sa) {
+    sa = min(sa, nks - 1);
 #pragma unroll
     for (int i = 0; i < NPASS; ++i) {
       const int r = (tid >> 4) + RPP * i;
-      if (CT % RPP != 0 && r >= CT) continue;
-      const int off = slot(a_oct, r);
+      float part = 0.f;
       if constexpr (AF == A_BF16) {
-        const u32x4_t v = alive[i] ? aq[i][0] : u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t *>(lds(b, 0) + off) = v;
+        u32x4_t v = alive[i] ? aq[i][0] : u32x4_t{0, 0, 0, 0};
+        if constexpr (AFF) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            part += __uint_as_float(v[h] << 16) + __uint_as_float(v[h] & 0xFFFF0000u);
+#pragma unroll
+          for (int h = 0; h < 4; h += 2) {  // bf16 elements 0..7 -> 0, 2, 1, 3, 4, 6, 5, 7
+            const uint32_t a0 = v[h], a1 = v[h + 1];
+            v[h] = (a0 & 0xFFFFu) | (a1 << 16);
+            v[h + 1] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+          }
+        }
+        if (CT % RPP == 0 || r < CT) *reinterpret_cast<u32x4_t *>(lds(b, 0) + slot(a_oct, r)) = v;
       } else {
         bf16x8_t hi, lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e0 = 0; e0 < 8; ++e0) {
+          const int e = AFF ? aff2_perm(e0) : e0;  // slot e0 holds element e
           const float f = alive[i] ? __uint_as_float(aq[i][e >> 2][e & 3]) : 0.f;
           if constexpr (AF == A_F32_SPLIT) {
             __bf16 h, l;
             split_bf16(f, h, l);
-            hi[e] = h;
-            lo[e] = l;
+            hi[e0] = h;
+            lo[e0] = l;
+            part += f;
           } else {
-            hi[e] = to_bf16(f);
+            hi[e0] = to_bf16(f);
+            part += from_bf16(hi[e0]);
           }
         }
-        *reinterpret_cast<bf16x8_t *>(lds(b, 0) + off) = hi;
-        if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(lds(b, NPL - 1) + off) = lo;
+        if (CT % RPP == 0 || r < CT) {
+          *reinterpret_cast<bf16x8_t *>(lds(b, 0) + slot(a_oct, r)) = hi;
+          if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(lds(b, NPL - 1) + slot(a_oct, r)) = lo;
+        }
+      }
+      if constexpr (AFF) {
+        // the eight octets of a group sit in lanes a_oct ^ 1, 2, 4 of the same row
+        part += __shfl_xor(part, 1, 64);
+        part += __shfl_xor(part, 2, 64);
+        part += __shfl_xor(part, 4, 64);
+        if ((a_oct & 7) == 0 && (CT % RPP == 0 || r < CT)) gsum[(2 * sa + (a_oct >> 3)) * CT + r] = part;
       }
     }
   };
@@ -186,19 +228,66 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     // let the scheduler interleave the LDS reads with the MFMAs of this region
     __builtin_amdgcn_iglp_opt(0);
   };
+  // affine weights: one K step, group by group
+  auto compute_aff = [&](int b, int s) {
+    (void)s;
+    float sc[NTILE][2][4];  // group scales of the lane's output rows 4 kg + r
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t sw = (uint32_t)__shfl((int)wsc[b][t], 4 * kg + r, 64);
+        sc[t][0][r] = bf16_lo_to_float(sw);
+        sc[t][1][r] = bf16_lo_to_float(sw >> 16);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4_t tmp[NTILE][NTA];
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+        for (int n = 0; n < NTA; ++n) tmp[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        bf16x8_t wa[NTILE];
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+          const uint32_t d = wq[b][t][h];
+          const uint32_t y = d & 0x33333333u, z = (d >> 2) & 0x33333333u;
+          wa[t] = jj ? aff2x8_to_bf16<2>(y, z) : aff2x8_to_bf16<0>(y, z);
+        }
+#pragma unroll
+        for (int p = 0; p < NPL; ++p)
+#pragma unroll
+          for (int n = 0; n < NTA; ++n) {
+            const bf16x8_t bq =
+                *reinterpret_cast<const bf16x8_t *>(lds(b, p) + slot(aff2_octet(h, kg, jj), 16 * n + r16));
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) tmp[t][n] = mfma_16x16x32(wa[t], bq, tmp[t][n]);
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+        for (int n = 0; n < NTA; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][n][r] = fmaf(sc[t][h][r], tmp[t][n][r], acc[t][n][r]);
+    }
+  };
   // one K step: activations of s+1 and weights of s+2 are requested while s computes
   auto step = [&](int h, int s) {
     load_a(s + 1);
-    compute(h, s);
+    if constexpr (AFF) compute_aff(h, s);
+    else compute(h, s);
     load_w(h, s + 2);
-    store_a(h ^ 1);
+    store_a(h ^ 1, s + 1);
     __syncthreads();
   };
 
   load_w(0, 0);
   load_a(0);
   load_w(1, 1);
-  store_a(0);
+  store_a(0, 0);
   __syncthreads();
   int s = 0;
   for (; s + 1 < nks; s += 2) {
@@ -206,6 +295,45 @@ __device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, int
     step(1, s + 1);
   }
   if (s < nks) step(0, s);
+
+  if constexpr (AFF) {
+    // the bias part sum_g b_g sum_{k in g} a_k: the biases of the lane's row,
+    // eight groups per slice (M side), against the rows' group sums in hi + lo
+    // (N side); groups past the row's end contribute zero
+    bf16x8_t bw[NTILE][2];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const __amdgpu_buffer_rsrc_t br =
+          make_rsrc((t / MT ? g.B1 : g.B0) + expert * (g.s_estride / 2), (uint32_t)N * srow_bytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g0 = 8 * kg + 32 * i;
+        const u32x4_t v = g0 < ngroups ? buf_load16(br, soff[t] + 2 * g0, 0) : u32x4_t{0, 0, 0, 0};
+        bw[t][i] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        bf16x8_t sh, sl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int grp = 32 * i + 8 * kg + e;
+          const float v = grp < ngroups ? gsum[grp * CT + 16 * n + r16] : 0.f;
+          __bf16 h, l;
+          split_bf16(v, h, l);
+          sh[e] = h;
+          sl[e] = l;
+        }
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+          acc[t][n] = mfma_16x16x32(bw[t][i], sh, acc[t][n]);
+          acc[t][n] = mfma_16x16x32(bw[t][i], sl, acc[t][n]);
+        }
+      }
+    }
+  }
 
   // ---- epilogue: SiTU-GLU of the gate/up pair (or the plain product), row scale, store
   const int col_base = wrow_base + 4 * kg;
@@ -246,6 +374,8 @@ template <int WF, int AF, bool PAIR, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(GemmArgs g) {
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * NPL * 16 * NT * KSTEP];
+  // affine weights: 64-element group sums of the chunk's rows [64 groups][rows]
+  __shared__ float gsum[WF == W_AFF2 ? 64 * 16 * NT : 1];
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
 
   // ---- work item (XCD-aware over the items that exist on the device): expert
@@ -260,15 +390,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(GemmArgs g) {
   const int expert = c.x, row0 = c.y, nrows = c.z;
   const int nta = min((nrows + 15) >> 4, NT);  // active 16-token tiles
   if (nta == NT) {
-    pf_item<WF, AF, PAIR, NT, MT, NW>(g, lds, expert, row0, nrows, nb);
+    pf_item<WF, AF, PAIR, NT, MT, NW>(g, lds, gsum, expert, row0, nrows, nb);
     return;
   }
   switch (nta) {
-    case 1: if constexpr (NT > 1) pf_item<WF, AF, PAIR, 1, MT, NW>(g, lds, expert, row0, nrows, nb); break;
-    case 2: if constexpr (NT > 2) pf_item<WF, AF, PAIR, 2, MT, NW>(g, lds, expert, row0, nrows, nb); break;
-    case 3: if constexpr (NT > 3) pf_item<WF, AF, PAIR, 3, MT, NW>(g, lds, expert, row0, nrows, nb); break;
-    case 4: if constexpr (NT > 4) pf_item<WF, AF, PAIR, 4, MT, NW>(g, lds, expert, row0, nrows, nb); break;
-    default: if constexpr (NT > 5) pf_item<WF, AF, PAIR, 5, MT, NW>(g, lds, expert, row0, nrows, nb); break;
+    case 1: if constexpr (NT > 1) pf_item<WF, AF, PAIR, 1, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
+    case 2: if constexpr (NT > 2) pf_item<WF, AF, PAIR, 2, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
+    case 3: if constexpr (NT > 3) pf_item<WF, AF, PAIR, 3, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
+    case 4: if constexpr (NT > 4) pf_item<WF, AF, PAIR, 4, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
+    default: if constexpr (NT > 5) pf_item<WF, AF, PAIR, 5, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
   }
 }
 
@@ -690,9 +820,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   }
 }
 
+// 16-row weight tiles per wave and matrix: affine weights keep a temporary
+// accumulator per tile beside the result, so their waves hold half the tiles
+constexpr int pf_mt(int wf, bool pair) {
+  return wf == W_AFF2 ? (pair ? PREFILL_MT_PAIR / 2 : PREFILL_MT_SINGLE / 2) : (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE);
+}
+
 template <int WF, int AF, bool PAIR>
 hipError_t launch_pf(const GemmArgs &a, long long grid, hipStream_t st) {
-  constexpr int MT = PAIR ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE;
+  constexpr int MT = pf_mt(WF, PAIR);
   hipLaunchKernelGGL((prefill_kernel<WF, AF, PAIR, PREFILL_NT, MT, PREFILL_NW>), dim3((unsigned)grid),
                      dim3(64 * PREFILL_NW), 0, st, a);
   return hipGetLastError();
@@ -712,6 +848,7 @@ hipError_t launch_wf(int afmt, bool pair, const GemmArgs &a, long long grid, hip
 }  // namespace
 
 int prefill_rows_per_wg(bool pair) { return 16 * PREFILL_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
+int prefill_rows_per_wg_fmt(bool pair, int wfmt) { return 16 * PREFILL_NW * pf_mt(wfmt, pair); }
 int prefill_mx_rows_per_wg(bool pair) { return 16 * PREFILL_MX_NW * (pair ? PREFILL_MX_MT_PAIR : PREFILL_MX_MT_SINGLE); }
 
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
@@ -729,7 +866,9 @@ hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a,
     }
     return hipGetLastError();
   }
-  if (wfmt != W_MXFP4 || a.chunks == nullptr) return hipErrorInvalidValue;  // expert segments only
+  if (a.chunks == nullptr) return hipErrorInvalidValue;  // expert segments only
+  if (wfmt == W_AFF2) return launch_wf<W_AFF2>(afmt, pair, a, grid, st);
+  if (wfmt != W_MXFP4) return hipErrorInvalidValue;
   return launch_wf<W_MXFP4>(afmt, pair, a, grid, st);
 }
 

@@ -61,6 +61,30 @@ def grouped_gemm(shape, op, P, offsets, sorted_pair, A, w_packed, w_scale, w3_pa
                                     _p(pair_weight), _p(C), _p(ws), ws.numel(), _s(stream)))
 
 
+def expert_bank(fmt, n_experts, tensors, op):
+    """moe_expert_bank for `op` from {w1,w3,w2}_{packed,scale[,bias]} tensors (stacked over the bank)."""
+    mats = ("w1", "w3") if op == MOE_OP_GATEUP_SITU else ("w2", None)
+    b = _lib.MoeExpertBank()
+    b.format, b.n_experts = int(fmt), int(n_experts)
+    if n_experts == 0:
+        return b
+    aff = fmt == _lib.MOE_WF_AFFINE2
+    b.packed, b.scale = _p(tensors[mats[0] + "_packed"]), _p(tensors[mats[0] + "_scale"])
+    b.bias = _p(tensors[mats[0] + "_bias"]) if aff else None
+    if mats[1]:
+        b.packed3, b.scale3 = _p(tensors[mats[1] + "_packed"]), _p(tensors[mats[1] + "_scale"])
+        b.bias3 = _p(tensors[mats[1] + "_bias"]) if aff else None
+    return b
+
+
+def grouped_gemm_two_bank(shape, op, P, offsets, sorted_pair, A, bank_a, bank_b, pair_weight, C, ws, stream=None):
+    """moe_grouped_gemm_two_bank; bank_a / bank_b are moe_expert_bank structs (see expert_bank)."""
+    a_dtype = MOE_DT_BF16 if A.dtype in (torch.bfloat16, torch.int16, torch.uint16) else MOE_DT_F32
+    check("moe_grouped_gemm_two_bank",
+          load().moe_grouped_gemm_two_bank(shape, op, P, _p(offsets), _p(sorted_pair), _p(A), A.shape[0], a_dtype,
+                                           bank_a, bank_b, _p(pair_weight), _p(C), _p(ws), ws.numel(), _s(stream)))
+
+
 def combine_norm_up(shape, T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, ws, stream=None):
     check("moe_combine_norm_up",
           load().moe_combine_norm_up(shape, T, _p(Y), _p(pair_pos), _p(topk_w), _p(gamma), _p(w_up),
@@ -121,12 +145,22 @@ class LatentMoE:
     """
 
     def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True,
-                 latent_on_side: bool = True, late_shared_join: bool = True):
+                 latent_on_side: bool = True, late_shared_join: bool = True, bank_b: dict | None = None):
         missing = [k for k in WEIGHT_KEYS if k not in weights]
         if missing:
             raise ValueError(f"missing weights: {missing}")
         self.shape = shape
         self.w = weights
+        # two-bank layer: the w1/w3/w2 tensors hold bank A (the first n_a experts,
+        # MXFP4) and bank_b = {"format": MOE_WF_*, "n_experts": n_b, tensors...}
+        # holds the rest; the expert GEMMs then run moe_grouped_gemm_two_bank
+        self.bank_b = bank_b
+        if bank_b is not None:
+            n_b = int(bank_b["n_experts"])
+            n_a = shape.n_experts - n_b
+            self._banks = {op: (expert_bank(_lib.MOE_WF_MXFP4, n_a, weights, op),
+                                expert_bank(bank_b["format"], n_b, bank_b, op))
+                           for op in (MOE_OP_GATEUP_SITU, MOE_OP_DOWN)}
         self.device = torch.device(device)
         self._bufs: dict = {}
         self.overlap_shared = overlap_shared
@@ -147,8 +181,9 @@ class LatentMoE:
             return self._bufs[T]
         s, dev = self.shape, self.device
         P = T * s.top_k
-        ws = max(workspace_bytes(s, fn, P if fn == MOE_FN_GROUPED_GEMM else T)
-                 for fn in (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP))
+        gfn = _lib.MOE_FN_GROUPED_GEMM_TWO_BANK if self.bank_b is not None else MOE_FN_GROUPED_GEMM
+        ws = max(workspace_bytes(s, fn, P if fn == gfn else T)
+                 for fn in (MOE_FN_ROUTE, MOE_FN_PERMUTE, gfn, MOE_FN_COMBINE_NORM_UP))
         ws_sh = max(16, workspace_bytes(s, MOE_FN_SHARED_FFN, T), workspace_bytes(s, MOE_FN_ROUTE, T))
         i32, f32 = torch.int32, torch.float32
         b = {
@@ -230,13 +265,23 @@ class LatentMoE:
                 st.wait_event(side_done)
             elif z_done is not None:
                 st.wait_event(z_done)
-        call("grouped_gemm_gateup", st,
-             lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"],
-                                  w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"],
-                                  ws, st))
-        call("grouped_gemm_down", st,
-             lambda: grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
-                                  w["w2_scale"], None, None, None, b["Y"], ws, st))
+        if self.bank_b is not None:
+            ga, gb = self._banks[MOE_OP_GATEUP_SITU]
+            da, db = self._banks[MOE_OP_DOWN]
+            call("grouped_gemm_gateup", st,
+                 lambda: grouped_gemm_two_bank(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"], ga,
+                                               gb, None, b["H"], ws, st))
+            call("grouped_gemm_down", st,
+                 lambda: grouped_gemm_two_bank(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], da, db,
+                                               None, b["Y"], ws, st))
+        else:
+            call("grouped_gemm_gateup", st,
+                 lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"],
+                                      w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"],
+                                      ws, st))
+            call("grouped_gemm_down", st,
+                 lambda: grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
+                                      w["w2_scale"], None, None, None, b["Y"], ws, st))
         if shared and side is not st and late:
             st.wait_event(side_done)
         call("moe_combine_norm_up", st,

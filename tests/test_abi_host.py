@@ -60,9 +60,9 @@ def _shape(**kw):
 
 def test_workspace_bytes(lib):
     s = _shape()
-    for fn in range(7):
+    for fn in range(8):
         assert lib.moe_workspace_bytes(s, fn, 16) > 0
-    assert lib.moe_workspace_bytes(s, 7, 16) == 0
+    assert lib.moe_workspace_bytes(s, 8, 16) == 0
     # the fused combine needs the combine's workspace plus one fp32 per pair
     assert (lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP_REAP, 16)
             >= lib.moe_workspace_bytes(s, _lib.MOE_FN_COMBINE_NORM_UP, 16) + 16 * s.top_k * 4)
@@ -242,3 +242,41 @@ def test_route_noalloc_validation(lib):
     assert lib.moe_route_noalloc(s, 65, *args) == _lib.MOE_EWORKSPACE
     assert lib.moe_route_noalloc(s, 0, *args) == _lib.MOE_EINVAL
     assert lib.moe_route_noalloc(None, 16, *args) == _lib.MOE_EINVAL
+
+
+def test_two_bank_validation(lib):
+    """The two-bank call checks banks, formats, expert counts and limits before any device work."""
+    s = _shape()
+    P = 256
+    ws = lib.moe_workspace_bytes(s, _lib.MOE_FN_GROUPED_GEMM_TWO_BANK, P)
+    assert ws >= lib.moe_workspace_bytes(s, _lib.MOE_FN_GROUPED_GEMM, P)
+    G, D = _lib.MOE_OP_GATEUP_SITU, _lib.MOE_OP_DOWN
+    f32 = _lib.MOE_DT_F32
+
+    def bank(fmt, n, op=G, bias=True, up=True):
+        b = _lib.MoeExpertBank()
+        b.format, b.n_experts = fmt, n
+        b.packed, b.scale = FAKE, FAKE
+        aff = fmt == _lib.MOE_WF_AFFINE2
+        b.bias = FAKE if (aff and bias) else None
+        if op == G and up:
+            b.packed3, b.scale3 = FAKE, FAKE
+            b.bias3 = FAKE if (aff and bias) else None
+        return b
+
+    def call(ba, bb, op=G, sp=FAKE, ar=P // 16, wsb=ws, shape=s):
+        return lib.moe_grouped_gemm_two_bank(shape, op, P, FAKE, sp, FAKE, ar, f32, ctypes.byref(ba),
+                                             ctypes.byref(bb), None, FAKE, FAKE, wsb, None)
+
+    M, A2 = _lib.MOE_WF_MXFP4, _lib.MOE_WF_AFFINE2
+    assert call(bank(M, 500), bank(A2, 395)) == _lib.MOE_EINVAL          # 895 != 896 experts
+    assert call(bank(M, 500), bank(7, 396)) == _lib.MOE_EINVAL           # unknown format
+    assert call(bank(M, 500), bank(A2, 396, bias=False)) == _lib.MOE_EINVAL  # affine needs biases
+    assert call(bank(M, 500), bank(A2, 396, up=False)) == _lib.MOE_EINVAL    # gate/up needs the up bank
+    assert call(bank(M, 500, op=D), bank(A2, 396, op=G), op=D) == _lib.MOE_EINVAL  # down takes no up tensors
+    assert call(bank(M, 500), bank(A2, 396), wsb=ws - 1) == _lib.MOE_EWORKSPACE
+    assert call(bank(M, 896), bank(A2, 0), wsb=ws - 1) == _lib.MOE_EWORKSPACE   # an empty bank is fine
+    mx = _shape(operand_mode=_lib.MOE_OPND_MX6X3)
+    assert call(bank(M, 500), bank(A2, 396), shape=mx) == _lib.MOE_ENOTSUP  # bf16 operand modes only
+    small_k = _shape(latent=1152, hidden=1152)  # 1152 is not a multiple of 512
+    assert call(bank(M, 500), bank(A2, 396), shape=small_k) == _lib.MOE_ENOTSUP
