@@ -109,7 +109,8 @@ def _pct(v, q):
 DOMINANT = "grouped_gemm_gateup"
 
 
-def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, breakdown_steps=10, operand_mode=0):
+def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, breakdown_steps=10, operand_mode=0,
+                 bank_bs=None):
     """Step i runs layer i % len(layers): consecutive steps read different
     weight copies, as consecutive layers of the model do, so no step finds the
     previous step's weights in the last-level cache.
@@ -120,7 +121,14 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, brea
     from synth.device import upload_tokens
     dev = torch.device("cuda:0")
     sh = wl.shape
-    moes = [mx.LatentMoE(mx.shape_of(sh, operand_mode), w, dev) for w in layers]
+    if bank_bs is None:
+        moes = [mx.LatentMoE(mx.shape_of(sh, operand_mode), w, dev) for w in layers]
+    else:
+        # two-bank layers: the MXFP4 tensors of the first E - n_b experts, then bank B
+        n_a = sh.n_experts - int(bank_bs[0]["n_experts"])
+        moes = [mx.LatentMoE(mx.shape_of(sh, operand_mode),
+                             {k: (v[:n_a] if k[:2] in ("w1", "w3", "w2") else v) for k, v in w.items()}, dev,
+                             bank_b=bb) for w, bb in zip(layers, bank_bs)]
     x = upload_tokens(wl, dev)
     for i in range(warmup):
         moes[i % len(moes)].forward(x)
@@ -149,7 +157,8 @@ def run_workload(mx, torch, synth, layers, wl, steps, warmup, cold_steps=0, brea
         spans.append(_span(marks))
     b = moes[0].buffers(wl.tokens)
     e_act = int(b["active"][0].item())
-    r = {"wall_s": wall, "per_call_ms": per_call, "e_act": e_act, "T": wl.tokens,
+    active_ids = b["active"][1:1 + e_act].cpu().numpy()
+    r = {"wall_s": wall, "per_call_ms": per_call, "e_act": e_act, "T": wl.tokens, "active_ids": active_ids,
          "dominant_ms": float(np.mean(dom_ms)), "down_ms": float(np.mean(down_ms)),
          "step_ms": {"median": _pct(spans, 50), "p10": _pct(spans, 10), "p90": _pct(spans, 90)}}
     if cold_steps > 0:
@@ -462,6 +471,55 @@ def _layer_flops(sh, T):
                       + 2 * sh.latent * sh.hidden + 3 * sh.n_shared * sh.shared_inter * sh.hidden)
 
 
+TWO_BANK_A = 504  # MXFP4 experts of the two-bank layer; the other 392 are affine 2-bit (82% of the expert bytes)
+
+
+def _affine_expert_bytes(sh) -> int:
+    """Codes plus bf16 scales and biases of one affine 2-bit expert (w1, w3, w2)."""
+    per = lambda n, k: n * k // 4 + 2 * n * (k // 64) * 2  # noqa: E731
+    return 2 * per(sh.inter, sh.latent) + per(sh.latent, sh.inter)
+
+
+def run_two_bank(mx, torch, synth, layers):
+    """The two-bank layer (experts 0..503 MXFP4, 504..895 affine 2-bit with
+    seeded codes, scales and biases) against the single MXFP4 bank, at decode
+    T = 16 and prefill T = 4096, each pair of runs back to back on the same
+    rotated weight copies; the split point stays on the device."""
+    from mxfp4_latent_moe_amd import _lib
+    dev = torch.device("cuda:0")
+    sh = synth.K3_SHAPE
+    n_b = sh.n_experts - TWO_BANK_A
+    wl = synth.workload("decode")
+    aff = synth.gen_expert_affine2_stack(wl, range(TWO_BANK_A, sh.n_experts))
+    b0 = {k: torch.from_numpy(v).to(dev) for k, v in aff.items()}
+    del aff
+    banks = [dict(b0, format=_lib.MOE_WF_AFFINE2, n_experts=n_b)]
+    banks += [dict({k: v.clone() for k, v in b0.items()}, format=_lib.MOE_WF_AFFINE2, n_experts=n_b)
+              for _ in range(len(layers) - 1)]
+    eb_a, eb_b = _expert_bytes(sh), _affine_expert_bytes(sh)
+    out = {"workload": f"two-bank layer, experts 0..{TWO_BANK_A - 1} MXFP4 and {TWO_BANK_A}..{sh.n_experts - 1} "
+                       f"affine 2-bit (group 64, bf16 scale and bias), full K3 shapes",
+           "expert_bytes_ratio_all_experts": round((TWO_BANK_A * eb_a + n_b * eb_b) / (sh.n_experts * eb_a), 4)}
+    for name, steps in (("decode", 100), ("prefill", PREFILL_STEPS)):
+        w_l = synth.workload(name)
+        r1 = run_workload(mx, torch, synth, layers, w_l, steps, 5, breakdown_steps=5)
+        r2 = run_workload(mx, torch, synth, layers, w_l, steps, 5, breakdown_steps=5, bank_bs=banks)
+        ms1, ms2 = 1e3 * r1["wall_s"] / steps, 1e3 * r2["wall_s"] / steps
+        ids = r2["active_ids"]
+        bytes2 = int((ids < TWO_BANK_A).sum()) * eb_a + int((ids >= TWO_BANK_A).sum()) * eb_b
+        bytes1 = r1["e_act"] * eb_a
+        g1, g2 = r1["dominant_ms"] + r1["down_ms"], r2["dominant_ms"] + r2["down_ms"]
+        out[name] = {"tokens": w_l.tokens, "steps": steps,
+                     "single_bank_ms": round(ms1, 4), "two_bank_ms": round(ms2, 4),
+                     "two_bank_over_single": round(ms2 / ms1, 4),
+                     "grouped_gemm_ms_single": round(g1, 4), "grouped_gemm_ms_two_bank": round(g2, 4),
+                     "expert_bytes_single": bytes1, "expert_bytes_two_bank": bytes2,
+                     "expert_gb_per_s_single": round(bytes1 / (g1 * 1e-3) / 1e9, 1),
+                     "expert_gb_per_s_two_bank": round(bytes2 / (g2 * 1e-3) / 1e9, 1)}
+    del banks, b0
+    return out
+
+
 def prefill_line(mx, torch, synth, layers, pf, mode, label):
     """Prefill T=4096 in one operand mode: tokens/s, the layer's algorithmic
     TFLOP/s against bf16 peak, and the expert GEMMs against the peak of the
@@ -701,6 +759,8 @@ def main():
             line[key] = prefill_line(mx, torch, synth, layers, pf, mode, label)
         print("bench: timing the grouped-GEMM microbenchmark", file=sys.stderr, flush=True)
         line["secondary_microbench"] = run_microbench(mx, torch, synth, layers[0])
+        print("bench: timing the two-bank layer", file=sys.stderr, flush=True)
+        line["secondary_two_bank"] = run_two_bank(mx, torch, synth, layers)
         print("bench: timing the layer-0 dense FFN", file=sys.stderr, flush=True)
         line["secondary_dense_ffn"] = run_dense_ffn(mx, torch, synth)
         print("bench: timing the REAP saliency pass", file=sys.stderr, flush=True)

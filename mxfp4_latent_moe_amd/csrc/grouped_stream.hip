@@ -16,18 +16,6 @@
 // fp4 -> bf16 instruction and fed to MFMA 16x16x32 bf16 as the M side; the
 // tokens are the N side.  Scales are read 16 bytes at a time (four K steps of
 // one row); the kernel takes rows whose K steps come in groups of four.
-//
-// Affine 2-bit weights (w = s q + b per 64-element group): the codes enter
-// the MFMA as exact integers q (aff2x8_to_bf16), laid out so that each MFMA
-// instruction stays inside one group (aff2_octet): a lane loads two dwords of
-// codes per K step, one per group.  The two instructions of a group sum into
-// a temporary accumulator, which is added to the result times the group's
-// scale of each output row (the four rows' scale dwords come from the lanes
-// that loaded them).  The bias part sum_g b_g sum_{k in g} a_k is one more
-// product per item: the biases of the lane's row (8 groups per lane, the M
-// side) against the per-group sums of the staged activation rows (hi + lo,
-// the N side).  Activations are staged in the convert's element order.  The
-// biases of an item are requested with its first weight group.
 #include <atomic>
 #include <type_traits>
 
@@ -41,7 +29,7 @@ constexpr int KSTEP = 128;
 constexpr int R = PERSIST_ROWS;
 constexpr int KSMAX = STREAM_GROUPED_KSMAX;
 
-template <int WF, int AF, bool PAIR, int MT, int AHEAD, int NW>
+template <int AF, bool PAIR, int MT, int AHEAD, int NW>
 __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   constexpr int D = 4;  // K steps per group: one 16-byte read of scales covers four steps
   constexpr int NMAT = PAIR ? 2 : 1;
@@ -50,11 +38,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   constexpr int ROWS_WG = 16 * NW * MT;
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
   constexpr int STEP = 16 * R * 8;  // bf16 elements per K step per plane: [octet][row][8]
-  constexpr bool AFF = WF == W_AFF2;
-  constexpr int SUMS = 2 * 4 * R * 8;  // per-group activation sums: [slice][octet][row][8] (64 groups)
   __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
-  __shared__ __attribute__((aligned(16))) __bf16 sums[2][AFF ? SUMS : 8];
-  typedef typename std::conditional<AFF, u32x2_t, u32x4_t>::type WQ;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -63,10 +47,8 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   const int r16 = lane & 15;
   const int N = g.N, K = g.K;
   const int nks = K / KSTEP;
-  const int ngroups = K / 64;  // affine groups of a row
-  const uint32_t row_bytes = AFF ? K / 4 : K / 2;
-  const uint32_t srow_bytes = AFF ? ngroups * 2 : K / 32;
-  constexpr uint32_t STEP_BYTES = AFF ? 32u : 64u;  // codes of one row per K step
+  const uint32_t row_bytes = K / 2;
+  const uint32_t srow_bytes = K / 32;
 
   const int n_items = *g.chunk_count * g.n_blocks;
   const int G = gridDim.x;
@@ -83,9 +65,6 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   int l_item = i_begin, l_q = 0;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
   uint32_t woff[NTILE], soff[NTILE];
-  // affine biases of an item, 8 groups per lane and slice (groups 8 kg + 32 i),
-  // in one of two slots by item parity: the load cursor runs at most one item ahead
-  u32x4_t bq[2][NTILE][2];
   auto set_load_item = [&](int it) {
     const int c = __builtin_amdgcn_readfirstlane(it / g.n_blocks);
     const int nb = it - c * g.n_blocks;
@@ -100,30 +79,14 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       const int n = min(nb * ROWS_WG + wave * 16 * MT + (t % MT) * 16 + r16, N - 1);
-      woff[t] = (uint32_t)n * row_bytes + kg * (AFF ? 4 : 16);
+      woff[t] = (uint32_t)n * row_bytes + kg * 16;
       soff[t] = (uint32_t)n * srow_bytes;
-    }
-    if constexpr (AFF) {
-#pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat) {
-        const __amdgpu_buffer_rsrc_t br =
-            make_rsrc((mat ? g.B1 : g.B0) + expert * (g.s_estride / 2), (uint32_t)N * srow_bytes);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const int t = mat * MT + m;
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int g0 = 8 * kg + 32 * i;
-            bq[it & 1][t][i] = g0 < ngroups ? buf_load16(br, soff[t] + 2 * g0, 0) : u32x4_t{0, 0, 0, 0};
-          }
-        }
-      }
     }
   };
   set_load_item(i_begin);
 
   // wq[0] / scg[0]: the group being computed; [1..AHEAD]: groups requested ahead
-  WQ wq[AHEAD + 1][D][NTILE];
+  u32x4_t wq[AHEAD + 1][D][NTILE];
   u32x4_t scg[AHEAD + 1][NTILE];
   // Request one whole group -- D consecutive K steps of every tile, one burst
   // of 4 x 64 contiguous bytes per weight row, then its 16 scale bytes -- into
@@ -135,15 +98,8 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) {
-        const uint32_t vo = live ? woff[t] : 0u, so = live ? (uint32_t)(l_q + d) * STEP_BYTES : 0u;
-        if constexpr (AFF) {
-          // dwords kg (group 0) and 4 + kg (group 1) of the step's codes
-          wq[bi][d][t] = u32x2_t{buf_load4(wr[t / MT], vo, so), buf_load4(wr[t / MT], vo + 16u, so)};
-        } else {
-          wq[bi][d][t] = buf_load16(wr[t / MT], vo, so);
-        }
-      }
+      for (int t = 0; t < NTILE; ++t)
+        wq[bi][d][t] = buf_load16(wr[t / MT], live ? woff[t] : 0u, live ? (uint32_t)(l_q + d) * 64u : 0u);
 #pragma unroll
     for (int t = 0; t < NTILE; ++t)
       scg[bi][t] = buf_load16(sr[t / MT], live ? soff[t] : 0u, live ? (uint32_t)l_q * 4u : 0u);
@@ -196,30 +152,19 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
       for (int ii = 0; ii < SG; ++ii) {
         if (aoff[ii] < 0) continue;
         if constexpr (AF == A_BF16) {
-          u32x4_t v = araw[ii][0];
-          if constexpr (AFF) {
-            // bf16 elements 0..7 -> 0, 2, 1, 3, 4, 6, 5, 7
-#pragma unroll
-            for (int h = 0; h < 4; h += 2) {
-              const uint32_t a = v[h], b = v[h + 1];
-              v[h] = (a & 0xFFFFu) | (b << 16);
-              v[h + 1] = (a >> 16) | (b & 0xFFFF0000u);
-            }
-          }
-          *reinterpret_cast<u32x4_t *>(&lds[0][aoff[ii]]) = v;
+          *reinterpret_cast<u32x4_t *>(&lds[0][aoff[ii]]) = araw[ii][0];
         } else {
           bf16x8_t hi, lo;
 #pragma unroll
-          for (int e0 = 0; e0 < 8; ++e0) {
-            const int e = AFF ? aff2_perm(e0) : e0;  // slot e0 holds element e
+          for (int e = 0; e < 8; ++e) {
             const float f = __uint_as_float(e < 4 ? araw[ii][0][e] : araw[ii][1][e - 4]);
             if constexpr (AF == A_F32_SPLIT) {
               __bf16 h, l;
               split_bf16(f, h, l);
-              hi[e0] = h;
-              lo[e0] = l;
+              hi[e] = h;
+              lo[e] = l;
             } else {
-              hi[e0] = to_bf16(f);
+              hi[e] = to_bf16(f);
             }
           }
           *reinterpret_cast<bf16x8_t *>(&lds[0][aoff[ii]]) = hi;
@@ -228,34 +173,6 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
       }
     }
     __syncthreads();
-    if constexpr (AFF) {
-      // per-group sums of the staged rows (the values the products see), as bf16
-      // hi + lo in the layout of an N-side operand: group 32 i + 8 o + e of row
-      // r at [i][o][r][e]; groups past the row's end are zero
-      for (int gi = tid; gi < 64 * R; gi += NTHR) {
-        const int grp = gi / R, r = gi - grp * R;
-        float sum = 0.f;
-        if (grp < ngroups) {
-          const int q = grp >> 1, o0 = 8 * (grp & 1);
-#pragma unroll
-          for (int o = 0; o < 8; ++o) {
-            const int off = q * STEP + ((o0 + o) * R + r) * 8;
-#pragma unroll
-            for (int p = 0; p < NPL; ++p) {
-              const bf16x8_t v = *reinterpret_cast<const bf16x8_t *>(&lds[p][off]);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) sum += from_bf16(v[e]);
-            }
-          }
-        }
-        __bf16 h, l;
-        split_bf16(sum, h, l);
-        const int so = (((grp >> 5) * 4 + ((grp >> 3) & 3)) * R + r) * 8 + (grp & 7);
-        sums[0][so] = h;
-        sums[1][so] = l;
-      }
-      __syncthreads();
-    }
     staged_chunk = c;
   };
 
@@ -275,25 +192,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
     reset_acc();
   };
 
-  // Lanes whose token column is >= R read row (r16 % R): those MFMA output
-  // columns are never stored.
-  const int brow = r16 % R;
   auto finish_item = [&]() {
-    if constexpr (AFF) {
-      // the bias part: biases of the lane's row against the staged rows' group sums
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int off = ((i * 4 + kg) * R + brow) * 8;
-        const bf16x8_t sh = *reinterpret_cast<const bf16x8_t *>(&sums[0][off]);
-        const bf16x8_t sl = *reinterpret_cast<const bf16x8_t *>(&sums[1][off]);
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-          const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, bq[c_item & 1][t][i]);
-          acc[t] = mfma_16x16x32(bw, sh, acc[t]);
-          accl[t] = mfma_16x16x32(bw, sl, accl[t]);
-        }
-      }
-    }
     const int tok = r16;
     if (tok < nrows) {
       const long long orow = row0 + tok;
@@ -302,13 +201,13 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
       for (int m = 0; m < MT; ++m) {
         const int col0 = wrow_base + m * 16 + 4 * kg;
         f32x4_t a = acc[m];
-        if constexpr (NPL == 2 || AFF) a += accl[m];
+        if constexpr (NPL == 2) a += accl[m];
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (PAIR) {
             f32x4_t u = acc[m + MT];
-            if constexpr (NPL == 2 || AFF) u += accl[m + MT];
+            if constexpr (NPL == 2) u += accl[m + MT];
             v[r] = situ_glu(a[r], u[r], g.beta, g.beta_lin);
           } else {
             v[r] = a[r];
@@ -331,71 +230,31 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
     }
   };
 
+  // Lanes whose token column is >= R read row (r16 % R): those MFMA output
+  // columns are never stored.
+  const int brow = r16 % R;
   // one K step from group slot 0
   auto compute = [&](int d, int q) {
-    if constexpr (AFF) {
-      // scale dwords (groups 2q, 2q+1) of the lane's output rows 4 kg + r,
-      // from the lanes that loaded those rows
-      float sc[NTILE][2][4];
+    float scl[NTILE];
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t)
+    for (int t = 0; t < NTILE; ++t) {
+      const uint32_t sw = scg[0][t][d];  // the scale dword of K step q
+      scl[t] = e8m0_to_float((sw >> (8 * kg)) & 0xFFu);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t sw = (uint32_t)__shfl((int)scg[0][t][d], 4 * kg + r, 64);
-          sc[t][0][r] = bf16_lo_to_float(sw);
-          sc[t][1][r] = bf16_lo_to_float(sw >> 16);
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+      bf16x8_t bl;
+      if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
+      bf16x8_t wa[NTILE];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t ym[NTILE], zm[NTILE];
+      for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[0][d][t][j], scl[t]);
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-          ym[t] = wq[0][d][t][h] & 0x33333333u;
-          zm[t] = (wq[0][d][t][h] >> 2) & 0x33333333u;
-        }
-        f32x4_t tmp[NTILE];
+      for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh, acc[t]);
+      if constexpr (NPL == 2) {
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) tmp[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int off = q * STEP + (aff2_octet(h, kg, jj) * R + brow) * 8;
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
-          bf16x8_t bl;
-          if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
-#pragma unroll
-          for (int t = 0; t < NTILE; ++t) {
-            const bf16x8_t wa = jj ? aff2x8_to_bf16<2>(ym[t], zm[t]) : aff2x8_to_bf16<0>(ym[t], zm[t]);
-            tmp[t] = mfma_16x16x32(wa, bh, tmp[t]);
-            if constexpr (NPL == 2) tmp[t] = mfma_16x16x32(wa, bl, tmp[t]);
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(sc[t][h][r], tmp[t][r], acc[t][r]);
-      }
-    } else {
-      float scl[NTILE];
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t) {
-        const uint32_t sw = scg[0][t][d];  // the scale dword of K step q
-        scl[t] = e8m0_to_float((sw >> (8 * kg)) & 0xFFu);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
-        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
-        bf16x8_t bl;
-        if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
-        bf16x8_t wa[NTILE];
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[0][d][t][j], scl[t]);
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh, acc[t]);
-        if constexpr (NPL == 2) {
-#pragma unroll
-          for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl, accl[t]);
-        }
+        for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl, accl[t]);
       }
     }
   };
@@ -427,26 +286,369 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   }
 }
 
+// Affine 2-bit weights (w = s q + b per 64-element group), the same
+// persistent weight stream as grouped_stream_kernel (kept a kernel of its own
+// so that the MXFP4 kernel's code generation stays as tuned).  The codes enter
+// the MFMA as exact integers q (aff2x8_to_bf16), laid out so that each MFMA
+// instruction stays inside one group (aff2_octet): a lane loads two dwords of
+// codes per K step, one per group.  The two instructions of a group sum into
+// a temporary accumulator, which is added to the result times the group's
+// scale of each output row (the four rows' scale dwords come from the lanes
+// that loaded them).  The bias part sum_g b_g sum_{k in g} a_k is one more
+// product per item: the biases of the lane's row (8 groups per lane, the M
+// side) against the per-group sums of the staged activation rows (hi + lo,
+// the N side).  Activations are staged in the convert's element order.  The
+// biases of an item are requested with its first weight group, into one of
+// two slots by item parity: the load cursor runs at most one item ahead when
+// an item has more than AHEAD groups of K steps (K >= 1536, checked by the
+// caller).
+template <int AF, bool PAIR, int MT, int AHEAD, int NW>
+__global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g) {
+  constexpr int D = 4;  // K steps per group: one 16-byte read of scales covers four steps
+  constexpr int NMAT = PAIR ? 2 : 1;
+  constexpr int NTILE = NMAT * MT;
+  constexpr int NTHR = 64 * NW;
+  constexpr int ROWS_WG = 16 * NW * MT;
+  constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
+  constexpr int STEP = 16 * R * 8;     // bf16 elements per K step per plane: [octet][row][8]
+  constexpr int SUMS = 2 * 4 * R * 8;  // per-group activation sums: [slice][octet][row][8] (64 groups)
+  constexpr uint32_t STEP_BYTES = 32;  // codes of one row per K step
+  __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
+  __shared__ __attribute__((aligned(16))) __bf16 sums[2][SUMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kg = lane >> 4;
+  const int r16 = lane & 15;
+  const int N = g.N, K = g.K;
+  const int nks = K / KSTEP;
+  const int ngroups = K / 64;
+  const uint32_t row_bytes = K / 4;
+  const uint32_t srow_bytes = ngroups * 2;  // bf16 scales (or biases) of a row
+
+  const int n_items = *g.chunk_count * g.n_blocks;
+  const int G = gridDim.x;
+  const int i_begin = (int)((long long)blockIdx.x * n_items / G);
+  const int i_end = (int)((long long)(blockIdx.x + 1) * n_items / G);
+  if (i_begin >= i_end) return;
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const_i32 *chunks = (const_i32 *)(g.chunks);  // {expert, row0, nrows, 0} per chunk
+
+  // ---- load cursor: item and K step of the next weight load
+  int l_item = i_begin, l_q = 0;
+  __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
+  uint32_t woff[NTILE], soff[NTILE];
+  u32x4_t bq[2][NTILE][2];  // biases of groups 8 kg + 32 i of the lane's row, per item parity
+  auto set_load_item = [&](int it) {
+    const int c = __builtin_amdgcn_readfirstlane(it / g.n_blocks);
+    const int nb = it - c * g.n_blocks;
+    const int expert = chunks[4 * c];
+#pragma unroll
+    for (int mat = 0; mat < NMAT; ++mat) {
+      const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0) + expert * g.w_estride;
+      const uint8_t *S = (mat ? g.S1 : g.S0) + expert * g.s_estride;
+      wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
+      sr[mat] = make_rsrc(S, (uint32_t)N * srow_bytes);
+    }
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const int n = min(nb * ROWS_WG + wave * 16 * MT + (t % MT) * 16 + r16, N - 1);
+      woff[t] = (uint32_t)n * row_bytes + kg * 4;
+      soff[t] = (uint32_t)n * srow_bytes;
+    }
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const __amdgpu_buffer_rsrc_t br =
+          make_rsrc((t / MT ? g.B1 : g.B0) + expert * (g.s_estride / 2), (uint32_t)N * srow_bytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g0 = 8 * kg + 32 * i;
+        bq[it & 1][t][i] = g0 < ngroups ? buf_load16(br, soff[t] + 2 * g0, 0) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  set_load_item(i_begin);
+
+  // wq[0] / scg[0]: the group being computed; [1..AHEAD]: groups requested ahead
+  u32x2_t wq[AHEAD + 1][D][NTILE];
+  u32x4_t scg[AHEAD + 1][NTILE];
+  // one group of D K steps: per step and tile the lane's dwords kg (group 0)
+  // and 4 + kg (group 1) of the row's codes, then the 16 scale bytes of the
+  // D steps; past the last item all lanes re-read one line
+  auto load_group = [&](int bi) {
+    const bool live = l_item < i_end;
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        const uint32_t vo = live ? woff[t] : 0u, so = live ? (uint32_t)(l_q + d) * STEP_BYTES : 0u;
+        wq[bi][d][t] = u32x2_t{buf_load4(wr[t / MT], vo, so), buf_load4(wr[t / MT], vo + 16u, so)};
+      }
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t)
+      scg[bi][t] = buf_load16(sr[t / MT], live ? soff[t] : 0u, live ? (uint32_t)l_q * 4u : 0u);
+    l_q += D;
+    if (l_q == nks) {
+      l_q = 0;
+      if (++l_item < i_end) set_load_item(l_item);
+    }
+  };
+
+  // ---- compute cursor
+  int c_item = i_begin, c_q = 0;
+  int staged_chunk = -1;
+  int row0 = 0, nrows = 0, c_nb = 0;
+
+  // the chunk's rows in LDS (bf16, or hi + lo), each octet in the convert's
+  // element order, then their per-group sums as bf16 hi + lo in the layout of
+  // an N-side operand: group 32 i + 8 o + e of row r at [i][o][r][e]
+  auto stage = [&](int c) {
+    c = __builtin_amdgcn_readfirstlane(c);
+    row0 = chunks[4 * c + 1];
+    nrows = chunks[4 * c + 2];
+    if (c == staged_chunk) return;
+    __syncthreads();  // every wave is done with the previous chunk's rows
+    constexpr int SG = 2;
+    const int esz = (AF == A_BF16) ? 2 : 4;
+    const int ngrp = R * nks * 16;
+    for (int i0 = tid; i0 < ngrp; i0 += NTHR * SG) {
+      u32x4_t araw[SG][(AF == A_BF16) ? 1 : 2];
+      int aoff[SG];
+#pragma unroll
+      for (int ii = 0; ii < SG; ++ii) {
+        const int gi = i0 + NTHR * ii;
+        const int r = gi % R;
+        const int oct = (gi / R) & 15;
+        const int q = gi / (16 * R);
+        aoff[ii] = (gi < ngrp) ? q * STEP + (oct * R + r) * 8 : -1;
+        araw[ii][0] = u32x4_t{0, 0, 0, 0};
+        if constexpr (AF != A_BF16) araw[ii][1] = u32x4_t{0, 0, 0, 0};
+        if (gi < ngrp && r < nrows) {
+          const int p = row0 + r;
+          const long long arow = g.a_map ? (long long)(g.a_map[p] / g.a_div) : (long long)p;
+          const char *src = static_cast<const char *>(g.A) + (arow * g.lda + (long long)q * KSTEP + oct * 8) * esz;
+          araw[ii][0] = reinterpret_cast<const u32x4_t *>(src)[0];
+          if constexpr (AF != A_BF16) araw[ii][1] = reinterpret_cast<const u32x4_t *>(src)[1];
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < SG; ++ii) {
+        if (aoff[ii] < 0) continue;
+        if constexpr (AF == A_BF16) {
+          u32x4_t v = araw[ii][0];
+#pragma unroll
+          for (int h = 0; h < 4; h += 2) {  // bf16 elements 0..7 -> 0, 2, 1, 3, 4, 6, 5, 7
+            const uint32_t a = v[h], b = v[h + 1];
+            v[h] = (a & 0xFFFFu) | (b << 16);
+            v[h + 1] = (a >> 16) | (b & 0xFFFF0000u);
+          }
+          *reinterpret_cast<u32x4_t *>(&lds[0][aoff[ii]]) = v;
+        } else {
+          bf16x8_t hi, lo;
+#pragma unroll
+          for (int e0 = 0; e0 < 8; ++e0) {
+            const int e = aff2_perm(e0);  // slot e0 holds element e
+            const float f = __uint_as_float(e < 4 ? araw[ii][0][e] : araw[ii][1][e - 4]);
+            if constexpr (AF == A_F32_SPLIT) {
+              __bf16 h, l;
+              split_bf16(f, h, l);
+              hi[e0] = h;
+              lo[e0] = l;
+            } else {
+              hi[e0] = to_bf16(f);
+            }
+          }
+          *reinterpret_cast<bf16x8_t *>(&lds[0][aoff[ii]]) = hi;
+          if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(&lds[NPL - 1][aoff[ii]]) = lo;
+        }
+      }
+    }
+    __syncthreads();
+    for (int gi = tid; gi < 64 * R; gi += NTHR) {
+      const int grp = gi / R, r = gi - grp * R;
+      float sum = 0.f;
+      if (grp < ngroups) {
+        const int q = grp >> 1, o0 = 8 * (grp & 1);
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+          const int off = q * STEP + ((o0 + o) * R + r) * 8;
+#pragma unroll
+          for (int p = 0; p < NPL; ++p) {
+            const bf16x8_t v = *reinterpret_cast<const bf16x8_t *>(&lds[p][off]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += from_bf16(v[e]);
+          }
+        }
+      }
+      __bf16 h, l;
+      split_bf16(sum, h, l);
+      const int so = (((grp >> 5) * 4 + ((grp >> 3) & 3)) * R + r) * 8 + (grp & 7);
+      sums[0][so] = h;
+      sums[1][so] = l;
+    }
+    __syncthreads();
+    staged_chunk = c;
+  };
+
+  f32x4_t acc[NTILE], accl[NTILE];
+  auto begin_item = [&]() {
+    const int c = c_item / g.n_blocks;
+    c_nb = c_item - c * g.n_blocks;
+    stage(c);
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accl[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // Lanes whose token column is >= R read row (r16 % R): those MFMA output
+  // columns are never stored.
+  const int brow = r16 % R;
+  auto finish_item = [&]() {
+    // the bias part: biases of the lane's row against the staged rows' group sums
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int off = ((i * 4 + kg) * R + brow) * 8;
+      const bf16x8_t sh = *reinterpret_cast<const bf16x8_t *>(&sums[0][off]);
+      const bf16x8_t sl = *reinterpret_cast<const bf16x8_t *>(&sums[1][off]);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, bq[c_item & 1][t][i]);
+        acc[t] = mfma_16x16x32(bw, sh, acc[t]);
+        accl[t] = mfma_16x16x32(bw, sl, accl[t]);
+      }
+    }
+    const int tok = r16;
+    if (tok < nrows) {
+      const long long orow = row0 + tok;
+      const int wrow_base = c_nb * ROWS_WG + wave * 16 * MT;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int col0 = wrow_base + m * 16 + 4 * kg;
+        const f32x4_t a = acc[m] + accl[m];
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (PAIR) {
+            const f32x4_t u = acc[m + MT] + accl[m + MT];
+            v[r] = situ_glu(a[r], u[r], g.beta, g.beta_lin);
+          } else {
+            v[r] = a[r];
+          }
+        }
+        if (g.rscale != nullptr) {
+          const float rs = g.rscale[g.rscale_map ? g.rscale_map[orow] : orow];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] *= rs;
+        }
+        float *cp = g.C + orow * g.ldc + col0;
+        if (col0 + 3 < N) {
+          *reinterpret_cast<f32x4_t *>(cp) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col0 + r < N) cp[r] = v[r];
+        }
+      }
+    }
+  };
+
+  // one K step from group slot 0, group by group
+  auto compute = [&](int d, int q) {
+    // scale dwords (groups 2q, 2q+1) of the lane's output rows 4 kg + r, from
+    // the lanes that loaded those rows
+    float sc[NTILE][2][4];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t sw = (uint32_t)__shfl((int)scg[0][t][d], 4 * kg + r, 64);
+        sc[t][0][r] = bf16_lo_to_float(sw);
+        sc[t][1][r] = bf16_lo_to_float(sw >> 16);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t ym[NTILE], zm[NTILE];
+      f32x4_t tmp[NTILE];
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        ym[t] = wq[0][d][t][h] & 0x33333333u;
+        zm[t] = (wq[0][d][t][h] >> 2) & 0x33333333u;
+        tmp[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int off = q * STEP + (aff2_octet(h, kg, jj) * R + brow) * 8;
+        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+        bf16x8_t bl;
+        if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+          const bf16x8_t wa = jj ? aff2x8_to_bf16<2>(ym[t], zm[t]) : aff2x8_to_bf16<0>(ym[t], zm[t]);
+          tmp[t] = mfma_16x16x32(wa, bh, tmp[t]);
+          if constexpr (NPL == 2) tmp[t] = mfma_16x16x32(wa, bl, tmp[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(sc[t][h][r], tmp[t][r], acc[t][r]);
+    }
+  };
+
+  // ---- prologue: groups 1..AHEAD are requested before the first staging
+#pragma unroll
+  for (int i = 1; i <= AHEAD; ++i) load_group(i);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  for (; c_item < i_end; ++c_item) {
+    begin_item();
+    for (c_q = 0; c_q < nks; c_q += D) {
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+          for (int t = 0; t < NTILE; ++t) wq[i][d][t] = wq[i + 1][d][t];
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) scg[i][t] = scg[i + 1][t];
+      }
+      load_group(AHEAD);
+#pragma unroll
+      for (int d = 0; d < D; ++d) compute(d, c_q + d);
+    }
+    finish_item();
+  }
+}
+
 // One 16-row tile per wave and matrix, two groups in flight; gate/up (two
 // matrices per wave) runs eight waves per work-group, down four.
 constexpr int gs_waves(bool pair) { return pair ? 8 : 4; }
 
-template <int WF, int AF, bool PAIR>
+template <int AF, bool PAIR>
 void *kernel_ptr() {
-  return reinterpret_cast<void *>(&grouped_stream_kernel<WF, AF, PAIR, 1, 2, gs_waves(PAIR)>);
+  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, 1, 2, gs_waves(PAIR)>);
 }
-
-template <int WF>
-void *select_af(int afmt, bool pair) {
-  switch (afmt) {
-    case A_BF16: return pair ? kernel_ptr<WF, A_BF16, true>() : kernel_ptr<WF, A_BF16, false>();
-    case A_F32_SPLIT: return pair ? kernel_ptr<WF, A_F32_SPLIT, true>() : kernel_ptr<WF, A_F32_SPLIT, false>();
-    default: return pair ? kernel_ptr<WF, A_F32_ROUND, true>() : kernel_ptr<WF, A_F32_ROUND, false>();
-  }
+template <int AF, bool PAIR>
+void *aff_kernel_ptr() {
+  return reinterpret_cast<void *>(&grouped_stream_aff_kernel<AF, PAIR, 1, 2, gs_waves(PAIR)>);
 }
 
 void *select_kernel(int wfmt, int afmt, bool pair) {
-  return wfmt == W_AFF2 ? select_af<W_AFF2>(afmt, pair) : select_af<W_MXFP4>(afmt, pair);
+  if (wfmt == W_AFF2) {
+    switch (afmt) {
+      case A_BF16: return pair ? aff_kernel_ptr<A_BF16, true>() : aff_kernel_ptr<A_BF16, false>();
+      case A_F32_SPLIT: return pair ? aff_kernel_ptr<A_F32_SPLIT, true>() : aff_kernel_ptr<A_F32_SPLIT, false>();
+      default: return pair ? aff_kernel_ptr<A_F32_ROUND, true>() : aff_kernel_ptr<A_F32_ROUND, false>();
+    }
+  }
+  switch (afmt) {
+    case A_BF16: return pair ? kernel_ptr<A_BF16, true>() : kernel_ptr<A_BF16, false>();
+    case A_F32_SPLIT: return pair ? kernel_ptr<A_F32_SPLIT, true>() : kernel_ptr<A_F32_SPLIT, false>();
+    default: return pair ? kernel_ptr<A_F32_ROUND, true>() : kernel_ptr<A_F32_ROUND, false>();
+  }
 }
 
 }  // namespace
