@@ -404,8 +404,23 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair) {
     p.n_blocks = ceil_div(N, dense_tile_cols(pair));
     p.max_chunks = ceil_div(rows, p.chunk_rows);
     const long long items = (long long)p.max_chunks * p.n_blocks;
+    // K is split only while the tiles leave CUs idle, and a split is taken
+    // only where it halves the time of the rounds of work over the 256 CUs
+    // (one tile per CU): 224 whole tiles take one round, as long as 448 half
+    // tiles take in two, and the split would add partials and a finalize pass
+    // for nothing
     int splits = 1;
-    while (items * splits < 256 && K % (128 * splits * 2) == 0 && splits < 8) splits *= 2;
+    if (items < 256) {
+      long long best = 256;  // rounds x 256 / s (in 1/256 of a whole tile); s = 1: one round
+      for (int s2 = 2; s2 <= 8 && K % (128 * s2) == 0; s2 *= 2) {
+        const long long rounds = (items * s2 + 255) / 256;
+        const long long cost = rounds * 256 / s2;
+        if (2 * cost <= best) {
+          best = cost;
+          splits = s2;
+        }
+      }
+    }
     p.splits = splits;
     p.grid_logical = items * splits;
   } else {

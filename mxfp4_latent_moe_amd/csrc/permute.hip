@@ -55,6 +55,11 @@ __device__ int block_excl_scan(int x, int *wave_tot, int *tot) {
   return before + inc - x;
 }
 
+// Thread e owns expert e's column of block counts.  The column is read in
+// batches of SB independent loads (all in flight at once), summed, and after
+// the scan over experts rewritten as absolute bases: offsets[e] plus the
+// counts of the blocks before.
+constexpr int SB = 32;
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int E, int P,
                                                          int32_t *__restrict__ blk,
                                                          int32_t *__restrict__ offsets,
@@ -63,17 +68,29 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int E, int P,
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk[(long long)b * E + e];
-      blk[(long long)b * E + e] = cnt;
-      cnt += c;
+    for (int b0 = 0; b0 < nblk; b0 += SB) {
+      int c[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) c[i] = b0 + i < nblk ? blk[(long long)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) cnt += c[i];
     }
   }
   int total;
   const int off = block_excl_scan(e < E ? cnt : 0, wave_tot, &total);
   if (e < E) {
     offsets[e] = off;
-    for (int b = 0; b < nblk; ++b) blk[(long long)b * E + e] += off;
+    int run = off;
+    for (int b0 = 0; b0 < nblk; b0 += SB) {
+      int c[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) c[i] = b0 + i < nblk ? blk[(long long)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        if (b0 + i < nblk) blk[(long long)(b0 + i) * E + e] = run;
+        run += c[i];
+      }
+    }
   }
   if (e == 0) offsets[E] = P;
   const int flag = (e < E && cnt > 0) ? 1 : 0;

@@ -77,6 +77,56 @@ def test_dequant_every_byte_and_exponent_through_down_gemm(mx):
         assert (got == np.transpose(ref, (0, 2, 1))).all(), a_dtype
 
 
+@pytest.mark.parametrize("mode", [0, 3])
+def test_e8m0_outside_the_exact_range(mx, mode):
+    """The header's e8m0 contract, through the down GEMM with one-hot activation
+    rows (Y[e*128 + r, n] = W2_e[n, r]), on the tiled path (bf16 hi + lo) and
+    the MX path (three fp6 terms; one-hot rows are exact in both):
+    scale bytes 2..252 exact; 0 and 1 give either the exact value or zero
+    (values below 2^-126 may be flushed); 253 and 254 exact while the value
+    stays below 2^128 (codes of magnitude <= 1.5 here); rows holding a 255
+    (NaN in OCP MX) group come out non-finite on the bf16 path and are not
+    checked on the MX path (unspecified); the call never faults and rows
+    without such groups stay exact."""
+    from mxfp4_latent_moe_amd import ops
+    say(f"case: e8m0 bytes 0, 1, 253, 254, 255 through MOE_OP_DOWN, operand mode {mode}")
+    sh = synth.TINY_SHAPE
+    E, L, I = sh.n_experts, sh.latent, sh.inter
+    G = I // 32
+    rng = np.random.default_rng(21)
+    packed = rng.integers(0, 256, size=(E, L, I // 2), dtype=np.uint8)
+    scale = rng.integers(2, 253, size=(E, L, G), dtype=np.uint8)
+    low, high, nan = slice(64, 80), slice(80, 96), slice(96, 128)  # weight rows n
+    scale[:, low, 1] = 0
+    scale[:, low, 2] = 1
+    scale[:, high, 0] = 253
+    scale[:, high, 3] = 254
+    # codes of magnitude <= 1.5 (e2m1 codes 0..3 and 8..11) in the 253 / 254 groups
+    for g in (0, 3):
+        blk = packed[:, high, 16 * g:16 * (g + 1)]
+        packed[:, high, 16 * g:16 * (g + 1)] = blk & np.uint8(0xBB)
+    scale[:, nan, 2] = 255
+    P = E * I
+    A = np.zeros((P, I), np.float32)
+    A[np.arange(P), np.arange(P) % I] = 1.0
+    offsets = (np.arange(E + 1) * I).astype(np.int32)
+    s = mx.shape_of(sh, mode)
+    ws = torch.empty(ops.workspace_bytes(s, 2, P), dtype=torch.uint8, device=DEV)
+    Y = torch.empty((P, L), dtype=torch.float32, device=DEV)
+    ops.grouped_gemm(s, ops.MOE_OP_DOWN, P, to_dev(offsets, DEV), None, to_dev(A, DEV), to_dev(packed, DEV),
+                     to_dev(scale, DEV), None, None, None, Y, ws)
+    torch.cuda.synchronize()
+    got = np.transpose(Y.cpu().numpy().reshape(E, I, L), (0, 2, 1))  # [E, L, I] like the weights
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = mxfp4.dequant(packed, scale)
+    assert np.array_equal(got[:, :64], ref[:, :64])
+    assert np.array_equal(got[:, high], ref[:, high]) and np.isfinite(got[:, high]).all()
+    lo_got, lo_ref = got[:, low], ref[:, low]
+    assert np.isfinite(lo_got).all() and ((lo_got == lo_ref) | (lo_got == 0)).all()
+    if mode == 0:
+        assert (~np.isfinite(got[:, nan])).any(axis=2).all()
+
+
 def test_tiny_layer_parity(mx):
     wl, x_bits, d, b, st = _tiny_setup()
     say("case: tiny layer, operand mode bf16x2")
