@@ -22,7 +22,7 @@ LIB = os.path.join(LIBDIR, "libmoe_latent.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["abi.hip", "gemm.hip", "stream.hip", "grouped_stream.hip", "prefill.hip", "route.hip",
-           "permute.hip", "combine.hip", "mx8.hip", "dense.hip", "reap.hip"]
+           "permute.hip", "combine.hip", "mx8.hip", "dense.hip", "reap.hip", "prefill_pl.hip"]
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

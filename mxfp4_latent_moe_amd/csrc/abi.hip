@@ -92,9 +92,12 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
   w.count = align_up((size_t)w.plan.max_chunks * 16);
   w.partial = w.count + ALIGN;
   w.mx = w.partial + align_up(w.plan.partial_bytes);
-  // the MX term planes hold at most P rows (gathered activations with more
-  // rows than P are split per sorted row)
-  w.total = w.mx + (use_mx8(s, w.plan, P, K) ? align_up(mx8_split_bytes(P, K)) : 0);
+  // the MX term planes or the bf16 activation planes hold at most P rows
+  // (gathered activations with more rows than P are split per sorted row)
+  size_t split = 0;
+  if (use_mx8(s, w.plan, P, K)) split = mx8_split_bytes(P, K);
+  else if (w.plan.variant == 3) split = split_rows_bytes(P, K, s->operand_mode == MOE_OPND_BF16 ? 1 : 2);
+  w.total = w.mx + align_up(split);
   return w;
 }
 
@@ -508,6 +511,30 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
       a.mx_rows = rows;
       if (split_gathers) a.a_map = nullptr;
       afmt = fp6 ? A_MX6X3 : A_MX8X3;
+    }
+    if (w.plan.variant == 3 && afmt != A_MX8X3 && afmt != A_MX6X3) {
+      // bf16 activation planes: bf16 activations are one plane already; fp32
+      // ones are split first (hi + lo, or rounded), over the same rows as the
+      // MX split above
+      int npl = 1;
+      if (a_dtype == MOE_DT_F32) {
+        npl = afmt == A_F32_SPLIT ? 2 : 1;
+        const bool split_gathers = gathered && a_rows > P;
+        const long long rows = (gathered && !split_gathers) ? (long long)a_rows : (long long)P;
+        uint16_t *planes = reinterpret_cast<uint16_t *>(wsp(ws, w.mx));
+        if (launch_split_rows(npl, static_cast<const float *>(A), K, rows, K, split_gathers ? sorted_pair : nullptr,
+                              s->top_k, planes, st) != hipSuccess)
+          return MOE_EHIP;
+        a.A = planes;
+        a.lda = (long long)npl * K;
+        a.a_rows = rows;
+        if (split_gathers) a.a_map = nullptr;
+      }
+      a.n_blocks = (N + prefill_pl_rows_per_wg(gateup) - 1) / prefill_pl_rows_per_wg(gateup);
+      const long long logical = (long long)w.plan.max_chunks * a.n_blocks;
+      a.grid_logical = (int)logical;
+      if (launch_prefill_planes(npl, gateup, a, (logical + 7) / 8 * 8, st) != hipSuccess) return MOE_EHIP;
+      return MOE_OK;
     }
     GemmPlan pl = w.plan;
     if (afmt == A_MX8X3 || afmt == A_MX6X3) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -138,3 +140,20 @@ MOE_DEV int xcd_logical(int total) {
   const int logical = (b & 7) * (t8 >> 3) + (b >> 3);
   return logical < total ? logical : -1;
 }
+
+// ---- direct-to-LDS loads and hand-scheduled LDS reads
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// fn(integral_constant<0>) .. fn(integral_constant<N - 1>), in order
+template <int N, typename Fn>
+MOE_DEV void static_for(Fn &&fn) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(fn);
+    fn(std::integral_constant<int, N - 1>{});
+  }
+}
+
+MOE_DEV uint32_t lds_addr(const uint8_t *p) { return (uint32_t)(uintptr_t)(const lds_void *)p; }

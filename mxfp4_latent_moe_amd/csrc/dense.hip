@@ -25,27 +25,16 @@ namespace moe {
 namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void dlds_void;
 
 constexpr int DT = 256;  // tokens and weight rows per work-group
 constexpr int DNW = 4;   // waves
 
-template <int N, typename Fn>
-MOE_DEV void static_for_d(Fn &&fn) {
-  if constexpr (N > 0) {
-    static_for_d<N - 1>(fn);
-    fn(std::integral_constant<int, N - 1>{});
-  }
-}
-// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
-constexpr int vmcnt_imm_d(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 MOE_DEV f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                  c, 0, 0, 0);
 }
 
-MOE_DEV uint32_t dlds_addr(const uint8_t *p) { return (uint32_t)(uintptr_t)(const dlds_void *)p; }
 
 // 16 bytes of LDS at a + O, issued without waiting
 template <int O>
@@ -156,7 +145,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
     const int ii = wave + DNW * k;  // uniform
     const int region = (DNW * k * 1024) / REG;
     const int upper = (PAIR && ((DNW * k * 1024) % REG) >= REG / 2) ? 1 : 0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc[region == 0 ? upper : 1 + region], (dlds_void *)(stg + ii * 1024),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc[region == 0 ? upper : 1 + region], (lds_void *)(stg + ii * 1024),
                                              16, dense_voff<KS, PAIR>(ii, lane, n0, t0, N, K, rows, g.lda, k0),
                                              (uint32_t)s * (uint32_t)(KS * 2), 0, 0);
   };
@@ -182,7 +171,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
     else return 128 * wn + 32 * a;
   };
   constexpr int NST = dense_stages(NPL);
-  const uint32_t ring_base = dlds_addr(ring);
+  const uint32_t ring_base = lds_addr(ring);
   // weight rows and token rows of the wave as region offsets
   const int wrow0 = wrow_tile(0);
   const int tokrow0 = 128 * wm;
@@ -212,7 +201,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
       dread<2 * TILE_OFF>(aw, fw[j & 1][2]);
       dread<3 * TILE_OFF>(aw, fw[j & 1][3]);
     }
-    static_for_d<NPL>([&](auto pc) {
+    static_for<NPL>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       dread<(1 + p) * REG>(at, ft[j & 1][p][0]);
       dread<(1 + p) * REG + TILE_OFF>(at, ft[j & 1][p][1]);
@@ -247,14 +236,14 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
   // so no step starts on an exposed LDS latency.
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) load_stage(ring + s * STAGE, min(s, nks - 1));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(KL * (NST - 2)));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(KL * (NST - 2)));
   __builtin_amdgcn_s_barrier();
   issue(slot_base(0), std::integral_constant<int, 0>{});
   for (int s = 0; s < nks; ++s) {
     const int fill = (s + NST - 1) % NST;
     load_stage(ring + fill * STAGE, min(s + NST - 1, nks - 1));
     const uint32_t base = slot_base(s);
-    static_for_d<J>([&](auto jc) {
+    static_for<J>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       if constexpr (j + 1 < J) {
         issue(base, std::integral_constant<int, j + 1>{});
@@ -266,7 +255,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
         tie(j & 1);
       }
     });
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(KL * (NST - 2)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(KL * (NST - 2)));
     __builtin_amdgcn_s_barrier();
     // the next step's first fragments (past the last step: a read of a slot
     // that holds valid data, drained below), then the deferred products
@@ -275,7 +264,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
   }
   dwait<0>();
   tie(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm_d(0));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // ---- epilogue: acc[a][b] register i of lane l is weight row 32 a + (i % 4)
   // + 8 (i / 4) + 4 (l / 32) and token 32 b + l % 32 of the wave's tiles

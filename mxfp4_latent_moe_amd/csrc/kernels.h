@@ -107,6 +107,14 @@ hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &
 int prefill_rows_per_wg(bool pair);
 int prefill_rows_per_wg_fmt(bool pair, int wfmt);
 int prefill_mx_rows_per_wg(bool pair);
+// tiled prefill kernel over bf16 activation planes ([rows][npl][K]: hi then lo,
+// or the rounded row), MXFP4 weights; and the fp32 -> planes split
+int prefill_pl_rows_per_wg(bool pair);
+hipError_t launch_prefill_planes(int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st);
+size_t split_rows_bytes(long long rows, int K, int npl);
+// map != nullptr: output row r is activation row map[r] / div
+hipError_t launch_split_rows(int npl, const float *A, long long lda, long long rows, int K, const int32_t *map,
+                             int div, uint16_t *out, hipStream_t st);
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st);
 size_t mx8_split_bytes(long long rows, int K);

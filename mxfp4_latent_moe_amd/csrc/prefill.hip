@@ -452,20 +452,6 @@ constexpr int MX_GSW_BYTES = 2 * 16 * PREFILL_MX_NW * PREFILL_MX_MT_PAIR * 16;
 static_assert(MX_GSW_BYTES == 16 * PREFILL_MX_NW * PREFILL_MX_MT_SINGLE * 16, "one scale area for both shapes");
 constexpr int mx_group_bytes(int nt) { return mx_gsa_bytes(nt) + MX_GSW_BYTES; }
 constexpr int MX_DUMMY_BYTES = 8 * 1024;  // target of the padding loads
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-template <int N, typename Fn>
-MOE_DEV void static_for(Fn &&fn) {
-  if constexpr (N > 0) {
-    static_for<N - 1>(fn);
-    fn(std::integral_constant<int, N - 1>{});
-  }
-}
-
-MOE_DEV uint32_t lds_addr(uint8_t *p) { return (uint32_t)(uintptr_t)(lds_void *)p; }
 
 // 16 activation bytes at ql + QO, 16 more at qh + QO and a scale dword at
 // sa + SO, issued without waiting

@@ -1,0 +1,350 @@
+// Tiled prefill GEMM for MXFP4 expert segments over activations given as bf16
+// planes: row r of the activations is [NPL][K] bf16, hi = bf16(a) then
+// lo = bf16(a - hi) (NPL = 2), or the rounded row alone (NPL = 1).
+//
+// kimi-k3-mlx README, Architecture table and the MXFP4 format of the
+// checkpoint (weight_packed e2m1 nibbles, weight_scale e8m0 per 32): each
+// weight code is dequantised to bf16 by the scaled fp4 convert and fed to the
+// bf16 MFMA with fp32 accumulation; a = hi + lo makes two products into the
+// same accumulator.
+//
+// Work item = (chunk of <= 16 NT expert-sorted rows of one expert, block of
+// 16 NW MT weight rows per matrix), as for the fp32-staging kernel.  Here the
+// activations need no register work on their way to LDS: each K step's planes
+// are loaded straight into a two-stage LDS ring one step ahead.  Eight waves,
+// two per SIMD, each hold 4 weight tiles of 16 rows (gate and up of a SiTU
+// pair: 2 + 2), so the accumulators and operands fit the 256 registers of a
+// wave without spilling, and each SIMD interleaves two instruction streams.
+// The weights go to registers through a ring of 2 steps, or 4 for items of
+// one or two token tiles, whose steps are too short to cover a memory trip.
+//
+// LDS stage: [plane][token][16 cells of 16 bytes]; cell c of token t holds
+// octet c ^ (t & 15) of the token's 128-wide K step.  A wave load of 64 cells
+// covers 4 tokens, 16 lanes reading one token's 256 contiguous bytes; a
+// fragment read (16 tokens, one octet each) touches 16 different cells.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int KSTEP = 128;
+constexpr int PL_NW = 8;  // waves per work-group
+constexpr int pl_stage_bytes(int npl, int nt) { return npl * 16 * nt * 256; }
+
+// 16 bytes of LDS at addr + OFF, issued without waiting
+template <int OFF>
+MOE_DEV void lds_read16(uint32_t addr, u32x4_t &v) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(v) : "v"(addr), "n"(OFF) : "memory");
+}
+// wait until at most N LDS reads are outstanding; the operand ties the wait to
+// the register it protects, so its users stay behind it
+template <int N>
+MOE_DEV void lds_wait16(u32x4_t &v) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N) : "memory");
+}
+
+template <bool PAIR, int NPL, int NTA, int MT, int NW, int RW>
+__device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8_t *st1, int expert, int row0,
+                                          int nrows, int nb) {
+  constexpr int NMAT = PAIR ? 2 : 1;
+  constexpr int NTILE = NMAT * MT;
+  constexpr int CT = 16 * NTA;          // staged tokens
+  constexpr int ROWS_WG = 16 * NW * MT;
+  constexpr int PLB = CT * 256;         // bytes of one plane in a stage
+  constexpr int QI = 4 * NPL * NTA;     // 1 KB wave loads per stage
+  constexpr int KQ = (QI + NW - 1) / NW;  // per wave (the last round may leave waves idle)
+  static_assert(pl_stage_bytes(NPL, NTA) == QI * 1024, "whole wave loads");
+  static_assert(RW == 2 || RW == 4, "weight ring of 2 or 4 slots");
+  uint8_t *stage[2] = {st0, st1};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
+  const int kg = lane >> 4;
+  const int r16 = lane & 15;
+  const int N = g.N, K = g.K;
+  const int nks = K / KSTEP;
+
+  // ---- weights: lane group kg's 16 bytes of a K step are its row's 32 codes
+  // of scale group kg; with the row's four scale bytes of the step, into a
+  // register ring of RW slots, RW - 1 steps ahead
+  const uint32_t row_bytes = K / 2, srow_bytes = K / 32;
+  __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
+#pragma unroll
+  for (int mat = 0; mat < NMAT; ++mat) {
+    const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0) + expert * g.w_estride;
+    wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
+    sr[mat] = make_rsrc((mat ? g.S1 : g.S0) + expert * g.s_estride, (uint32_t)N * srow_bytes);
+  }
+  const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
+  uint32_t woff[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
+    woff[t] = (uint32_t)n * row_bytes + kg * 16;
+  }
+  u32x4_t wq[RW][NTILE];
+  uint32_t wsc[RW][NTILE];
+
+  // ---- activation planes straight into LDS: wave load k of this wave fills
+  // cells [64 (wave + NW k), +64) of a stage.  Gathered rows index A from its
+  // start; rows in sorted order from the chunk's first row.  Rows past the
+  // chunk repeat its first row (their columns are never stored).
+  const long long lda = g.lda;  // bf16 elements per activation row
+  const char *abase = static_cast<const char *>(g.A) + (g.a_map ? 0LL : (long long)row0 * lda * 2);
+  const long long abytes = (g.a_map ? g.a_rows : (long long)nrows) * lda * 2;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(abase, (uint32_t)min(abytes, 0x7FFFFFF0LL));
+  uint32_t qoff[KQ];
+#pragma unroll
+  for (int k = 0; k < KQ; ++k) {
+    const int q = min(64 * (wave + NW * k), 64 * (QI - 1)) + lane;
+    const int p = q / (16 * CT), rem = q - p * 16 * CT;
+    const int tok = rem >> 4, oct = (rem & 15) ^ (tok & 15);
+    const int tt = tok < nrows ? tok : 0;
+    const long long arow = g.a_map ? (long long)(g.a_map[row0 + tt] / g.a_div) : (long long)tt;
+    qoff[k] = (uint32_t)((arow * lda + (long long)p * K) * 2 + oct * 16);
+  }
+  // the memory operations of one step: KQ loads into LDS stage sb, then the
+  // codes and scales of each weight tile into ring slot wb
+  constexpr int NOPS = KQ + 2 * NTILE;
+  auto issue_op = [&](int o, int sb, int wb, int sa, int sw) {
+    if (o < KQ) {
+      const int ii = wave + NW * o;  // uniform
+      if (ii < QI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(stage[sb] + ii * 1024), 16, qoff[o],
+                                                 (uint32_t)sa * 256u, 0, 0);
+    } else if (o < KQ + NTILE) {
+      const int t = o - KQ;
+      wq[wb][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)sw * 64u);
+    } else {
+      const int t = o - KQ - NTILE;
+      // the scale row starts at the code row's offset / 16 (K / 32 bytes against K / 2)
+      wsc[wb][t] = buf_load4(sr[t / MT], (woff[t] - kg * 16) >> 4, (uint32_t)sw * 4u);
+    }
+  };
+
+  f32x4_t acc[NTILE][NTA];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // fragment reads: in sub-step j (K 32 wide) lane (token r16, group kg) takes
+  // octet 4 kg + j of its token, the K positions of its weight codes 8j .. 8j+7
+  uint32_t la[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage[b]) + (uint32_t)(r16 * 256 + (((4 * kg + j) ^ r16) << 4));
+
+  // step s from LDS stage SB and weight slot WB; its fragments f = (sub-step
+  // j, plane p, token tile n) are read from LDS two ahead of their MFMAs; the
+  // weights of sub-step j + 1 are converted tile by tile over sub-step j's
+  // fragments; the loads of LDS stage s + 1 and weight step s + RW - 1 go out
+  // over the first half of the step
+  auto compute = [&](auto sbc, auto wbc, int s) {
+    constexpr int SB = decltype(sbc)::value, WB = decltype(wbc)::value;
+    constexpr int WN = (WB + RW - 1) % RW;  // the slot of step s - 1, free again
+    const int sa = min(s + 1, nks - 1), sw = min(s + RW - 1, nks - 1);
+    constexpr int FJ = NPL * NTA;  // fragments per sub-step
+    constexpr int F = 4 * FJ;
+    constexpr int D = 2;
+    constexpr int J = (NOPS + F / 2 - 1) / (F / 2);  // loads issued per fragment
+    u32x4_t bq[D + 1];
+    bf16x8_t wa[2][NTILE];
+    float scl[NTILE];
+    auto scale_of = [&](int t) { return e8m0_to_float((wsc[WB][t] >> (8 * kg)) & 0xFFu); };
+    auto issue = [&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      constexpr int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
+      lds_read16<p * PLB + n * 16 * 256>(la[SB][j], bq[f % (D + 1)]);
+    };
+    static_for<D>([&](auto fc) { issue(fc); });
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      scl[t] = scale_of(t);
+      wa[0][t] = fp4x8_to_bf16(wq[WB][t][0], scl[t]);
+    }
+    static_for<F>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      constexpr int j = f / FJ, i = f % FJ, n = f % NTA;
+      if constexpr (f + D < F) issue(std::integral_constant<int, f + D>{});
+      if constexpr (j + 1 < 4) {
+        // tiles [i NTILE / FJ, (i + 1) NTILE / FJ) of sub-step j + 1
+#pragma unroll
+        for (int t = (i * NTILE) / FJ; t < ((i + 1) * NTILE) / FJ; ++t)
+          wa[(j + 1) & 1][t] = fp4x8_to_bf16(wq[WB][t][j + 1], scl[t]);
+      }
+      constexpr int behind = (f + D < F) ? D : F - 1 - f;  // reads issued after f
+      lds_wait16<behind>(bq[f % (D + 1)]);
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bq[f % (D + 1)]);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bv, acc[t][n]);
+#pragma unroll
+      for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, SB ^ 1, WN, sa, sw);
+    });
+  };
+  // after step s: stage s + 1 (requested during s) must be in LDS for every
+  // wave, and weight step s + 1 in registers; weight loads issued after the
+  // last LDS load of the step may stay in flight
+  constexpr int VM_LEFT = RW > 2 ? 2 * NTILE : 0;
+  auto step = [&](auto ic, int s) {
+    constexpr int I = decltype(ic)::value;
+    compute(std::integral_constant<int, I & 1>{}, std::integral_constant<int, I % RW>{}, s);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_LEFT));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);  // keep the next step's register work behind the wait
+  };
+
+  // prologue: stage 0 and weight steps 0 .. RW - 2
+#pragma unroll
+  for (int o = 0; o < KQ; ++o) issue_op(o, 0, 0, 0, 0);
+  static_for<RW - 1>([&](auto wc) {
+    constexpr int w = decltype(wc)::value;
+#pragma unroll
+    for (int o = KQ; o < NOPS; ++o) issue_op(o, 0, w, 0, min(w, nks - 1));
+  });
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((RW - 2) * 2 * NTILE));
+  __builtin_amdgcn_s_barrier();
+  int s = 0;
+  for (; s + RW - 1 < nks; s += RW) static_for<RW>([&](auto ic) { step(ic, s + decltype(ic)::value); });
+  // tail: s is a multiple of RW (even), so step i keeps stage i & 1 and slot i
+  static_for<RW - 1>([&](auto ic) {
+    if (s + decltype(ic)::value < nks) step(ic, s + decltype(ic)::value);
+  });
+  // drain the loads past the last step before the LDS is reused
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  // ---- epilogue: SiTU-GLU of the gate/up pair (or the plain product), row scale, store
+  const int col_base = wrow_base + 4 * kg;
+#pragma unroll
+  for (int n = 0; n < NTA; ++n) {
+    const int tok = 16 * n + r16;
+    if (tok < nrows) {
+      const long long orow = row0 + tok;
+      float rs = 1.f;
+      if (g.rscale != nullptr) rs = g.rscale[g.rscale_map ? g.rscale_map[orow] : orow];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int col0 = col_base + m * 16;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (PAIR) v[r] = situ_glu(acc[m][n][r], acc[m + MT][n][r], g.beta, g.beta_lin) * rs;
+          else v[r] = acc[m][n][r] * rs;
+        }
+        float *cp = g.C + orow * g.ldc + col0;
+        if (col0 + 3 < N) {
+          f32x4_t o = f32x4_t{v[0], v[1], v[2], v[3]};
+          if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
+          *reinterpret_cast<f32x4_t *>(cp) = o;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col0 + r < N) cp[r] = g.accumulate ? cp[r] + v[r] : v[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// weight-ring slots: items with few token tiles stream their weights with
+// little compute per step, so they keep more steps in flight
+constexpr int pl_ring(int nta) { return nta <= 2 ? 4 : 2; }
+
+template <bool PAIR, int NPL, int NT, int MT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
+  // two activation stages (separate objects, so waits on one stage's loads do
+  // not cover the other)
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[pl_stage_bytes(NPL, NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[pl_stage_bytes(NPL, NT)];
+  static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
+  const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
+  const int logical = xcd_logical(total);
+  if (logical < 0) return;
+  const int chunk = logical / g.n_blocks;
+  const int nb = logical - chunk * g.n_blocks;
+  const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
+  const int nta = min((c.z + 15) >> 4, NT);
+#define MOE_PL_ITEM(A) pfpl_item<PAIR, NPL, A, MT, NW, pl_ring(A)>(g, st0, st1, c.x, c.y, c.z, nb)
+  if (nta == NT) {
+    MOE_PL_ITEM(NT);
+    return;
+  }
+  switch (nta) {
+    case 1: if constexpr (NT > 1) MOE_PL_ITEM(1); break;
+    case 2: if constexpr (NT > 2) MOE_PL_ITEM(2); break;
+    case 3: if constexpr (NT > 3) MOE_PL_ITEM(3); break;
+    case 4: if constexpr (NT > 4) MOE_PL_ITEM(4); break;
+    default: if constexpr (NT > 5) MOE_PL_ITEM(5); break;
+  }
+#undef MOE_PL_ITEM
+}
+
+// fp32 rows -> [rows][NPL][K] bf16 rows: hi = bf16(a) and lo = bf16(a - hi)
+// (NPL 2), or the rounded row alone (NPL 1); output row r is activation row
+// map[r] / div (map NULL: row r); 8 values per thread
+template <int NPL>
+__global__ __launch_bounds__(256) void split_rows_kernel(const float *__restrict__ A, long long lda, long long rows,
+                                                         int K, const int32_t *__restrict__ map, int div,
+                                                         __bf16 *__restrict__ out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = K / 8;
+  if (i >= rows * per_row) return;
+  const long long row = i / per_row;
+  const int c = (int)(i - row * per_row);
+  const long long src = map ? (long long)(map[row] / div) : row;
+  const f32x4_t *p = reinterpret_cast<const f32x4_t *>(A + src * lda + c * 8);
+  const f32x4_t x0 = p[0], x1 = p[1];
+  bf16x8_t h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = e < 4 ? x0[e] : x1[e - 4];
+    __bf16 vh, vl;
+    split_bf16(v, vh, vl);
+    h[e] = vh;
+    l[e] = vl;
+  }
+  __bf16 *o = out + row * NPL * K + c * 8;
+  *reinterpret_cast<bf16x8_t *>(o) = h;
+  if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(o + K) = l;
+}
+
+}  // namespace
+
+// 16-row weight tiles per wave and matrix: 8 tiles per wave in all
+constexpr int PL_MT_PAIR = 4 * PREFILL_MX_NW / PL_NW;
+constexpr int PL_MT_SINGLE = 8 * PREFILL_MX_NW / PL_NW;
+
+int prefill_pl_rows_per_wg(bool pair) { return 16 * PL_NW * (pair ? PL_MT_PAIR : PL_MT_SINGLE); }
+
+hipError_t launch_prefill_planes(int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
+  if (a.chunks == nullptr || (npl != 1 && npl != 2) || a.K % KSTEP != 0) return hipErrorInvalidValue;
+  const dim3 gr((unsigned)grid), blk(64 * PL_NW);
+  if (npl == 2) {
+    if (pair) hipLaunchKernelGGL((prefill_pl_kernel<true, 2, PREFILL_NT, PL_MT_PAIR, PL_NW>), gr, blk, 0, st, a);
+    else hipLaunchKernelGGL((prefill_pl_kernel<false, 2, PREFILL_NT, PL_MT_SINGLE, PL_NW>), gr, blk, 0, st, a);
+  } else {
+    if (pair) hipLaunchKernelGGL((prefill_pl_kernel<true, 1, PREFILL_NT, PL_MT_PAIR, PL_NW>), gr, blk, 0, st, a);
+    else hipLaunchKernelGGL((prefill_pl_kernel<false, 1, PREFILL_NT, PL_MT_SINGLE, PL_NW>), gr, blk, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+size_t split_rows_bytes(long long rows, int K, int npl) { return (size_t)rows * npl * K * 2; }
+
+hipError_t launch_split_rows(int npl, const float *A, long long lda, long long rows, int K, const int32_t *map,
+                             int div, uint16_t *out, hipStream_t st) {
+  if ((npl != 1 && npl != 2) || K % 8 != 0) return hipErrorInvalidValue;
+  const long long n = rows * (K / 8);
+  const dim3 gr((unsigned)((n + 255) / 256)), blk(256);
+  __bf16 *o = reinterpret_cast<__bf16 *>(out);
+  if (npl == 2) hipLaunchKernelGGL(split_rows_kernel<2>, gr, blk, 0, st, A, lda, rows, K, map, div, o);
+  else hipLaunchKernelGGL(split_rows_kernel<1>, gr, blk, 0, st, A, lda, rows, K, map, div, o);
+  return hipGetLastError();
+}
+
+}  // namespace moe
