@@ -11,17 +11,21 @@
 // Work item = (chunk of <= 16 NT expert-sorted rows of one expert, block of
 // 16 NW MT weight rows per matrix), as for the fp32-staging kernel.  Here the
 // activations need no register work on their way to LDS: each K step's planes
-// are loaded straight into a two-stage LDS ring one step ahead.  Eight waves,
-// two per SIMD, each hold 4 weight tiles of 16 rows (gate and up of a SiTU
-// pair: 2 + 2), so the accumulators and operands fit the 256 registers of a
-// wave without spilling, and each SIMD interleaves two instruction streams.
-// The weights go to registers through a ring of 2 steps, or 4 for items of
-// one or two token tiles, whose steps are too short to cover a memory trip.
+// are loaded straight into an LDS ring (three stages, two for items of one or
+// two token tiles).  Eight waves, two per SIMD, each hold 4 weight tiles of
+// 16 rows (gate and up of a SiTU pair: 2 + 2), so the accumulators and
+// operands fit the 256 registers of a wave without spilling, and each SIMD
+// interleaves two instruction streams.  The weights go to registers through a
+// ring of 3 steps, or 4 for items of one or two token tiles, whose steps are
+// too short to cover a memory trip.
 //
 // LDS stage: [plane][token][16 cells of 16 bytes]; cell c of token t holds
-// octet c ^ (t & 15) of the token's 128-wide K step.  A wave load of 64 cells
-// covers 4 tokens, 16 lanes reading one token's 256 contiguous bytes; a
-// fragment read (16 tokens, one octet each) touches 16 different cells.
+// octet c ^ pl_swz(t) of the token's 128-wide K step.  A wave load of 64 cells
+// covers 4 tokens, 16 lanes reading one token's 256 contiguous bytes.  A
+// fragment read takes one octet of 16 tokens (one 256-byte row each); with
+// pl_swz(t) = t mod 16 such reads cost two LDS passes instead of one on
+// gfx950 (bank-conflict counter, measured by a probe), with the swizzle
+// below they cost one.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +35,8 @@ namespace {
 constexpr int KSTEP = 128;
 constexpr int PL_NW = 8;  // waves per work-group
 constexpr int pl_stage_bytes(int npl, int nt) { return npl * 16 * nt * 256; }
+// a bijection of 0..15: the even cells for tokens 0..7, the odd ones for 8..15
+MOE_DEV constexpr int pl_swz(int t) { return ((t << 1) & 15) ^ ((t >> 3) & 1); }
 
 // 16 bytes of LDS at addr + OFF, issued without waiting
 template <int OFF>
@@ -45,8 +51,11 @@ MOE_DEV void lds_wait16(u32x4_t &v) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N) : "memory");
 }
 
-template <bool PAIR, int NPL, int NTA, int MT, int NW, int RW>
-__device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8_t *st1, int expert, int row0,
+constexpr int pl_gcd(int a, int b) { return b == 0 ? a : pl_gcd(b, a % b); }
+
+// RW weight-ring slots, S LDS stages, LDS reads D fragments ahead
+template <bool PAIR, int NPL, int NTA, int MT, int NW, int RW, int S, int D>
+__device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *stage, int expert, int row0,
                                           int nrows, int nb) {
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
@@ -56,8 +65,8 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8
   constexpr int QI = 4 * NPL * NTA;     // 1 KB wave loads per stage
   constexpr int KQ = (QI + NW - 1) / NW;  // per wave (the last round may leave waves idle)
   static_assert(pl_stage_bytes(NPL, NTA) == QI * 1024, "whole wave loads");
-  static_assert(RW == 2 || RW == 4, "weight ring of 2 or 4 slots");
-  uint8_t *stage[2] = {st0, st1};
+  static_assert(RW >= 2 && RW <= 4 && (S == 2 || S == 3), "ring shapes");
+  constexpr int U = RW * S / pl_gcd(RW, S);  // steps per unrolled round: slot and stage repeat
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,14 +110,18 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8
   for (int k = 0; k < KQ; ++k) {
     const int q = min(64 * (wave + NW * k), 64 * (QI - 1)) + lane;
     const int p = q / (16 * CT), rem = q - p * 16 * CT;
-    const int tok = rem >> 4, oct = (rem & 15) ^ (tok & 15);
+    const int tok = rem >> 4, oct = (rem & 15) ^ pl_swz(tok & 15);
     const int tt = tok < nrows ? tok : 0;
     const long long arow = g.a_map ? (long long)(g.a_map[row0 + tt] / g.a_div) : (long long)tt;
     qoff[k] = (uint32_t)((arow * lda + (long long)p * K) * 2 + oct * 16);
   }
-  // the memory operations of one step: KQ loads into LDS stage sb, then the
-  // codes and scales of each weight tile into ring slot wb
+  // the memory operations of one step: KQ loads into LDS stage sb (a wave
+  // past the stage's last load skips it: KQ_MIN of them are issued by every
+  // wave), then the codes and scales of each weight tile into ring slot wb.
+  // The LDS loads go first: they feed the next step, and loads complete in
+  // the order they are issued.
   constexpr int NOPS = KQ + 2 * NTILE;
+  constexpr int KQ_MIN = QI / NW;
   auto issue_op = [&](int o, int sb, int wb, int sa, int sw) {
     if (o < KQ) {
       const int ii = wave + NW * o;  // uniform
@@ -133,24 +146,25 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8
 
   // fragment reads: in sub-step j (K 32 wide) lane (token r16, group kg) takes
   // octet 4 kg + j of its token, the K positions of its weight codes 8j .. 8j+7
-  uint32_t la[2][4];
+  uint32_t la[S][4];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < S; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage[b]) + (uint32_t)(r16 * 256 + (((4 * kg + j) ^ r16) << 4));
+    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage[b]) + (uint32_t)(r16 * 256 + (((4 * kg + j) ^ pl_swz(r16)) << 4));
 
   // step s from LDS stage SB and weight slot WB; its fragments f = (sub-step
-  // j, plane p, token tile n) are read from LDS two ahead of their MFMAs; the
+  // j, plane p, token tile n) are read from LDS D ahead of their MFMAs; the
   // weights of sub-step j + 1 are converted tile by tile over sub-step j's
-  // fragments; the loads of LDS stage s + 1 and weight step s + RW - 1 go out
-  // over the first half of the step
+  // fragments; over the first half of the step go out the loads of LDS stage
+  // s + S - 1 (stage SN, which held step s - 1) and then of weight step
+  // s + RW - 1 (slot WN, which held step s - 1).  Step indices past the last
+  // step reload the last one; before the first (the prologue) they load step 0.
   auto compute = [&](auto sbc, auto wbc, int s) {
     constexpr int SB = decltype(sbc)::value, WB = decltype(wbc)::value;
-    constexpr int WN = (WB + RW - 1) % RW;  // the slot of step s - 1, free again
-    const int sa = min(s + 1, nks - 1), sw = min(s + RW - 1, nks - 1);
+    constexpr int WN = (WB + RW - 1) % RW, SN = (SB + S - 1) % S;
+    const int sa = min(s + S - 1, nks - 1), sw = min(s + RW - 1, nks - 1);
     constexpr int FJ = NPL * NTA;  // fragments per sub-step
     constexpr int F = 4 * FJ;
-    constexpr int D = 2;
     constexpr int J = (NOPS + F / 2 - 1) / (F / 2);  // loads issued per fragment
     u32x4_t bq[D + 1];
     bf16x8_t wa[2][NTILE];
@@ -161,7 +175,7 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8
       constexpr int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
       lds_read16<p * PLB + n * 16 * 256>(la[SB][j], bq[f % (D + 1)]);
     };
-    static_for<D>([&](auto fc) { issue(fc); });
+    static_for<(D < F ? D : F)>([&](auto fc) { issue(fc); });
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       scl[t] = scale_of(t);
@@ -183,35 +197,42 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bv, acc[t][n]);
 #pragma unroll
-      for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, SB ^ 1, WN, sa, sw);
+      for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, SN, WN, sa, sw);
     });
   };
-  // after step s: stage s + 1 (requested during s) must be in LDS for every
-  // wave, and weight step s + 1 in registers; weight loads issued after the
-  // last LDS load of the step may stay in flight
-  constexpr int VM_LEFT = RW > 2 ? 2 * NTILE : 0;
-  auto step = [&](auto ic, int s) {
-    constexpr int I = decltype(ic)::value;
-    compute(std::integral_constant<int, I & 1>{}, std::integral_constant<int, I % RW>{}, s);
+  // After step s, stage s + 1 must be in LDS for every wave and weight step
+  // s + 1 in registers.  Every step issues [LDS loads][weight loads]; stage
+  // s + 1 went out in step s + 2 - S, weight step s + 1 in step s + 2 - RW, and
+  // the loads issued after the later of the two may stay in flight.
+  constexpr int PER_STEP = KQ_MIN + 2 * NTILE;
+  constexpr int AFTER_A = 2 * NTILE + (S - 2) * PER_STEP, AFTER_W = (RW - 2) * PER_STEP;
+  constexpr int VM_LEFT = AFTER_A < AFTER_W ? AFTER_A : AFTER_W;
+  static_assert(VM_LEFT < 64, "vmcnt range");
+  auto wait_and_sync = [&]() {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_LEFT));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);  // keep the next step's register work behind the wait
   };
+  auto step = [&](auto ic, int s) {
+    constexpr int I = decltype(ic)::value;
+    compute(std::integral_constant<int, I % S>{}, std::integral_constant<int, I % RW>{}, s);
+    wait_and_sync();
+  };
 
-  // prologue: stage 0 and weight steps 0 .. RW - 2
+  // prologue: the loads of steps -M .. -1, in the same pattern as every step
+  constexpr int M = (RW > S ? RW : S) - 1;
+  static_for<M>([&](auto ic) {
+    constexpr int r = decltype(ic)::value - M;  // -M .. -1
+    constexpr int SN = ((r + S - 1) % S + S) % S, WN = ((r + RW - 1) % RW + RW) % RW;
+    const int sa = max(min(r + S - 1, nks - 1), 0), sw = max(min(r + RW - 1, nks - 1), 0);
 #pragma unroll
-  for (int o = 0; o < KQ; ++o) issue_op(o, 0, 0, 0, 0);
-  static_for<RW - 1>([&](auto wc) {
-    constexpr int w = decltype(wc)::value;
-#pragma unroll
-    for (int o = KQ; o < NOPS; ++o) issue_op(o, 0, w, 0, min(w, nks - 1));
+    for (int o = 0; o < NOPS; ++o) issue_op(o, SN, WN, sa, sw);
   });
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((RW - 2) * 2 * NTILE));
-  __builtin_amdgcn_s_barrier();
+  wait_and_sync();
   int s = 0;
-  for (; s + RW - 1 < nks; s += RW) static_for<RW>([&](auto ic) { step(ic, s + decltype(ic)::value); });
-  // tail: s is a multiple of RW (even), so step i keeps stage i & 1 and slot i
-  static_for<RW - 1>([&](auto ic) {
+  for (; s + U - 1 < nks; s += U) static_for<U>([&](auto ic) { step(ic, s + decltype(ic)::value); });
+  // tail: s is a multiple of U, so step i keeps stage i % S and slot i % RW
+  static_for<U - 1>([&](auto ic) {
     if (s + decltype(ic)::value < nks) step(ic, s + decltype(ic)::value);
   });
   // drain the loads past the last step before the LDS is reused
@@ -253,14 +274,20 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *st0, uint8
 
 // weight-ring slots: items with few token tiles stream their weights with
 // little compute per step, so they keep more steps in flight
-constexpr int pl_ring(int nta) { return nta <= 2 ? 4 : 2; }
+constexpr int pl_ring(int nta) { return nta <= 2 ? 4 : 3; }
+// LDS stages
+constexpr int pl_stages(int nta) { return nta >= 3 ? 3 : 2; }
+constexpr int PL_D = 2;  // fragment reads ahead of their MFMAs
+constexpr bool pl_any_three(int nt) { return nt > 0 && (pl_stages(nt) == 3 || pl_any_three(nt - 1)); }
 
 template <bool PAIR, int NPL, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
-  // two activation stages (separate objects, so waits on one stage's loads do
-  // not cover the other)
+  // activation stages (separate objects, so waits on one stage's loads do
+  // not cover the others)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[pl_stage_bytes(NPL, NT)];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[pl_stage_bytes(NPL, NT)];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[pl_any_three(NT) ? pl_stage_bytes(NPL, NT) : 16];
+  uint8_t *const stage[3] = {st0, st1, st2};
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
   const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
   const int logical = xcd_logical(total);
@@ -269,7 +296,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
   const int nb = logical - chunk * g.n_blocks;
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
-#define MOE_PL_ITEM(A) pfpl_item<PAIR, NPL, A, MT, NW, pl_ring(A)>(g, st0, st1, c.x, c.y, c.z, nb)
+#define MOE_PL_ITEM(A) \
+  pfpl_item<PAIR, NPL, A, MT, NW, pl_ring(A), pl_stages(A), PL_D>(g, stage, c.x, c.y, c.z, nb)
   if (nta == NT) {
     MOE_PL_ITEM(NT);
     return;
