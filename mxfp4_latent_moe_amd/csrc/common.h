@@ -78,13 +78,14 @@ MOE_DEV constexpr int aff2_octet(int h, int kg, int jj) { return 8 * h + 2 * kg 
 // fp32 value of the bf16 in the low 16 bits of a pattern
 MOE_DEV float bf16_lo_to_float(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-// tanh in fp32 from two identities: the odd Taylor series of tanh (Bernoulli-
-// number coefficients, terms to x^11) for |x| < 0.4, where the first omitted
-// term is below 1e-7 of the value, and tanh|x| = (1 - e) / (1 + e) with
-// e = exp(-2|x|) above, where 1 - e does not cancel.  The exponential and the
-// reciprocal are the hardware ones (about 1 ulp); worst relative error over
-// the fp32 range about 2.4e-7.
-MOE_DEV float tanh_f32(float x) {
+// tanh x in fp32 as a fraction num / den, from two identities: the odd
+// Taylor series of tanh (Bernoulli-number coefficients, terms to x^11) over 1
+// for |x| < 0.4, where the first omitted term is below 1e-7 of the value, and
+// sign(x) (1 - e) over (1 + e) with e = exp(-2|x|) above, where 1 - e does not
+// cancel.  The exponential is the hardware one (about 1 ulp); after one
+// hardware reciprocal the worst relative error over the fp32 range is about
+// 2.4e-7.
+MOE_DEV void tanh_frac_f32(float x, float &num, float &den) {
   const float ax = fabsf(x);
   const float x2 = x * x;
   float p = -1382.0f / 155925.0f;
@@ -94,20 +95,21 @@ MOE_DEV float tanh_f32(float x) {
   p = fmaf(p, x2, -1.0f / 3.0f);
   const float series = fmaf(x * x2, p, x);
   const float e = __builtin_amdgcn_exp2f(ax * -2.8853900817779268f);  // exp(-2|x|) as 2^(-2|x| log2 e)
-  const float identity = copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), x);
-  return ax < 0.4f ? series : identity;
+  const bool small = ax < 0.4f;
+  num = small ? series : copysignf(1.0f - e, x);
+  den = small ? 1.0f : 1.0f + e;
 }
 
-// logistic sigmoid 1 / (1 + exp(-g)) through the hardware exp2 and reciprocal
-MOE_DEV float sigmoid_f32(float g) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
-}
-
-// SiTU-GLU in fp32: beta*tanh(g/beta)*sigmoid(g) * beta_lin*tanh(u/beta_lin).
+// SiTU-GLU in fp32: beta*tanh(g/beta)*sigmoid(g) * beta_lin*tanh(u/beta_lin),
+// with sigmoid(g) = 1 / (1 + exp(-g)).  The three denominators share one
+// hardware reciprocal: for g below about -88, 1 + exp(-g) is +inf and the
+// result is 0, the limit of the product.
 MOE_DEV float situ_glu(float g, float u, float beta, float beta_lin) {
-  const float tg = tanh_f32(g * __builtin_amdgcn_rcpf(beta));
-  const float tu = tanh_f32(u * __builtin_amdgcn_rcpf(beta_lin));
-  return beta * tg * sigmoid_f32(g) * (beta_lin * tu);
+  float ng, dg, nu, du;
+  tanh_frac_f32(g * __builtin_amdgcn_rcpf(beta), ng, dg);
+  tanh_frac_f32(u * __builtin_amdgcn_rcpf(beta_lin), nu, du);
+  const float ds = 1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return (beta * ng) * (beta_lin * nu) * __builtin_amdgcn_rcpf(dg * du * ds);
 }
 
 MOE_DEV int lane_id() { return threadIdx.x & 63; }

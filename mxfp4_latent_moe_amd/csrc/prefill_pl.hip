@@ -65,7 +65,7 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   constexpr int QI = 4 * NPL * NTA;     // 1 KB wave loads per stage
   constexpr int KQ = (QI + NW - 1) / NW;  // per wave (the last round may leave waves idle)
   static_assert(pl_stage_bytes(NPL, NTA) == QI * 1024, "whole wave loads");
-  static_assert(RW >= 2 && RW <= 4 && (S == 2 || S == 3), "ring shapes");
+  static_assert(RW >= 2 && RW <= 8 && (S == 2 || S == 3), "ring shapes");
   constexpr int U = RW * S / pl_gcd(RW, S);  // steps per unrolled round: slot and stage repeat
 
   const int tid = threadIdx.x;
