@@ -103,7 +103,7 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
 
 // two-bank call: a chunk list and count per bank, then the split-K partials
 struct TwoBankWs {
-  size_t chunks[2], count[2], partial, total;
+  size_t chunks[2], count[2], partial, planes, sums, total;
   GemmPlan plan;
 };
 TwoBankWs two_bank_ws(const moe_shape *s, int P, bool gateup) {
@@ -116,7 +116,13 @@ TwoBankWs two_bank_ws(const moe_shape *s, int P, bool gateup) {
   w.chunks[1] = w.count[0] + ALIGN;
   w.count[1] = w.chunks[1] + list;
   w.partial = w.count[1] + ALIGN;
-  w.total = w.partial + align_up(w.plan.partial_bytes);
+  w.planes = w.partial + align_up(w.plan.partial_bytes);
+  // the tiled path's bf16 activation planes and (for an affine bank) their
+  // 64-element group sums, at most P rows as in the single-bank call
+  const int K = gateup ? s->latent : s->inter;
+  const bool tiled = w.plan.variant == 3;
+  w.sums = w.planes + (tiled ? align_up(split_rows_bytes(P, K, s->operand_mode == MOE_OPND_BF16 ? 1 : 2)) : 0);
+  w.total = w.sums + (tiled && K % 512 == 0 ? align_up(row_sums_bytes(P, K)) : 0);
   return w;
 }
 
@@ -523,17 +529,18 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
         const long long rows = (gathered && !split_gathers) ? (long long)a_rows : (long long)P;
         uint16_t *planes = reinterpret_cast<uint16_t *>(wsp(ws, w.mx));
         if (launch_split_rows(npl, static_cast<const float *>(A), K, rows, K, split_gathers ? sorted_pair : nullptr,
-                              s->top_k, planes, st) != hipSuccess)
+                              s->top_k, planes, nullptr, st) != hipSuccess)
           return MOE_EHIP;
         a.A = planes;
         a.lda = (long long)npl * K;
         a.a_rows = rows;
         if (split_gathers) a.a_map = nullptr;
       }
-      a.n_blocks = (N + prefill_pl_rows_per_wg(gateup) - 1) / prefill_pl_rows_per_wg(gateup);
+      const int rows_wg = prefill_pl_rows_per_wg(gateup, W_MXFP4);
+      a.n_blocks = (N + rows_wg - 1) / rows_wg;
       const long long logical = (long long)w.plan.max_chunks * a.n_blocks;
       a.grid_logical = (int)logical;
-      if (launch_prefill_planes(npl, gateup, a, (logical + 7) / 8 * 8, st) != hipSuccess) return MOE_EHIP;
+      if (launch_prefill_planes(W_MXFP4, npl, gateup, a, (logical + 7) / 8 * 8, st) != hipSuccess) return MOE_EHIP;
       return MOE_OK;
     }
     GemmPlan pl = w.plan;
@@ -636,6 +643,35 @@ int moe_grouped_gemm_two_bank(const moe_shape *s, int op, int P, const int32_t *
     a.beta = s->beta;
     a.beta_lin = s->beta_lin;
     const int afmt = a_dtype == MOE_DT_BF16 ? A_BF16 : afmt_of(s);
+    // the tiled path reads bf16 activation planes: bf16 activations as they
+    // are, fp32 ones split once (over the same rows as in the single-bank
+    // call); an affine bank also takes the rows' 64-element group sums
+    const bool tiled = w.plan.variant == 3;
+    int npl = 1;
+    if (tiled) {
+      const bool split_gathers = gathered && a_rows > P;
+      const long long rows = (gathered && !split_gathers) ? (long long)a_rows : (long long)P;
+      const int32_t *map = split_gathers ? sorted_pair : nullptr;
+      float *sums = any_affine ? reinterpret_cast<float *>(wsp(ws, w.sums)) : nullptr;
+      if (a_dtype == MOE_DT_F32) {
+        npl = afmt == A_F32_SPLIT ? 2 : 1;
+        uint16_t *planes = reinterpret_cast<uint16_t *>(wsp(ws, w.planes));
+        if (launch_split_rows(npl, static_cast<const float *>(A), K, rows, K, map, s->top_k, planes, sums, st) !=
+            hipSuccess)
+          return MOE_EHIP;
+        a.A = planes;
+        a.lda = (long long)npl * K;
+        a.a_rows = rows;
+        if (split_gathers) a.a_map = nullptr;
+      } else if (sums) {
+        // bf16 activations are their own plane (gathered through sorted_pair
+        // as given); their group sums follow the rows the split would have
+        if (launch_row_sums(static_cast<const uint16_t *>(A), K, rows, K, map, s->top_k, sums, st) != hipSuccess)
+          return MOE_EHIP;
+        a.asum_sorted = split_gathers ? 1 : 0;
+      }
+      a.asum = sums;
+    }
     // bank A owns experts [0, E_a), bank B [E_a, E): each bank's chunks come from
     // its slice of the offsets on the device, so its sorted rows are found with
     // no host round trip
@@ -661,16 +697,22 @@ int moe_grouped_gemm_two_bank(const moe_shape *s, int op, int P, const int32_t *
       ab.chunks = chunks;
       ab.chunk_count = count;
       GemmPlan pl = w.plan;
-      if (pl.variant == 3) {
-        // the tiled kernel's affine variant covers fewer weight rows per work-group
-        const int rows_wg = prefill_rows_per_wg_fmt(gateup, aff ? W_AFF2 : W_MXFP4);
+      if (tiled) {
+        // weight rows per work-group of the plane kernel in the bank's format
+        const int rows_wg = prefill_pl_rows_per_wg(gateup, aff ? W_AFF2 : W_MXFP4);
         pl.n_blocks = (N + rows_wg - 1) / rows_wg;
         ab.n_blocks = pl.n_blocks;
       }
       pl.max_chunks = P / pl.chunk_rows + (ne < P ? ne : P);
       pl.grid_logical = (long long)pl.max_chunks * pl.n_blocks * pl.splits;
       ab.grid_logical = (int)pl.grid_logical;
-      if (launch_gemm(pl, aff ? W_AFF2 : W_MXFP4, afmt, gateup, ab, st) != hipSuccess) return MOE_EHIP;
+      if (tiled) {
+        if (launch_prefill_planes(aff ? W_AFF2 : W_MXFP4, npl, gateup, ab, (pl.grid_logical + 7) / 8 * 8, st) !=
+            hipSuccess)
+          return MOE_EHIP;
+      } else if (launch_gemm(pl, aff ? W_AFF2 : W_MXFP4, afmt, gateup, ab, st) != hipSuccess) {
+        return MOE_EHIP;
+      }
       e0 += ne;
     }
     if (w.plan.splits > 1) {

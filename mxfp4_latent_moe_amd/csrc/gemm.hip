@@ -465,8 +465,8 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair) {
     p.variant = 3;
     p.nt = PREFILL_NT;
     p.chunk_rows = 16 * PREFILL_NT;
-    p.mt = prefill_rows_per_wg(pair) / 64;
-    p.n_blocks = ceil_div(N, prefill_rows_per_wg(pair));
+    p.mt = prefill_pl_rows_per_wg(pair, W_MXFP4) / 64;
+    p.n_blocks = ceil_div(N, prefill_pl_rows_per_wg(pair, W_MXFP4));
     p.splits = 1;
   }
   p.max_chunks = P / p.chunk_rows + (E < P ? E : P);

@@ -25,6 +25,8 @@ struct GemmArgs {
   const void *W0, *W1;    // weights [E][N][K] bf16 or packed [E][N][K/2]; W1 for SiTU pairs
   const uint8_t *S0, *S1; // e8m0 scales [E][N][K/32] (MXFP4), bf16 scales [E][N][K/64] (W_AFF2)
   const uint16_t *B0, *B1; // bf16 biases [E][N][K/64] (W_AFF2)
+  const float *asum;      // W_AFF2 on the plane kernel: 64-element group sums of A's rows [rows][K/64]
+  int asum_sorted;        // asum rows follow the sorted rows (a_map not applied to them)
   long long w_estride;    // per-expert stride of W (elements for bf16, bytes for packed)
   long long s_estride;    // per-expert stride of S in bytes
   int N, K;
@@ -75,9 +77,6 @@ constexpr int PERSIST_ROWS = 4;
 // tiled prefill kernel: 16-token tiles per chunk, 16-row weight tiles per wave
 // and matrix, waves per work-group
 constexpr int PREFILL_NT = 6;
-constexpr int PREFILL_MT_PAIR = 2;
-constexpr int PREFILL_MT_SINGLE = 4;
-constexpr int PREFILL_NW = 8;
 constexpr int PREFILL_MX_NW = 4;  // MX-scaled variant: one wave per SIMD
 constexpr int PREFILL_MX_MT_PAIR = 4;
 constexpr int PREFILL_MX_MT_SINGLE = 8;
@@ -104,17 +103,22 @@ int stream_rows_per_wg(int wfmt, bool pair);
 int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
 hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st);
-int prefill_rows_per_wg(bool pair);
-int prefill_rows_per_wg_fmt(bool pair, int wfmt);
 int prefill_mx_rows_per_wg(bool pair);
 // tiled prefill kernel over bf16 activation planes ([rows][npl][K]: hi then lo,
-// or the rounded row), MXFP4 weights; and the fp32 -> planes split
-int prefill_pl_rows_per_wg(bool pair);
-hipError_t launch_prefill_planes(int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st);
+// or the rounded row), MXFP4 or affine 2-bit weights (affine: a.asum holds the
+// activation rows' 64-element group sums); the fp32 -> planes split (with the
+// group sums when sums != nullptr; out == nullptr: sums only) and the group
+// sums of bf16 rows
+int prefill_pl_rows_per_wg(bool pair, int wfmt);
+hipError_t launch_prefill_planes(int wfmt, int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st);
 size_t split_rows_bytes(long long rows, int K, int npl);
+size_t row_sums_bytes(long long rows, int K);
 // map != nullptr: output row r is activation row map[r] / div
 hipError_t launch_split_rows(int npl, const float *A, long long lda, long long rows, int K, const int32_t *map,
-                             int div, uint16_t *out, hipStream_t st);
+                             int div, uint16_t *out, float *sums, hipStream_t st);
+hipError_t launch_row_sums(const uint16_t *A, long long lda, long long rows, int K, const int32_t *map, int div,
+                           float *sums, hipStream_t st);
+// the MX-scaled tiled kernel (A_MX8X3 / A_MX6X3 activations, MXFP4 weights)
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
                                hipStream_t st);
 size_t mx8_split_bytes(long long rows, int K);

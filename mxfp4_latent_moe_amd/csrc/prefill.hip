@@ -1,24 +1,11 @@
-// Tiled GEMM for prefill-sized work: MXFP4 expert segments (grouped).  The
-// dense bf16 products of the layer at prefill sizes run on dense.hip's tiles.
+// MX-scaled tiled GEMM for prefill-sized MXFP4 expert segments (the MX8X3
+// and MX6X3 operand modes); bf16 and fp32 activations run on the plane kernel
+// of prefill_pl.hip, the dense bf16 products of the layer on dense.hip's
+// tiles.
 //
 // Work item = (chunk of <= 16*NT expert-sorted token rows of one expert,
-// block of 64*MT weight rows).  Weight rows are the MFMA's M side, tokens its
-// N side (v_mfma_f32_16x16x32_bf16), so each wave dequantises only its own
-// weight rows and every dequantised fragment feeds NT (x2 for hi + lo) MFMAs.
-//
-// Per 128-wide K step:
-//  * weights: one 16-byte buffer load per lane per 16-row tile (32 e2m1 codes
-//    = one scale group of one row), issued a full step before use, converted
-//    in registers by the scaled fp4 -> bf16 instruction;
-//  * activations: the chunk's rows are loaded one step ahead into registers,
-//    split into bf16 hi + lo (or rounded), and written to a double-buffered
-//    LDS tile [octet][token ^ octet][8] -- the XOR swizzle keeps both the
-//    octet-wise writes and the token-wise fragment reads free of bank
-//    conflicts;
-//  * one barrier per step.
-// The item body is specialised on the number of active 16-token tiles, so the
-// K loop is straight-line code and token tiles past the chunk's last row cost
-// nothing.
+// block of 16*NW*MT weight rows).  Weight rows are the MFMA's M side, tokens
+// its N side, so each wave holds only its own weight rows.
 #include <type_traits>
 
 #include "common.h"
@@ -28,380 +15,6 @@ namespace moe {
 namespace {
 
 constexpr int KSTEP = 128;
-
-// One work item with NTA active 16-token tiles (the K loop has no branches).
-template <int WF, int AF, bool PAIR, int NTA, int MT, int NW>
-__device__ __forceinline__ void pf_item(const GemmArgs &g, __bf16 *lds_base, float *gsum, int expert, int row0,
-                                        int nrows, int nb) {
-  constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;  // LDS planes (hi, lo)
-  constexpr int NMAT = PAIR ? 2 : 1;
-  constexpr int NTILE = NMAT * MT;                  // 16-row weight tiles per wave
-  constexpr int CT = 16 * NTA;                      // staged tokens
-  constexpr int ROWS_WG = 16 * NW * MT;             // weight rows per matrix per work-group
-  constexpr int PLANE = CT * KSTEP;                 // bf16 elements per plane per stage
-  constexpr int AW = (AF == A_BF16) ? 1 : 2;        // 16-byte loads per staged octet
-  constexpr int RPP = 4 * NW;                       // token rows staged per pass (16 threads a row)
-  constexpr int NPASS = (CT + RPP - 1) / RPP;       // staging passes per K step
-  auto lds = [&](int b, int p) { return lds_base + (b * NPL + p) * PLANE; };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int kg = lane >> 4;
-  const int r16 = lane & 15;
-  const int N = g.N, K = g.K;
-  const int nks = K / KSTEP;
-
-  // ---- weight rows of this wave: buffer resources per matrix, offsets per tile.
-  // MXFP4: lane group kg's 16 bytes of a 128-wide K step are its 32 codes (one
-  // scale group); bf16: its 64 bytes (32 values), one 16-byte load per sub-step.
-  // Affine 2-bit weights: the codes enter the MFMA as exact integers, each
-  // instruction inside one 64-element group (aff2_octet: a lane loads dwords
-  // kg and 4 + kg of a step's codes); a group's two instructions sum into a
-  // temporary that is added times the group's scale of each output row, and
-  // the bias part is one more product at the end of the item.
-  constexpr bool FP4 = WF == W_MXFP4;
-  constexpr bool AFF = WF == W_AFF2;
-  static_assert(FP4 || AFF, "MXFP4 or affine 2-bit weights");
-  const int ngroups = K / 64;
-  const uint32_t row_bytes = FP4 ? K / 2 : K / 4, srow_bytes = FP4 ? K / 32 : ngroups * 2;
-  constexpr uint32_t STEP_BYTES = FP4 ? 64u : 32u;
-  typedef typename std::conditional<FP4, u32x4_t, u32x2_t>::type WQ;
-  __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
-#pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) {
-    const uint8_t *W = static_cast<const uint8_t *>(mat ? g.W1 : g.W0) + expert * g.w_estride;
-    wr[mat] = make_rsrc(W, (uint32_t)N * row_bytes);
-    sr[mat] = make_rsrc((mat ? g.S1 : g.S0) + expert * g.s_estride, (uint32_t)N * srow_bytes);
-  }
-  const int wrow_base = nb * ROWS_WG + wave * 16 * MT;
-  uint32_t woff[NTILE], soff[NTILE];
-#pragma unroll
-  for (int t = 0; t < NTILE; ++t) {
-    const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
-    woff[t] = (uint32_t)n * row_bytes + kg * (FP4 ? 16 : 4);
-    soff[t] = (uint32_t)n * srow_bytes;
-  }
-
-  // ---- activation rows this thread stages: token (tid >> 4) + RPP i, octet tid & 15
-  // Gathered rows index A from its start (the boundary keeps A below 2^31
-  // bytes then); rows in sorted order are addressed from the chunk's first
-  // row, so the number of sorted rows is not limited by 32-bit offsets.
-  const int a_oct = tid & 15;
-  const int esz = (AF == A_BF16) ? 2 : 4;
-  const char *abase = static_cast<const char *>(g.A) + (g.a_map ? 0LL : (long long)row0 * g.lda * esz);
-  const long long abytes = (g.a_map ? g.a_rows : (long long)nrows) * g.lda * esz;
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(abase, (uint32_t)min(abytes, 0x7FFFFFF0LL));
-  uint32_t aoff[NPASS];
-  bool alive[NPASS];
-#pragma unroll
-  for (int i = 0; i < NPASS; ++i) {
-    const int r = (tid >> 4) + RPP * i;
-    alive[i] = r < nrows;
-    const int rr = min(r, nrows - 1);
-    const long long arow = g.a_map ? (long long)(g.a_map[row0 + rr] / g.a_div) : (long long)rr;
-    aoff[i] = (uint32_t)((arow * g.lda + a_oct * 8) * esz);
-  }
-
-  WQ wq[2][NTILE];          // codes of one K step per stage
-  uint32_t wsc[2][NTILE];
-  u32x4_t aq[NPASS][AW];
-
-  // loads past the last K step re-read the last one (never past the rows)
-  auto load_w = [&](int b, int s) {
-    s = min(s, nks - 1);
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) {
-      if constexpr (FP4) {
-        wq[b][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)s * STEP_BYTES);
-      } else {
-        wq[b][t] = u32x2_t{buf_load4(wr[t / MT], woff[t], (uint32_t)s * STEP_BYTES),
-                           buf_load4(wr[t / MT], woff[t] + 16u, (uint32_t)s * STEP_BYTES)};
-      }
-      wsc[b][t] = buf_load4(sr[t / MT], soff[t], (uint32_t)s * 4u);
-    }
-  };
-  auto load_a = [&](int s) {
-    s = min(s, nks - 1);
-    const uint32_t so = (uint32_t)s * KSTEP * esz;
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-#pragma unroll
-      for (int h = 0; h < AW; ++h) aq[i][h] = buf_load16(ar, aoff[i] + 16 * h, so);
-    }
-  };
-  // swizzled LDS slot of (octet, token): octet-major, token XOR octet
-  auto slot = [](int oct, int tok) { return (oct * CT + (tok ^ oct)) * 8; };
-  // step sa's activations into LDS stage b; for affine weights in the
-  // convert's element order, with each row's two 64-element group sums of the
-  // staged values written to gsum[group][row]
-  auto store_a = [&](int b, int sa) {
-    sa = min(sa, nks - 1);
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = (tid >> 4) + RPP * i;
-      float part = 0.f;
-      if constexpr (AF == A_BF16) {
-        u32x4_t v = alive[i] ? aq[i][0] : u32x4_t{0, 0, 0, 0};
-        if constexpr (AFF) {
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-            part += __uint_as_float(v[h] << 16) + __uint_as_float(v[h] & 0xFFFF0000u);
-#pragma unroll
-          for (int h = 0; h < 4; h += 2) {  // bf16 elements 0..7 -> 0, 2, 1, 3, 4, 6, 5, 7
-            const uint32_t a0 = v[h], a1 = v[h + 1];
-            v[h] = (a0 & 0xFFFFu) | (a1 << 16);
-            v[h + 1] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-          }
-        }
-        if (CT % RPP == 0 || r < CT) *reinterpret_cast<u32x4_t *>(lds(b, 0) + slot(a_oct, r)) = v;
-      } else {
-        bf16x8_t hi, lo;
-#pragma unroll
-        for (int e0 = 0; e0 < 8; ++e0) {
-          const int e = AFF ? aff2_perm(e0) : e0;  // slot e0 holds element e
-          const float f = alive[i] ? __uint_as_float(aq[i][e >> 2][e & 3]) : 0.f;
-          if constexpr (AF == A_F32_SPLIT) {
-            __bf16 h, l;
-            split_bf16(f, h, l);
-            hi[e0] = h;
-            lo[e0] = l;
-            part += f;
-          } else {
-            hi[e0] = to_bf16(f);
-            part += from_bf16(hi[e0]);
-          }
-        }
-        if (CT % RPP == 0 || r < CT) {
-          *reinterpret_cast<bf16x8_t *>(lds(b, 0) + slot(a_oct, r)) = hi;
-          if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(lds(b, NPL - 1) + slot(a_oct, r)) = lo;
-        }
-      }
-      if constexpr (AFF) {
-        // the eight octets of a group sit in lanes a_oct ^ 1, 2, 4 of the same row
-        part += __shfl_xor(part, 1, 64);
-        part += __shfl_xor(part, 2, 64);
-        part += __shfl_xor(part, 4, 64);
-        if ((a_oct & 7) == 0 && (CT % RPP == 0 || r < CT)) gsum[(2 * sa + (a_oct >> 3)) * CT + r] = part;
-      }
-    }
-  };
-
-  f32x4_t acc[NTILE][NTA];
-#pragma unroll
-  for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-    for (int n = 0; n < NTA; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Fragments f = (sub-step j, plane p, token tile n) in order; each B fragment
-  // is read from LDS two fragments ahead of its MFMAs, and the weights of
-  // sub-step j+1 are converted while sub-step j's MFMAs run.
-  auto compute = [&](int b, int s) {
-    float scl[NTILE];
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[b][t] >> (8 * kg)) & 0xFFu);
-    constexpr int FJ = NPL * NTA;  // fragments per sub-step
-    constexpr int F = 4 * FJ;      // fragments per K step
-    constexpr int D = 2;           // read-ahead distance
-    auto rd = [&](int f) {
-      const int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
-      return *reinterpret_cast<const bf16x8_t *>(lds(b, p) + slot(4 * kg + j, 16 * n + r16));
-    };
-    auto wfrag = [&](int j, int t) { return fp4x8_to_bf16(wq[b][t][j], scl[t]); };
-    bf16x8_t bq[D + 1];
-#pragma unroll
-    for (int f = 0; f < D; ++f) bq[f] = rd(f);
-    bf16x8_t wa[2][NTILE];
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) wa[0][t] = wfrag(0, t);
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const int j = f / FJ, n = f % NTA;
-      if (f + D < F) bq[(f + D) % (D + 1)] = rd(f + D);
-      if (f % FJ == 0 && j + 1 < 4) {
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) wa[(j + 1) & 1][t] = wfrag(j + 1, t);
-      }
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bq[f % (D + 1)], acc[t][n]);
-    }
-    // let the scheduler interleave the LDS reads with the MFMAs of this region
-    __builtin_amdgcn_iglp_opt(0);
-  };
-  // affine weights: one K step, group by group
-  auto compute_aff = [&](int b, int s) {
-    (void)s;
-    float sc[NTILE][2][4];  // group scales of the lane's output rows 4 kg + r
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t sw = (uint32_t)__shfl((int)wsc[b][t], 4 * kg + r, 64);
-        sc[t][0][r] = bf16_lo_to_float(sw);
-        sc[t][1][r] = bf16_lo_to_float(sw >> 16);
-      }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4_t tmp[NTILE][NTA];
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-        for (int n = 0; n < NTA; ++n) tmp[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        bf16x8_t wa[NTILE];
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-          const uint32_t d = wq[b][t][h];
-          const uint32_t y = d & 0x33333333u, z = (d >> 2) & 0x33333333u;
-          wa[t] = jj ? aff2x8_to_bf16<2>(y, z) : aff2x8_to_bf16<0>(y, z);
-        }
-#pragma unroll
-        for (int p = 0; p < NPL; ++p)
-#pragma unroll
-          for (int n = 0; n < NTA; ++n) {
-            const bf16x8_t bq =
-                *reinterpret_cast<const bf16x8_t *>(lds(b, p) + slot(aff2_octet(h, kg, jj), 16 * n + r16));
-#pragma unroll
-            for (int t = 0; t < NTILE; ++t) tmp[t][n] = mfma_16x16x32(wa[t], bq, tmp[t][n]);
-          }
-      }
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t)
-#pragma unroll
-        for (int n = 0; n < NTA; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[t][n][r] = fmaf(sc[t][h][r], tmp[t][n][r], acc[t][n][r]);
-    }
-  };
-  // one K step: activations of s+1 and weights of s+2 are requested while s computes
-  auto step = [&](int h, int s) {
-    load_a(s + 1);
-    if constexpr (AFF) compute_aff(h, s);
-    else compute(h, s);
-    load_w(h, s + 2);
-    store_a(h ^ 1, s + 1);
-    __syncthreads();
-  };
-
-  load_w(0, 0);
-  load_a(0);
-  load_w(1, 1);
-  store_a(0, 0);
-  __syncthreads();
-  int s = 0;
-  for (; s + 1 < nks; s += 2) {
-    step(0, s);
-    step(1, s + 1);
-  }
-  if (s < nks) step(0, s);
-
-  if constexpr (AFF) {
-    // the bias part sum_g b_g sum_{k in g} a_k: the biases of the lane's row,
-    // eight groups per slice (M side), against the rows' group sums in hi + lo
-    // (N side); groups past the row's end contribute zero
-    bf16x8_t bw[NTILE][2];
-#pragma unroll
-    for (int t = 0; t < NTILE; ++t) {
-      const __amdgpu_buffer_rsrc_t br =
-          make_rsrc((t / MT ? g.B1 : g.B0) + expert * (g.s_estride / 2), (uint32_t)N * srow_bytes);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int g0 = 8 * kg + 32 * i;
-        const u32x4_t v = g0 < ngroups ? buf_load16(br, soff[t] + 2 * g0, 0) : u32x4_t{0, 0, 0, 0};
-        bw[t][i] = __builtin_bit_cast(bf16x8_t, v);
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NTA; ++n) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        bf16x8_t sh, sl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int grp = 32 * i + 8 * kg + e;
-          const float v = grp < ngroups ? gsum[grp * CT + 16 * n + r16] : 0.f;
-          __bf16 h, l;
-          split_bf16(v, h, l);
-          sh[e] = h;
-          sl[e] = l;
-        }
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-          acc[t][n] = mfma_16x16x32(bw[t][i], sh, acc[t][n]);
-          acc[t][n] = mfma_16x16x32(bw[t][i], sl, acc[t][n]);
-        }
-      }
-    }
-  }
-
-  // ---- epilogue: SiTU-GLU of the gate/up pair (or the plain product), row scale, store
-  const int col_base = wrow_base + 4 * kg;
-#pragma unroll
-  for (int n = 0; n < NTA; ++n) {
-    const int tok = 16 * n + r16;
-    if (tok < nrows) {
-      const long long orow = row0 + tok;
-      float rs = 1.f;
-      if (g.rscale != nullptr) rs = g.rscale[g.rscale_map ? g.rscale_map[orow] : orow];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int col0 = col_base + m * 16;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if constexpr (PAIR) v[r] = situ_glu(acc[m][n][r], acc[m + MT][n][r], g.beta, g.beta_lin) * rs;
-          else v[r] = acc[m][n][r] * rs;
-        }
-        float *cp = g.C + orow * g.ldc + col0;
-        if (col0 + 3 < N) {
-          f32x4_t o = f32x4_t{v[0], v[1], v[2], v[3]};
-          if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
-          *reinterpret_cast<f32x4_t *>(cp) = o;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (col0 + r < N) cp[r] = g.accumulate ? cp[r] + v[r] : v[r];
-        }
-        // one output group at a time: interleaving all of them costs registers
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-}
-
-template <int WF, int AF, bool PAIR, int NT, int MT, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(GemmArgs g) {
-  constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * NPL * 16 * NT * KSTEP];
-  // affine weights: 64-element group sums of the chunk's rows [64 groups][rows]
-  __shared__ float gsum[WF == W_AFF2 ? 64 * 16 * NT : 1];
-  static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
-
-  // ---- work item (XCD-aware over the items that exist on the device): expert
-  // chunks from the chunk list, chunk-major (the weight blocks of one chunk
-  // share its activations)
-  const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
-  const int logical = xcd_logical(total);
-  if (logical < 0) return;
-  const int chunk = logical / g.n_blocks;
-  const int nb = logical - chunk * g.n_blocks;
-  const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
-  const int expert = c.x, row0 = c.y, nrows = c.z;
-  const int nta = min((nrows + 15) >> 4, NT);  // active 16-token tiles
-  if (nta == NT) {
-    pf_item<WF, AF, PAIR, NT, MT, NW>(g, lds, gsum, expert, row0, nrows, nb);
-    return;
-  }
-  switch (nta) {
-    case 1: if constexpr (NT > 1) pf_item<WF, AF, PAIR, 1, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
-    case 2: if constexpr (NT > 2) pf_item<WF, AF, PAIR, 2, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
-    case 3: if constexpr (NT > 3) pf_item<WF, AF, PAIR, 3, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
-    case 4: if constexpr (NT > 4) pf_item<WF, AF, PAIR, 4, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
-    default: if constexpr (NT > 5) pf_item<WF, AF, PAIR, 5, MT, NW>(g, lds, gsum, expert, row0, nrows, nb); break;
-  }
-}
-
 
 // ---------------------------------------------------------------------------
 // MX-scaled variant for MXFP4 weights and activations given as three e4m3
@@ -806,35 +419,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_mx_kernel(GemmArgs g) {
   }
 }
 
-// 16-row weight tiles per wave and matrix: affine weights keep a temporary
-// accumulator per tile beside the result, so their waves hold half the tiles
-constexpr int pf_mt(int wf, bool pair) {
-  return wf == W_AFF2 ? (pair ? PREFILL_MT_PAIR / 2 : PREFILL_MT_SINGLE / 2) : (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE);
-}
-
-template <int WF, int AF, bool PAIR>
-hipError_t launch_pf(const GemmArgs &a, long long grid, hipStream_t st) {
-  constexpr int MT = pf_mt(WF, PAIR);
-  hipLaunchKernelGGL((prefill_kernel<WF, AF, PAIR, PREFILL_NT, MT, PREFILL_NW>), dim3((unsigned)grid),
-                     dim3(64 * PREFILL_NW), 0, st, a);
-  return hipGetLastError();
-}
-
-template <int WF>
-hipError_t launch_wf(int afmt, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
-  switch (afmt) {
-    case A_BF16: return pair ? launch_pf<WF, A_BF16, true>(a, grid, st) : launch_pf<WF, A_BF16, false>(a, grid, st);
-    case A_F32_SPLIT:
-      return pair ? launch_pf<WF, A_F32_SPLIT, true>(a, grid, st) : launch_pf<WF, A_F32_SPLIT, false>(a, grid, st);
-    default:
-      return pair ? launch_pf<WF, A_F32_ROUND, true>(a, grid, st) : launch_pf<WF, A_F32_ROUND, false>(a, grid, st);
-  }
-}
-
 }  // namespace
 
-int prefill_rows_per_wg(bool pair) { return 16 * PREFILL_NW * (pair ? PREFILL_MT_PAIR : PREFILL_MT_SINGLE); }
-int prefill_rows_per_wg_fmt(bool pair, int wfmt) { return 16 * PREFILL_NW * pf_mt(wfmt, pair); }
 int prefill_mx_rows_per_wg(bool pair) { return 16 * PREFILL_MX_NW * (pair ? PREFILL_MX_MT_PAIR : PREFILL_MX_MT_SINGLE); }
 
 hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a, long long grid,
@@ -852,10 +438,8 @@ hipError_t launch_prefill_gemm(int wfmt, int afmt, bool pair, const GemmArgs &a,
     }
     return hipGetLastError();
   }
-  if (a.chunks == nullptr) return hipErrorInvalidValue;  // expert segments only
-  if (wfmt == W_AFF2) return launch_wf<W_AFF2>(afmt, pair, a, grid, st);
-  if (wfmt != W_MXFP4) return hipErrorInvalidValue;
-  return launch_wf<W_MXFP4>(afmt, pair, a, grid, st);
+  // bf16 or fp32 activations run on the plane kernel (launch_prefill_planes)
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

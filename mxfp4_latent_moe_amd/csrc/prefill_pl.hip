@@ -19,6 +19,14 @@
 // ring of 3 steps, or 4 for items of one or two token tiles, whose steps are
 // too short to cover a memory trip.
 //
+// Affine 2-bit weights (w = scale * q + bias per 64-element group; the
+// second bank of kimi-k3-mlx README, Tiers section) run the same loop with
+// the codes entering the MFMA as exact integers q: each instruction stays
+// inside one 64-element group, the two instructions of a group sum into a
+// temporary that is added times the group's scale of each output row, and
+// the bias part sum_g bias_g * sum_{k in g} a_k is one more product per item,
+// against the activation rows' group sums written beside the planes.
+//
 // LDS stage: [plane][token][16 cells of 16 bytes]; cell c of token t holds
 // octet c ^ pl_swz(t) of the token's 128-wide K step.  A wave load of 64 cells
 // covers 4 tokens, 16 lanes reading one token's 256 contiguous bytes.  A
@@ -33,7 +41,6 @@ namespace moe {
 namespace {
 
 constexpr int KSTEP = 128;
-constexpr int PL_NW = 8;  // waves per work-group
 constexpr int pl_stage_bytes(int npl, int nt) { return npl * 16 * nt * 256; }
 // a bijection of 0..15: the even cells for tokens 0..7, the odd ones for 8..15
 MOE_DEV constexpr int pl_swz(int t) { return ((t << 1) & 15) ^ ((t >> 3) & 1); }
@@ -53,10 +60,25 @@ MOE_DEV void lds_wait16(u32x4_t &v) {
 
 constexpr int pl_gcd(int a, int b) { return b == 0 ? a : pl_gcd(b, a % b); }
 
-// RW weight-ring slots, S LDS stages, LDS reads D fragments ahead
-template <bool PAIR, int NPL, int NTA, int MT, int NW, int RW, int S, int D>
+// Eight affine 2-bit codes (a 16-bit run, code i in bits 2i .. 2i+1) as
+// exact bf16 integers in element order: the codes are spread one per nibble
+// (the low two bits of nibble i), where code q reads as the e2m1 value q / 2,
+// and the convert's scale 2 (a power of two: the convert takes only the
+// exponent of its scale) gives q.
+MOE_DEV bf16x8_t aff2x8_ordered(uint32_t x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;  // codes 0-3 in byte 0, 4-7 in byte 2
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;  // two codes per byte
+  x = (x | (x << 2)) & 0x33333333u;  // one code per nibble
+  return fp4x8_to_bf16(x, 2.0f);
+}
+
+// WF: MXFP4 or affine 2-bit weights; RW weight-ring slots, S LDS stages, LDS
+// reads D fragments ahead
+template <int WF, bool PAIR, int NPL, int NTA, int MT, int NW, int RW, int S, int D>
 __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *stage, int expert, int row0,
                                           int nrows, int nb) {
+  constexpr bool AFF = WF == W_AFF2;
+  static_assert(WF == W_MXFP4 || AFF, "MXFP4 or affine 2-bit weights");
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
   constexpr int CT = 16 * NTA;          // staged tokens
@@ -76,10 +98,13 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   const int N = g.N, K = g.K;
   const int nks = K / KSTEP;
 
-  // ---- weights: lane group kg's 16 bytes of a K step are its row's 32 codes
-  // of scale group kg; with the row's four scale bytes of the step, into a
-  // register ring of RW slots, RW - 1 steps ahead
-  const uint32_t row_bytes = K / 2, srow_bytes = K / 32;
+  // ---- weights into a register ring of RW slots, RW - 1 steps ahead.
+  // MXFP4: lane group kg's 16 bytes of a K step are its row's 32 codes of
+  // scale group kg, with the row's four scale bytes of the step.  Affine: the
+  // lane loads dwords kg and 4 + kg of the step's 32 code bytes (16 codes of
+  // each of the step's two groups), with the row's two bf16 scales of the step.
+  // Both formats keep K / 32 scale bytes per row.
+  const uint32_t row_bytes = AFF ? K / 4 : K / 2, srow_bytes = K / 32;
   __amdgpu_buffer_rsrc_t wr[NMAT], sr[NMAT];
 #pragma unroll
   for (int mat = 0; mat < NMAT; ++mat) {
@@ -92,10 +117,11 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
     const int n = min(wrow_base + (t % MT) * 16 + r16, N - 1);
-    woff[t] = (uint32_t)n * row_bytes + kg * 16;
+    woff[t] = (uint32_t)n * row_bytes + kg * (AFF ? 4 : 16);
   }
-  u32x4_t wq[RW][NTILE];
+  typename std::conditional<AFF, u32x2_t, u32x4_t>::type wq[RW][NTILE];
   uint32_t wsc[RW][NTILE];
+  auto scale_row = [&](int t) { return AFF ? (woff[t] - kg * 4) >> 3 : (woff[t] - kg * 16) >> 4; };
 
   // ---- activation planes straight into LDS: wave load k of this wave fills
   // cells [64 (wave + NW k), +64) of a stage.  Gathered rows index A from its
@@ -117,11 +143,13 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   }
   // the memory operations of one step: KQ loads into LDS stage sb (a wave
   // past the stage's last load skips it: KQ_MIN of them are issued by every
-  // wave), then the codes and scales of each weight tile into ring slot wb.
-  // The LDS loads go first: they feed the next step, and loads complete in
-  // the order they are issued.
+  // wave), then the codes and scales of each weight tile into ring slot wb
+  // (WI memory instructions).  The LDS loads go first: they feed the next
+  // step, and loads complete in the order they are issued.
   constexpr int NOPS = KQ + 2 * NTILE;
   constexpr int KQ_MIN = QI / NW;
+  constexpr int WI = (AFF ? 3 : 2) * NTILE;
+  constexpr uint32_t STEP_BYTES = AFF ? 32u : 64u;
   auto issue_op = [&](int o, int sb, int wb, int sa, int sw) {
     if (o < KQ) {
       const int ii = wave + NW * o;  // uniform
@@ -130,11 +158,14 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
                                                  (uint32_t)sa * 256u, 0, 0);
     } else if (o < KQ + NTILE) {
       const int t = o - KQ;
-      wq[wb][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)sw * 64u);
+      if constexpr (AFF)
+        wq[wb][t] = u32x2_t{buf_load4(wr[t / MT], woff[t], (uint32_t)sw * STEP_BYTES),
+                            buf_load4(wr[t / MT], woff[t] + 16u, (uint32_t)sw * STEP_BYTES)};
+      else
+        wq[wb][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)sw * STEP_BYTES);
     } else {
       const int t = o - KQ - NTILE;
-      // the scale row starts at the code row's offset / 16 (K / 32 bytes against K / 2)
-      wsc[wb][t] = buf_load4(sr[t / MT], (woff[t] - kg * 16) >> 4, (uint32_t)sw * 4u);
+      wsc[wb][t] = buf_load4(sr[t / MT], scale_row(t), (uint32_t)sw * 4u);
     }
   };
 
@@ -145,12 +176,15 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
     for (int n = 0; n < NTA; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment reads: in sub-step j (K 32 wide) lane (token r16, group kg) takes
-  // octet 4 kg + j of its token, the K positions of its weight codes 8j .. 8j+7
+  // one octet of its token: MXFP4, octet 4 kg + j, the K positions of its
+  // weight codes 8j .. 8j+7; affine, octet aff2_octet(j / 2, kg, j % 2), so
+  // that sub-steps 2h and 2h + 1 cover 64-element group h of the step
+  auto octet = [&](int j) { return AFF ? aff2_octet(j >> 1, kg, j & 1) : 4 * kg + j; };
   uint32_t la[S][4];
 #pragma unroll
   for (int b = 0; b < S; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage[b]) + (uint32_t)(r16 * 256 + (((4 * kg + j) ^ pl_swz(r16)) << 4));
+    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage[b]) + (uint32_t)(r16 * 256 + ((octet(j) ^ pl_swz(r16)) << 4));
 
   // step s from LDS stage SB and weight slot WB; its fragments f = (sub-step
   // j, plane p, token tile n) are read from LDS D ahead of their MFMAs; the
@@ -168,8 +202,29 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
     constexpr int J = (NOPS + F / 2 - 1) / (F / 2);  // loads issued per fragment
     u32x4_t bq[D + 1];
     bf16x8_t wa[2][NTILE];
+    // MXFP4: the scale of the lane's scale group; affine: the two groups'
+    // scales of the lane's four output rows 4 kg + r (from the lanes that
+    // loaded those rows), with a temporary sum per group
     float scl[NTILE];
-    auto scale_of = [&](int t) { return e8m0_to_float((wsc[WB][t] >> (8 * kg)) & 0xFFu); };
+    uint32_t sc[AFF ? NTILE : 1][4];  // bf16 pairs: group 0 low, group 1 high
+    f32x4_t tmp[AFF ? NTILE : 1][AFF ? NTA : 1];
+    if constexpr (AFF) {
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[t][r] = (uint32_t)__shfl((int)wsc[WB][t], 4 * kg + r, 64);
+#pragma unroll
+        for (int n = 0; n < NTA; ++n) tmp[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) scl[t] = e8m0_to_float((wsc[WB][t] >> (8 * kg)) & 0xFFu);
+    }
+    // sub-step j of tile t: MXFP4 dword j; affine, half j % 2 of dword j / 2
+    auto convert = [&](int j, int t) -> bf16x8_t {
+      if constexpr (AFF) return aff2x8_ordered((wq[WB][t][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      else return fp4x8_to_bf16(wq[WB][t][j], scl[t]);
+    };
     auto issue = [&](auto fc) {
       constexpr int f = decltype(fc)::value;
       constexpr int j = f / FJ, p = (f / NTA) % NPL, n = f % NTA;
@@ -177,10 +232,7 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
     };
     static_for<(D < F ? D : F)>([&](auto fc) { issue(fc); });
 #pragma unroll
-    for (int t = 0; t < NTILE; ++t) {
-      scl[t] = scale_of(t);
-      wa[0][t] = fp4x8_to_bf16(wq[WB][t][0], scl[t]);
-    }
+    for (int t = 0; t < NTILE; ++t) wa[0][t] = convert(0, t);
     static_for<F>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
       constexpr int j = f / FJ, i = f % FJ, n = f % NTA;
@@ -188,14 +240,32 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
       if constexpr (j + 1 < 4) {
         // tiles [i NTILE / FJ, (i + 1) NTILE / FJ) of sub-step j + 1
 #pragma unroll
-        for (int t = (i * NTILE) / FJ; t < ((i + 1) * NTILE) / FJ; ++t)
-          wa[(j + 1) & 1][t] = fp4x8_to_bf16(wq[WB][t][j + 1], scl[t]);
+        for (int t = (i * NTILE) / FJ; t < ((i + 1) * NTILE) / FJ; ++t) wa[(j + 1) & 1][t] = convert(j + 1, t);
       }
       constexpr int behind = (f + D < F) ? D : F - 1 - f;  // reads issued after f
       lds_wait16<behind>(bq[f % (D + 1)]);
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bq[f % (D + 1)]);
+      if constexpr (AFF) {
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bv, acc[t][n]);
+        for (int t = 0; t < NTILE; ++t) tmp[t][n] = mfma_16x16x32(wa[j & 1][t], bv, tmp[t][n]);
+        if constexpr ((f + 1) % (2 * FJ) == 0) {
+          // group h of the step is complete: add it times its scales
+          constexpr int h = f / (2 * FJ);
+#pragma unroll
+          for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+            for (int m = 0; m < NTA; ++m) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[t][m][r] = fmaf(h ? __uint_as_float(sc[t][r] & 0xFFFF0000u) : bf16_lo_to_float(sc[t][r]),
+                                    tmp[t][m][r], acc[t][m][r]);
+              tmp[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bv, acc[t][n]);
+      }
 #pragma unroll
       for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, SN, WN, sa, sw);
     });
@@ -204,8 +274,8 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   // s + 1 in registers.  Every step issues [LDS loads][weight loads]; stage
   // s + 1 went out in step s + 2 - S, weight step s + 1 in step s + 2 - RW, and
   // the loads issued after the later of the two may stay in flight.
-  constexpr int PER_STEP = KQ_MIN + 2 * NTILE;
-  constexpr int AFTER_A = 2 * NTILE + (S - 2) * PER_STEP, AFTER_W = (RW - 2) * PER_STEP;
+  constexpr int PER_STEP = KQ_MIN + WI;
+  constexpr int AFTER_A = WI + (S - 2) * PER_STEP, AFTER_W = (RW - 2) * PER_STEP;
   constexpr int VM_LEFT = AFTER_A < AFTER_W ? AFTER_A : AFTER_W;
   static_assert(VM_LEFT < 64, "vmcnt range");
   auto wait_and_sync = [&]() {
@@ -237,6 +307,55 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   });
   // drain the loads past the last step before the LDS is reused
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  if constexpr (AFF) {
+    // the bias part sum_g b_g sum_{k in g} a_k: the biases of the lane's row,
+    // eight groups per 32-group slice (M side), against the token rows' group
+    // sums in hi + lo (N side); groups past the row's end contribute zero
+    const int ngroups = K / 64;
+    bf16x8_t bw[NTILE][2];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const __amdgpu_buffer_rsrc_t br =
+          make_rsrc((t / MT ? g.B1 : g.B0) + expert * (g.s_estride / 2), (uint32_t)N * srow_bytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g0 = 8 * kg + 32 * i;
+        const u32x4_t v = g0 < ngroups ? buf_load16(br, scale_row(t) + 2 * g0, 0) : u32x4_t{0, 0, 0, 0};
+        bw[t][i] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) {
+      const int tok = 16 * n + r16;
+      const int tt = tok < nrows ? tok : 0;
+      const long long arow = (g.a_map && !g.asum_sorted) ? (long long)(g.a_map[row0 + tt] / g.a_div)
+                                                          : (long long)(row0 + tt);
+      const float *srow = g.asum + arow * ngroups;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g0 = 8 * kg + 32 * i;
+        f32x4_t v0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (g0 < ngroups) {
+          v0 = reinterpret_cast<const f32x4_t *>(srow + g0)[0];
+          v1 = reinterpret_cast<const f32x4_t *>(srow + g0)[1];
+        }
+        bf16x8_t sh, sl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 h, l;
+          split_bf16(e < 4 ? v0[e] : v1[e - 4], h, l);
+          sh[e] = h;
+          sl[e] = l;
+        }
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+          acc[t][n] = mfma_16x16x32(bw[t][i], sh, acc[t][n]);
+          acc[t][n] = mfma_16x16x32(bw[t][i], sl, acc[t][n]);
+        }
+      }
+    }
+  }
 
   // ---- epilogue: SiTU-GLU of the gate/up pair (or the plain product), row scale, store
   const int col_base = wrow_base + 4 * kg;
@@ -273,20 +392,22 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
 }
 
 // weight-ring slots: items with few token tiles stream their weights with
-// little compute per step, so they keep more steps in flight
-constexpr int pl_ring(int nta) { return nta <= 2 ? 4 : 3; }
+// little compute per step, so they keep more steps in flight.  Affine weights
+// (more registers per tile) keep two slots and two LDS stages.
+constexpr int pl_ring(int wf, int nta) { return nta <= 2 ? 4 : wf == W_AFF2 ? 2 : 3; }
 // LDS stages
-constexpr int pl_stages(int nta) { return nta >= 3 ? 3 : 2; }
-constexpr int PL_D = 2;  // fragment reads ahead of their MFMAs
-constexpr bool pl_any_three(int nt) { return nt > 0 && (pl_stages(nt) == 3 || pl_any_three(nt - 1)); }
+constexpr int pl_stages(int wf, int nta) { return nta >= 3 && wf != W_AFF2 ? 3 : 2; }
+// fragment reads ahead of their MFMAs (affine weights: one, for registers)
+constexpr int pl_d(int wf) { return wf == W_AFF2 ? 1 : 2; }
+constexpr bool pl_any_three(int wf, int nt) { return nt > 0 && (pl_stages(wf, nt) == 3 || pl_any_three(wf, nt - 1)); }
 
-template <bool PAIR, int NPL, int NT, int MT, int NW>
+template <int WF, bool PAIR, int NPL, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
   // activation stages (separate objects, so waits on one stage's loads do
   // not cover the others)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[pl_stage_bytes(NPL, NT)];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[pl_stage_bytes(NPL, NT)];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[pl_any_three(NT) ? pl_stage_bytes(NPL, NT) : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[pl_any_three(WF, NT) ? pl_stage_bytes(NPL, NT) : 16];
   uint8_t *const stage[3] = {st0, st1, st2};
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
   const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
@@ -297,7 +418,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
 #define MOE_PL_ITEM(A) \
-  pfpl_item<PAIR, NPL, A, MT, NW, pl_ring(A), pl_stages(A), PL_D>(g, stage, c.x, c.y, c.z, nb)
+  pfpl_item<WF, PAIR, NPL, A, MT, NW, pl_ring(WF, A), pl_stages(WF, A), pl_d(WF)>(g, stage, c.x, c.y, c.z, nb)
   if (nta == NT) {
     MOE_PL_ITEM(NT);
     return;
@@ -314,64 +435,117 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
 
 // fp32 rows -> [rows][NPL][K] bf16 rows: hi = bf16(a) and lo = bf16(a - hi)
 // (NPL 2), or the rounded row alone (NPL 1); output row r is activation row
-// map[r] / div (map NULL: row r); 8 values per thread
-template <int NPL>
-__global__ __launch_bounds__(256) void split_rows_kernel(const float *__restrict__ A, long long lda, long long rows,
+// map[r] / div (map NULL: row r); 8 values per thread.  With sums given, also
+// each row's 64-element group sums [rows][K / 64] (fp32, the eight threads of
+// a group in one wavefront; bf16 input: the sums alone).
+template <typename TIn, int NPL, bool SUMS>
+__global__ __launch_bounds__(256) void split_rows_kernel(const TIn *__restrict__ A, long long lda, long long rows,
                                                          int K, const int32_t *__restrict__ map, int div,
-                                                         __bf16 *__restrict__ out) {
+                                                         __bf16 *__restrict__ out, float *__restrict__ sums) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const int per_row = K / 8;
-  if (i >= rows * per_row) return;
+  if (i >= rows * per_row) return;  // whole groups of eight threads (K / 8 is a multiple of 8 with sums)
   const long long row = i / per_row;
   const int c = (int)(i - row * per_row);
   const long long src = map ? (long long)(map[row] / div) : row;
-  const f32x4_t *p = reinterpret_cast<const f32x4_t *>(A + src * lda + c * 8);
-  const f32x4_t x0 = p[0], x1 = p[1];
-  bf16x8_t h, l;
+  float v[8];
+  if constexpr (std::is_same<TIn, float>::value) {
+    const f32x4_t *p = reinterpret_cast<const f32x4_t *>(A + src * lda + c * 8);
+    const f32x4_t x0 = p[0], x1 = p[1];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float v = e < 4 ? x0[e] : x1[e - 4];
-    __bf16 vh, vl;
-    split_bf16(v, vh, vl);
-    h[e] = vh;
-    l[e] = vl;
+    for (int e = 0; e < 8; ++e) v[e] = e < 4 ? x0[e] : x1[e - 4];
+  } else {
+    const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(A + src * lda + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = from_bf16(x[e]);
   }
-  __bf16 *o = out + row * NPL * K + c * 8;
-  *reinterpret_cast<bf16x8_t *>(o) = h;
-  if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(o + K) = l;
+  if (out != nullptr) {
+    bf16x8_t h, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 vh, vl;
+      split_bf16(v[e], vh, vl);
+      h[e] = NPL == 2 ? vh : to_bf16(v[e]);
+      l[e] = vl;
+    }
+    __bf16 *o = out + row * NPL * K + c * 8;
+    *reinterpret_cast<bf16x8_t *>(o) = h;
+    if constexpr (NPL == 2) *reinterpret_cast<bf16x8_t *>(o + K) = l;
+  }
+  if constexpr (SUMS) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part += v[e];
+    part += __shfl_xor(part, 1, 64);
+    part += __shfl_xor(part, 2, 64);
+    part += __shfl_xor(part, 4, 64);
+    if ((c & 7) == 0) sums[row * (K / 64) + (c >> 3)] = part;
+  }
 }
 
-}  // namespace
+// Waves per work-group and 16-row weight tiles per wave and matrix: eight
+// waves (two per SIMD); MXFP4, 4 tiles per wave (2 + 2 for a SiTU pair);
+// affine weights keep a temporary sum per tile beside the result, so their
+// waves hold 2 tiles.
+constexpr int pl_nw(int wf) { return 8; }
+constexpr int pl_mt(int wf, bool pair) { return (wf == W_AFF2 ? 1 : 2) * (pair ? 1 : 2); }
 
-// 16-row weight tiles per wave and matrix: 8 tiles per wave in all
-constexpr int PL_MT_PAIR = 4 * PREFILL_MX_NW / PL_NW;
-constexpr int PL_MT_SINGLE = 8 * PREFILL_MX_NW / PL_NW;
-
-int prefill_pl_rows_per_wg(bool pair) { return 16 * PL_NW * (pair ? PL_MT_PAIR : PL_MT_SINGLE); }
-
-hipError_t launch_prefill_planes(int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
-  if (a.chunks == nullptr || (npl != 1 && npl != 2) || a.K % KSTEP != 0) return hipErrorInvalidValue;
-  const dim3 gr((unsigned)grid), blk(64 * PL_NW);
+template <int WF>
+hipError_t launch_pl(int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
+  constexpr int NW = pl_nw(WF);
+  const dim3 gr((unsigned)grid), blk(64 * NW);
   if (npl == 2) {
-    if (pair) hipLaunchKernelGGL((prefill_pl_kernel<true, 2, PREFILL_NT, PL_MT_PAIR, PL_NW>), gr, blk, 0, st, a);
-    else hipLaunchKernelGGL((prefill_pl_kernel<false, 2, PREFILL_NT, PL_MT_SINGLE, PL_NW>), gr, blk, 0, st, a);
+    if (pair) hipLaunchKernelGGL((prefill_pl_kernel<WF, true, 2, PREFILL_NT, pl_mt(WF, true), NW>), gr, blk, 0, st, a);
+    else hipLaunchKernelGGL((prefill_pl_kernel<WF, false, 2, PREFILL_NT, pl_mt(WF, false), NW>), gr, blk, 0, st, a);
   } else {
-    if (pair) hipLaunchKernelGGL((prefill_pl_kernel<true, 1, PREFILL_NT, PL_MT_PAIR, PL_NW>), gr, blk, 0, st, a);
-    else hipLaunchKernelGGL((prefill_pl_kernel<false, 1, PREFILL_NT, PL_MT_SINGLE, PL_NW>), gr, blk, 0, st, a);
+    if (pair) hipLaunchKernelGGL((prefill_pl_kernel<WF, true, 1, PREFILL_NT, pl_mt(WF, true), NW>), gr, blk, 0, st, a);
+    else hipLaunchKernelGGL((prefill_pl_kernel<WF, false, 1, PREFILL_NT, pl_mt(WF, false), NW>), gr, blk, 0, st, a);
   }
   return hipGetLastError();
 }
 
+}  // namespace
+
+int prefill_pl_rows_per_wg(bool pair, int wfmt) {
+  return 16 * (wfmt == W_AFF2 ? pl_nw(W_AFF2) : pl_nw(W_MXFP4)) * pl_mt(wfmt, pair);
+}
+
+hipError_t launch_prefill_planes(int wfmt, int npl, bool pair, const GemmArgs &a, long long grid, hipStream_t st) {
+  if (a.chunks == nullptr || (npl != 1 && npl != 2) || a.K % KSTEP != 0) return hipErrorInvalidValue;
+  if (wfmt == W_AFF2) {
+    // whole 512-element runs of groups, at most 64 groups (two 32-group bias slices)
+    if (a.asum == nullptr || a.B0 == nullptr || a.K % 512 != 0 || a.K > 4096) return hipErrorInvalidValue;
+    return launch_pl<W_AFF2>(npl, pair, a, grid, st);
+  }
+  if (wfmt != W_MXFP4) return hipErrorInvalidValue;
+  return launch_pl<W_MXFP4>(npl, pair, a, grid, st);
+}
+
 size_t split_rows_bytes(long long rows, int K, int npl) { return (size_t)rows * npl * K * 2; }
+size_t row_sums_bytes(long long rows, int K) { return (size_t)rows * (K / 64) * 4; }
 
 hipError_t launch_split_rows(int npl, const float *A, long long lda, long long rows, int K, const int32_t *map,
-                             int div, uint16_t *out, hipStream_t st) {
-  if ((npl != 1 && npl != 2) || K % 8 != 0) return hipErrorInvalidValue;
+                             int div, uint16_t *out, float *sums, hipStream_t st) {
+  if ((npl != 1 && npl != 2) || K % 8 != 0 || (sums && K % 512 != 0)) return hipErrorInvalidValue;
   const long long n = rows * (K / 8);
   const dim3 gr((unsigned)((n + 255) / 256)), blk(256);
   __bf16 *o = reinterpret_cast<__bf16 *>(out);
-  if (npl == 2) hipLaunchKernelGGL(split_rows_kernel<2>, gr, blk, 0, st, A, lda, rows, K, map, div, o);
-  else hipLaunchKernelGGL(split_rows_kernel<1>, gr, blk, 0, st, A, lda, rows, K, map, div, o);
+  if (sums) {
+    if (npl == 2) hipLaunchKernelGGL((split_rows_kernel<float, 2, true>), gr, blk, 0, st, A, lda, rows, K, map, div, o, sums);
+    else hipLaunchKernelGGL((split_rows_kernel<float, 1, true>), gr, blk, 0, st, A, lda, rows, K, map, div, o, sums);
+  } else {
+    if (npl == 2) hipLaunchKernelGGL((split_rows_kernel<float, 2, false>), gr, blk, 0, st, A, lda, rows, K, map, div, o, sums);
+    else hipLaunchKernelGGL((split_rows_kernel<float, 1, false>), gr, blk, 0, st, A, lda, rows, K, map, div, o, sums);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const uint16_t *A, long long lda, long long rows, int K, const int32_t *map, int div,
+                           float *sums, hipStream_t st) {
+  if (K % 512 != 0) return hipErrorInvalidValue;
+  const long long n = rows * (K / 8);
+  hipLaunchKernelGGL((split_rows_kernel<__bf16, 1, true>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const __bf16 *>(A), lda, rows, K, map, div, nullptr, sums);
   return hipGetLastError();
 }
 
