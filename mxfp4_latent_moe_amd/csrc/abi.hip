@@ -80,9 +80,18 @@ bool use_mx8(const moe_shape *s, const GemmPlan &pl, long long rows, int K) {
 }
 
 struct GroupedWs {
-  size_t chunks, count, partial, mx, total;
+  size_t chunks, count, chunks2, count2, partial, mx, total;
   GemmPlan plan;
 };
+
+// Batches of a few rows per expert (P < 8 E) on the tiled path: the experts
+// with at most PERSIST_ROWS_WIDE rows run on the persistent streaming kernel
+// (one chunk each, its weights streamed once at the decode kernel's rate),
+// the larger ones on the tiled kernel.
+bool hybrid_grouped(const moe_shape *s, const GemmPlan &pl, int P, int K) {
+  return pl.variant == 3 && s->operand_mode != MOE_OPND_MX8X3 && s->operand_mode != MOE_OPND_MX6X3 &&
+         grouped_stream_fits(K) && (long long)P < 8LL * s->n_experts;
+}
 GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
   GroupedWs w{};
   const int K = gateup ? s->latent : s->inter;
@@ -90,7 +99,10 @@ GroupedWs grouped_ws(const moe_shape *s, int P, bool gateup) {
                   : plan_grouped(P, s->n_experts, s->latent, s->inter, false);
   w.chunks = 0;
   w.count = align_up((size_t)w.plan.max_chunks * 16);
-  w.partial = w.count + ALIGN;
+  // the streaming kernel's chunk list of a split batch: at most one chunk per expert
+  w.chunks2 = w.count + ALIGN;
+  w.count2 = w.chunks2 + (w.plan.variant == 3 ? align_up((size_t)s->n_experts * 16) : 0);
+  w.partial = w.count2 + ALIGN;
   w.mx = w.partial + align_up(w.plan.partial_bytes);
   // the MX term planes or the bf16 activation planes hold at most P rows
   // (gathered activations with more rows than P are split per sorted row)
@@ -464,11 +476,13 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t *chunks = reinterpret_cast<int32_t *>(wsp(ws, w.chunks));
     int32_t *count = reinterpret_cast<int32_t *>(wsp(ws, w.count));
-    if (launch_plan_chunks(expert_offsets, s->n_experts, w.plan.chunk_rows, chunks, count, st) !=
-        hipSuccess)
-      return MOE_EHIP;
     const int N = gateup ? s->inter : s->latent;
     const int K = gateup ? s->latent : s->inter;
+    const bool hybrid = hybrid_grouped(s, w.plan, P, K);
+    // the tiled kernel's chunks: every expert, or in a split batch the experts above the streaming kernel's rows
+    if (launch_plan_chunks(expert_offsets, s->n_experts, w.plan.chunk_rows, chunks, count, st,
+                           hybrid ? PERSIST_ROWS_WIDE + 1 : 1) != hipSuccess)
+      return MOE_EHIP;
     GemmArgs a{};
     a.A = A;
     a.lda = K;
@@ -517,6 +531,21 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
       a.mx_rows = rows;
       if (split_gathers) a.a_map = nullptr;
       afmt = fp6 ? A_MX6X3 : A_MX8X3;
+    }
+    if (hybrid) {
+      // the small experts on the streaming kernel, which stages their rows itself
+      int32_t *chunks2 = reinterpret_cast<int32_t *>(wsp(ws, w.chunks2));
+      int32_t *count2 = reinterpret_cast<int32_t *>(wsp(ws, w.count2));
+      if (launch_plan_chunks(expert_offsets, s->n_experts, PERSIST_ROWS_WIDE, chunks2, count2, st, 1,
+                             PERSIST_ROWS_WIDE) != hipSuccess)
+        return MOE_EHIP;
+      GemmArgs as = a;
+      as.chunks = chunks2;
+      as.chunk_count = count2;
+      as.n_blocks = (N + grouped_stream_rows_per_wg(gateup) - 1) / grouped_stream_rows_per_wg(gateup);
+      as.splits = 1;
+      as.grid_logical = s->n_experts * as.n_blocks;
+      if (launch_grouped_stream(W_MXFP4, afmt, gateup, as, st, PERSIST_ROWS_WIDE) != hipSuccess) return MOE_EHIP;
     }
     if (w.plan.variant == 3 && afmt != A_MX8X3 && afmt != A_MX6X3) {
       // bf16 activation planes: bf16 activations are one plane already; fp32

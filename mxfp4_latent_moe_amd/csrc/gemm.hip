@@ -302,17 +302,18 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs f) {
 }
 
 // One workgroup: chunk list {expert, row0, nrows, 0} in expert order from the
-// expert offsets, chunks of at most `chunk_rows` rows.
+// expert offsets, chunks of at most `chunk_rows` rows, for the experts whose
+// row count lies in [min_rows, max_rows].
 __global__ __launch_bounds__(1024) void plan_chunks_kernel(const int32_t *offsets, int E,
                                                            int chunk_rows, int32_t *chunks,
-                                                           int32_t *count) {
+                                                           int32_t *count, int min_rows, int max_rows) {
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = tid;
   int ne = 0, nch = 0;
   if (e < E) {
     ne = offsets[e + 1] - offsets[e];
-    nch = (ne + chunk_rows - 1) / chunk_rows;
+    nch = (ne < min_rows || ne > max_rows) ? 0 : (ne + chunk_rows - 1) / chunk_rows;
   }
   // inclusive wave scan
   int x = nch;
@@ -499,9 +500,9 @@ hipError_t launch_finalize(const FinalizeArgs &f, hipStream_t st) {
 }
 
 hipError_t launch_plan_chunks(const int32_t *offsets, int E, int chunk_rows, int32_t *chunks,
-                              int32_t *count, hipStream_t st) {
+                              int32_t *count, hipStream_t st, int min_rows, int max_rows) {
   hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(1024), 0, st, offsets, E, chunk_rows, chunks,
-                     count);
+                     count, min_rows, max_rows);
   return hipGetLastError();
 }
 

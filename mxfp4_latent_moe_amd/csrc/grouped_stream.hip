@@ -1,7 +1,8 @@
 // Persistent streaming MXFP4 grouped GEMM for decode-sized expert segments.
 //
-// Work item = (row chunk of <= R = 4 sorted rows of one expert, block of
-// weight rows).  The grid holds one resident wave of work-groups; work-group
+// Work item = (row chunk of <= R sorted rows of one expert, block of weight
+// rows); R = 4 at decode sizes, 8 for the small experts of a batch whose
+// larger experts run on the tiled kernel.  The grid holds one resident wave of work-groups; work-group
 // w takes the contiguous item range [w*n/G, (w+1)*n/G) of the n items that
 // exist on the device (n is read from the chunk list, so nothing waits on the
 // host).  Within a work-group the weight stream never stops: every wave walks
@@ -26,10 +27,9 @@ namespace moe {
 namespace {
 
 constexpr int KSTEP = 128;
-constexpr int R = PERSIST_ROWS;
 constexpr int KSMAX = STREAM_GROUPED_KSMAX;
 
-template <int AF, bool PAIR, int MT, int AHEAD, int NW>
+template <int AF, bool PAIR, int MT, int AHEAD, int NW, int R>
 __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   constexpr int D = 4;  // K steps per group: one 16-byte read of scales covers four steps
   constexpr int NMAT = PAIR ? 2 : 1;
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
 // caller).
 template <int AF, bool PAIR, int MT, int AHEAD, int NW>
 __global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g) {
+  constexpr int R = PERSIST_ROWS;
   constexpr int D = 4;  // K steps per group: one 16-byte read of scales covers four steps
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int NTILE = NMAT * MT;
@@ -627,16 +628,25 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g)
 // matrices per wave) runs eight waves per work-group, down four.
 constexpr int gs_waves(bool pair) { return pair ? 8 : 4; }
 
-template <int AF, bool PAIR>
+template <int AF, bool PAIR, int R>
 void *kernel_ptr() {
-  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, 1, 2, gs_waves(PAIR)>);
+  return reinterpret_cast<void *>(&grouped_stream_kernel<AF, PAIR, 1, 2, gs_waves(PAIR), R>);
 }
 template <int AF, bool PAIR>
 void *aff_kernel_ptr() {
   return reinterpret_cast<void *>(&grouped_stream_aff_kernel<AF, PAIR, 1, 2, gs_waves(PAIR)>);
 }
 
-void *select_kernel(int wfmt, int afmt, bool pair) {
+template <int R>
+void *select_mxfp4(int afmt, bool pair) {
+  switch (afmt) {
+    case A_BF16: return pair ? kernel_ptr<A_BF16, true, R>() : kernel_ptr<A_BF16, false, R>();
+    case A_F32_SPLIT: return pair ? kernel_ptr<A_F32_SPLIT, true, R>() : kernel_ptr<A_F32_SPLIT, false, R>();
+    default: return pair ? kernel_ptr<A_F32_ROUND, true, R>() : kernel_ptr<A_F32_ROUND, false, R>();
+  }
+}
+
+void *select_kernel(int wfmt, int afmt, bool pair, int rows) {
   if (wfmt == W_AFF2) {
     switch (afmt) {
       case A_BF16: return pair ? aff_kernel_ptr<A_BF16, true>() : aff_kernel_ptr<A_BF16, false>();
@@ -644,11 +654,7 @@ void *select_kernel(int wfmt, int afmt, bool pair) {
       default: return pair ? aff_kernel_ptr<A_F32_ROUND, true>() : aff_kernel_ptr<A_F32_ROUND, false>();
     }
   }
-  switch (afmt) {
-    case A_BF16: return pair ? kernel_ptr<A_BF16, true>() : kernel_ptr<A_BF16, false>();
-    case A_F32_SPLIT: return pair ? kernel_ptr<A_F32_SPLIT, true>() : kernel_ptr<A_F32_SPLIT, false>();
-    default: return pair ? kernel_ptr<A_F32_ROUND, true>() : kernel_ptr<A_F32_ROUND, false>();
-  }
+  return rows == PERSIST_ROWS ? select_mxfp4<PERSIST_ROWS>(afmt, pair) : select_mxfp4<PERSIST_ROWS_WIDE>(afmt, pair);
 }
 
 }  // namespace
@@ -660,14 +666,15 @@ bool grouped_stream_fits(int K) {
   return nks % 4 == 0 && nks <= KSMAX;
 }
 
-hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st) {
+hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st, int rows) {
   if (wfmt != W_MXFP4 && wfmt != W_AFF2) return hipErrorInvalidValue;
-  void *fn = select_kernel(wfmt, afmt, pair);
+  if (rows != PERSIST_ROWS && (rows != PERSIST_ROWS_WIDE || wfmt != W_MXFP4)) return hipErrorInvalidValue;
+  void *fn = select_kernel(wfmt, afmt, pair, rows);
   // one resident wave of work-groups (occupancy queried once per kernel and device)
-  static std::atomic<int> cache[64][12];
+  static std::atomic<int> cache[64][18];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const int slot = (wfmt == W_AFF2 ? 6 : 0) + afmt * 2 + (pair ? 1 : 0);
+  const int slot = (wfmt == W_AFF2 ? 6 : rows == PERSIST_ROWS_WIDE ? 12 : 0) + afmt * 2 + (pair ? 1 : 0);
   int per_cu = cache[dev][slot].load();
   if (per_cu == 0) {
     int blocks = 0;

@@ -74,6 +74,9 @@ constexpr int STREAM_GROUPED_ROWS = 2;
 constexpr int STREAM_GROUPED_KSMAX = 32;
 // persistent grouped kernel: rows per chunk (decode segments rarely exceed 4)
 constexpr int PERSIST_ROWS = 4;
+// the same kernel over chunks of up to 8 rows: the small experts of a batch
+// whose other experts run on the tiled kernel
+constexpr int PERSIST_ROWS_WIDE = 8;
 // tiled prefill kernel: 16-token tiles per chunk, 16-row weight tiles per wave
 // and matrix, waves per work-group
 constexpr int PREFILL_NT = 6;
@@ -102,7 +105,9 @@ GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
 int stream_rows_per_wg(int wfmt, bool pair);
 int grouped_stream_rows_per_wg(bool pair);
 bool grouped_stream_fits(int K);
-hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st);
+// rows: chunk rows the kernel stages (PERSIST_ROWS, or PERSIST_ROWS_WIDE for MXFP4)
+hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st,
+                                 int rows = PERSIST_ROWS);
 int prefill_mx_rows_per_wg(bool pair);
 // tiled prefill kernel over bf16 activation planes ([rows][npl][K]: hi then lo,
 // or the rounded row), MXFP4 or affine 2-bit weights (affine: a.asum holds the
@@ -136,8 +141,9 @@ hipError_t launch_split_planes(const float *A, long long lda, int rows, int K, u
 hipError_t launch_gemm(const GemmPlan &pl, int wfmt, int afmt, bool pair, const GemmArgs &a,
                        hipStream_t st);
 hipError_t launch_finalize(const FinalizeArgs &f, hipStream_t st);
+// experts with fewer than min_rows or more than max_rows rows get no chunks
 hipError_t launch_plan_chunks(const int32_t *offsets, int E, int chunk_rows, int32_t *chunks,
-                              int32_t *count, hipStream_t st);
+                              int32_t *count, hipStream_t st, int min_rows = 1, int max_rows = 1 << 30);
 
 // partial != nullptr: logits are the sum of `splits` split-K partials [splits][T][E]
 // (logits unused); promoted == nullptr: no cap

@@ -75,8 +75,8 @@ MOE_DEV bf16x8_t aff2x8_ordered(uint32_t x) {
 // WF: MXFP4 or affine 2-bit weights; RW weight-ring slots, S LDS stages, LDS
 // reads D fragments ahead
 template <int WF, bool PAIR, int NPL, int NTA, int MT, int NW, int RW, int S, int D>
-__device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *stage, int expert, int row0,
-                                          int nrows, int nb) {
+__device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int expert, int row0, int nrows,
+                                          int nb) {
   constexpr bool AFF = WF == W_AFF2;
   static_assert(WF == W_MXFP4 || AFF, "MXFP4 or affine 2-bit weights");
   constexpr int NMAT = PAIR ? 2 : 1;
@@ -87,7 +87,9 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   constexpr int QI = 4 * NPL * NTA;     // 1 KB wave loads per stage
   constexpr int KQ = (QI + NW - 1) / NW;  // per wave (the last round may leave waves idle)
   static_assert(pl_stage_bytes(NPL, NTA) == QI * 1024, "whole wave loads");
-  static_assert(RW >= 2 && RW <= 8 && (S == 2 || S == 3), "ring shapes");
+  static_assert(RW >= 2 && RW <= 8 && S >= 2 && S <= 4, "ring shapes");
+  // stage b of the LDS ring
+  auto stage = [&](int b) { return lds + b * pl_stage_bytes(NPL, NTA); };
   constexpr int U = RW * S / pl_gcd(RW, S);  // steps per unrolled round: slot and stage repeat
 
   const int tid = threadIdx.x;
@@ -154,7 +156,7 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
     if (o < KQ) {
       const int ii = wave + NW * o;  // uniform
       if (ii < QI)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(stage[sb] + ii * 1024), 16, qoff[o],
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(stage(sb) + ii * 1024), 16, qoff[o],
                                                  (uint32_t)sa * 256u, 0, 0);
     } else if (o < KQ + NTILE) {
       const int t = o - KQ;
@@ -184,7 +186,7 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
 #pragma unroll
   for (int b = 0; b < S; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage[b]) + (uint32_t)(r16 * 256 + ((octet(j) ^ pl_swz(r16)) << 4));
+    for (int j = 0; j < 4; ++j) la[b][j] = lds_addr(stage(b)) + (uint32_t)(r16 * 256 + ((octet(j) ^ pl_swz(r16)) << 4));
 
   // step s from LDS stage SB and weight slot WB; its fragments f = (sub-step
   // j, plane p, token tile n) are read from LDS D ahead of their MFMAs; the
@@ -391,24 +393,28 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *const *sta
   }
 }
 
-// weight-ring slots: items with few token tiles stream their weights with
-// little compute per step, so they keep more steps in flight.  Affine weights
-// (more registers per tile) keep two slots and two LDS stages.
+// Weight-ring slots and LDS stages.  Items with one or two token tiles have
+// steps too short to cover a memory trip: their weights go three steps ahead
+// and their activation stages (small, so four fit) three steps ahead too.
+// Larger items: three and three; affine weights (more registers per tile),
+// two and two.
 constexpr int pl_ring(int wf, int nta) { return nta <= 2 ? 4 : wf == W_AFF2 ? 2 : 3; }
-// LDS stages
-constexpr int pl_stages(int wf, int nta) { return nta >= 3 && wf != W_AFF2 ? 3 : 2; }
+constexpr int pl_stages(int wf, int nta) { return nta <= 2 ? 4 : wf == W_AFF2 ? 2 : 3; }
 // fragment reads ahead of their MFMAs (affine weights: one, for registers)
 constexpr int pl_d(int wf) { return wf == W_AFF2 ? 1 : 2; }
-constexpr bool pl_any_three(int wf, int nt) { return nt > 0 && (pl_stages(wf, nt) == 3 || pl_any_three(wf, nt - 1)); }
+// LDS of the largest ring over the item shapes 1 .. nt
+constexpr int pl_lds_bytes(int wf, int npl, int nt) {
+  return nt == 0 ? 0
+                 : (pl_stages(wf, nt) * pl_stage_bytes(npl, nt) > pl_lds_bytes(wf, npl, nt - 1)
+                        ? pl_stages(wf, nt) * pl_stage_bytes(npl, nt)
+                        : pl_lds_bytes(wf, npl, nt - 1));
+}
 
 template <int WF, bool PAIR, int NPL, int NT, int MT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
-  // activation stages (separate objects, so waits on one stage's loads do
-  // not cover the others)
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[pl_stage_bytes(NPL, NT)];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[pl_stage_bytes(NPL, NT)];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[pl_any_three(WF, NT) ? pl_stage_bytes(NPL, NT) : 16];
-  uint8_t *const stage[3] = {st0, st1, st2};
+  // the activation ring: stages of the item's shape, back to back (the LDS
+  // reads wait on their own loads explicitly, so one object serves all stages)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[pl_lds_bytes(WF, NPL, NT)];
   static_assert(NT >= 1 && NT <= 6, "the item dispatch covers 1..6 active token tiles");
   const int total = min(*g.chunk_count * g.n_blocks, g.grid_logical);
   const int logical = xcd_logical(total);
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
 #define MOE_PL_ITEM(A) \
-  pfpl_item<WF, PAIR, NPL, A, MT, NW, pl_ring(WF, A), pl_stages(WF, A), pl_d(WF)>(g, stage, c.x, c.y, c.z, nb)
+  pfpl_item<WF, PAIR, NPL, A, MT, NW, pl_ring(WF, A), pl_stages(WF, A), pl_d(WF)>(g, lds, c.x, c.y, c.z, nb)
   if (nta == NT) {
     MOE_PL_ITEM(NT);
     return;
