@@ -215,10 +215,11 @@ GemmArgs dense_args(const GemmPlan &pl, const void *A, long long lda, const void
 
 // dense GEMM plus, for split K, the finalize pass.  The tiled kernel takes
 // fp32 activations as bf16 planes, written first into `planes`.
+// planes_ready: a0.A (and a0.A2) already hold the activations as bf16 planes
 hipError_t run_dense(const GemmPlan &pl, int afmt, bool pair, const GemmArgs &a0, void *planes,
-                     hipStream_t st) {
+                     hipStream_t st, bool planes_ready = false) {
   GemmArgs a = a0;
-  if (pl.variant == 4 && afmt != A_BF16) {
+  if (pl.variant == 4 && afmt != A_BF16 && !planes_ready) {
     uint16_t *hi = static_cast<uint16_t *>(planes);
     uint16_t *lo = afmt == A_F32_SPLIT ? hi + (size_t)a.dense_rows * a.K : nullptr;
     hipError_t e = launch_split_planes(static_cast<const float *>(a.A), a.lda, a.dense_rows, a.K, hi, lo, st);
@@ -320,6 +321,27 @@ static int route_impl(const moe_shape *s, int T, const uint16_t *x, const uint16
   return MOE_OK;
 }
 
+// combine + RMSNorm writing y_n straight into the bf16 planes the tiled
+// up_proj reads (no fp32 y_n, no split pass), then up_proj
+static bool combine_planes_ok(const moe_shape *s, const CombineWs &w) {
+  return w.pu.variant == 4 && s->latent <= 4096 && s->latent % 4 == 0;
+}
+static int combine_planes_up(const moe_shape *s, int T, const float *Y, const int32_t *pair_pos, const float *topk_w,
+                             const uint16_t *gamma, const uint16_t *w_up, float *out, int accumulate,
+                             const CombineWs &w, void *ws, hipStream_t st) {
+  const int afmt = afmt_of(s);
+  uint16_t *hi = reinterpret_cast<uint16_t *>(wsp(ws, w.planes));
+  uint16_t *lo = afmt == A_F32_SPLIT ? hi + (size_t)T * s->latent : nullptr;
+  if (launch_combine_norm_planes(Y, pair_pos, topk_w, gamma, T, s->top_k, s->latent, s->rms_eps, hi, lo, st) !=
+      hipSuccess)
+    return MOE_EHIP;
+  GemmArgs a = dense_args(w.pu, hi, s->latent, w_up, nullptr, s->hidden, s->latent, out, s->hidden, accumulate, T,
+                          reinterpret_cast<float *>(wsp(ws, w.partial)), s);
+  a.A2 = lo;
+  if (run_dense(w.pu, afmt, false, a, nullptr, st, true) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
 // The combine call, with the REAP saliency pass fused in when sal_sum is given
 // (its per-row contributions go to the workspace after the combine's own).
 static int combine_norm_up_impl(const moe_shape *s, int T, const float *Y, const int32_t *pair_pos,
@@ -338,6 +360,8 @@ static int combine_norm_up_impl(const moe_shape *s, int T, const float *Y, const
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if ((rc = check_device())) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!reap && combine_planes_ok(s, w))
+    return combine_planes_up(s, T, Y, pair_pos, topk_w, gamma, w_up, out, accumulate, w, ws, st);
   float *yn = reinterpret_cast<float *>(wsp(ws, w.yn));
   float *contrib = reap ? reinterpret_cast<float *>(wsp(ws, w.total)) : nullptr;
   if (launch_combine_norm(Y, pair_pos, topk_w, gamma, T, s->top_k, s->latent, s->rms_eps, yn, contrib, st) !=
@@ -351,6 +375,7 @@ static int combine_norm_up_impl(const moe_shape *s, int T, const float *Y, const
   if (run_dense(w.pu, afmt_of(s), false, a, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
+
 
 extern "C" {
 
@@ -807,10 +832,19 @@ int shared_expert_ffn(const moe_shape *s, int T, const uint16_t *x, const uint16
     float *partial = reinterpret_cast<float *>(wsp(ws, w.partial));
     GemmArgs g = dense_args(w.pgu, x, s->hidden, w_gate, w_up, NS, s->hidden, hs, NS, 0, T, partial,
                             s);
+    const int afmt = afmt_of(s);
+    // whole-K gate/up tiles write h straight into the bf16 planes the tiled
+    // down_proj reads (no fp32 h, no split pass)
+    const bool planes = w.pgu.variant == 4 && w.pgu.splits == 1 && w.pdn.variant == 4 && NS % 4 == 0;
+    if (planes) {
+      g.c_hi = reinterpret_cast<uint16_t *>(wsp(ws, w.planes));
+      g.c_lo = afmt == A_F32_SPLIT ? g.c_hi + (size_t)T * NS : nullptr;
+    }
     if (run_dense(w.pgu, A_BF16, true, g, nullptr, st) != hipSuccess) return MOE_EHIP;
-    GemmArgs d = dense_args(w.pdn, hs, NS, w_down, nullptr, s->hidden, NS, out, s->hidden,
-                            accumulate, T, partial, s);
-    if (run_dense(w.pdn, afmt_of(s), false, d, wsp(ws, w.planes), st) != hipSuccess) return MOE_EHIP;
+    GemmArgs d = dense_args(w.pdn, planes ? static_cast<const void *>(g.c_hi) : hs, NS, w_down, nullptr, s->hidden,
+                            NS, out, s->hidden, accumulate, T, partial, s);
+    if (planes) d.A2 = g.c_lo;
+    if (run_dense(w.pdn, afmt, false, d, wsp(ws, w.planes), st, planes) != hipSuccess) return MOE_EHIP;
     return MOE_OK;
   });
 }

@@ -300,6 +300,21 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[a][b][4 * q + r], acc[a + 2][b][4 * q + r], g.beta, g.beta_lin);
+          if (g.c_hi != nullptr) {
+            // bf16 planes for the next GEMM's operands (whole K, no accumulate: host-checked)
+            const long long o = (long long)t * ldc + col;
+            bf16x4_t h, l;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              __bf16 vh, vl;
+              split_bf16(v[r], vh, vl);
+              h[r] = vh;
+              l[r] = vl;
+            }
+            *reinterpret_cast<bf16x4_t *>(g.c_hi + o) = h;
+            if (g.c_lo != nullptr) *reinterpret_cast<bf16x4_t *>(g.c_lo + o) = l;
+            continue;
+          }
           if (acc_in) v += *reinterpret_cast<const f32x4_t *>(crow + col);
           *reinterpret_cast<f32x4_t *>(crow + col) = v;
         }

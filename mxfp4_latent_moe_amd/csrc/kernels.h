@@ -27,6 +27,10 @@ struct GemmArgs {
   const uint16_t *B0, *B1; // bf16 biases [E][N][K/64] (W_AFF2)
   const float *asum;      // W_AFF2 on the plane kernel: 64-element group sums of A's rows [rows][K/64]
   int asum_sorted;        // asum rows follow the sorted rows (a_map not applied to them)
+  // dense tiled kernel, SiTU pairs with whole K: the result as bf16 planes
+  // c_hi = bf16(v), c_lo = bf16(v - c_hi) ([rows][ldc] each; c_lo NULL: the
+  // rounded plane only) instead of fp32 C
+  uint16_t *c_hi, *c_lo;
   long long w_estride;    // per-expert stride of W (elements for bf16, bytes for packed)
   long long s_estride;    // per-expert stride of S in bytes
   int N, K;
@@ -165,6 +169,11 @@ hipError_t launch_reap(const float *Y, int P, int L, const float *pair_weight, c
 hipError_t launch_combine_norm(const float *Y, const int32_t *pair_pos, const float *w,
                                const uint16_t *gamma, int T, int k, int L, float eps, float *yn,
                                float *contrib, hipStream_t st);
+// the combine writing y_n as bf16 planes hi = bf16(y_n), lo = bf16(y_n - hi) ([T][L] each; lo NULL:
+// the rounded plane only), for L <= 4096
+hipError_t launch_combine_norm_planes(const float *Y, const int32_t *pair_pos, const float *w,
+                                      const uint16_t *gamma, int T, int k, int L, float eps, uint16_t *hi,
+                                      uint16_t *lo, hipStream_t st);
 // the per-expert pass of launch_reap alone, over contributions already made
 hipError_t launch_reap_experts(const float *contrib, const int32_t *offsets, int E, double *sal_sum,
                                long long *counts, int accumulate, hipStream_t st);
