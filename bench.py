@@ -466,11 +466,12 @@ def run_reap(mx, torch, synth):
                                    "reap_extra_ms": round(fused_ms - plain_ms, 4)}}
 
 
-PEAK_OF_MODE = {"bf16x2": ("bf16", BF16_MFMA_PEAK_TFLOPS), "mx8x3": ("fp8", FP8_MFMA_PEAK_TFLOPS),
+PEAK_OF_MODE = {"bf16x2": ("bf16", BF16_MFMA_PEAK_TFLOPS), "bf16": ("bf16", BF16_MFMA_PEAK_TFLOPS),
+                "mx8x3": ("fp8", FP8_MFMA_PEAK_TFLOPS),
                 "mx6x3": ("fp6/fp4", FP4_MFMA_PEAK_TFLOPS)}
 # MFMA products executed per algorithmic product in each operand mode's expert
 # GEMMs (gate/up with z, down with H): hi + lo planes, or three MX terms
-EXEC_PER_ALG = {"bf16x2": 2, "mx8x3": 3, "mx6x3": 3}
+EXEC_PER_ALG = {"bf16x2": 2, "bf16": 1, "mx8x3": 3, "mx6x3": 3}
 
 
 def _layer_flops(sh, T):
@@ -655,7 +656,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
-    ap.add_argument("--operand-mode", default="bf16x2", choices=["bf16x2", "mx8x3", "mx6x3"],
+    ap.add_argument("--operand-mode", default="bf16x2", choices=["bf16x2", "bf16", "mx8x3", "mx6x3"],
                     help="operand mode of the timed workload (the decode line's prefill extras cover all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -696,7 +697,7 @@ def main():
     layers = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(max(1, args.layers) - 1)]
     torch.cuda.synchronize()
     print("bench: timing", wl.name, file=sys.stderr, flush=True)
-    opnd = {"bf16x2": mx.MOE_OPND_BF16X2, "mx8x3": mx.MOE_OPND_MX8X3, "mx6x3": mx.MOE_OPND_MX6X3}[args.operand_mode]
+    opnd = {"bf16x2": mx.MOE_OPND_BF16X2, "bf16": mx.MOE_OPND_BF16, "mx8x3": mx.MOE_OPND_MX8X3, "mx6x3": mx.MOE_OPND_MX6X3}[args.operand_mode]
     r = run_workload(mx, torch, synth, layers, wl, args.steps, args.warmup, args.cold_steps, operand_mode=opnd)
     ms = 1e3 * r["wall_s"] / args.steps
     value = wl.tokens * args.steps / r["wall_s"]
@@ -740,6 +741,7 @@ def main():
             "tokens": wl.tokens,
             "operands": "MXFP4 expert weights (checkpoint bytes), bf16 dense weights, "
                         + {"bf16x2": "bf16 hi+lo split activations",
+                           "bf16": "activations rounded once to bf16",
                            "mx8x3": "expert GEMM activations as three e4m3 terms, other activations bf16 hi+lo",
                            "mx6x3": "expert GEMM activations as three e2m3 terms, other activations bf16 hi+lo"}[
                             args.operand_mode] + ", fp32 accumulate, fp32 output",

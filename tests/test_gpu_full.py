@@ -83,7 +83,7 @@ def _oracle_for(k3, wl, bias, sample):
     return _ORACLE[key]
 
 
-def _full_check(mx, k3, wl, bias, tag, operand_mode=0, inter_tol=1e-4):
+def _full_check(mx, k3, wl, bias, tag, operand_mode=0, inter_tol=1e-4, tol=TOL):
     say(f"case: {tag} (T={wl.tokens}) full layer on GPU")
     g = _run_layer(mx, k3, wl, None if wl.bias_mode == "normal" else bias, operand_mode)
     x_bits = synth.gen_tokens(wl)
@@ -108,7 +108,7 @@ def _full_check(mx, k3, wl, bias, tag, operand_mode=0, inter_tol=1e-4):
     ex = r["perm"]["counts"]
     say(f"{tag}: max|gpu-oracle|/rms over {int(keep.sum())} tokens ({int((ex > 0).sum())} experts) = {err:.3e} "
         f"(excluded near-ties: {excl.size})")
-    assert err <= TOL
+    assert err <= tol
     # every pair of the compared tokens: H and Y rows at the GPU's sorted positions
     k = wl.shape.top_k
     pp = g["pair_pos"].reshape(-1, k)[sample[keep]].reshape(-1)
@@ -170,6 +170,25 @@ def test_prefill_T4096(mx, k3):
     wl = synth.workload("prefill")
     bias = synth.gen_bias(wl)
     _full_check(mx, k3, wl, bias, "prefill")
+
+
+def test_prefill_T4096_bf16(mx, k3):
+    """Prefill with z and H each rounded once to bf16 (one bf16 MFMA per product).
+
+    This mode is outside the layer tolerance at full shapes: the one rounded z
+    feeds all sixteen experts of a token, so its error does not average out
+    over them (on the CPU, rounding z alone gives 8e-3 of the output rms on
+    four tokens, z, H, y_n and the shared h together 1.1e-2).  The test holds
+    the mode to what the rounding gives, which is why the hi + lo split is the
+    default."""
+    from mxfp4_latent_moe_amd import _lib
+    wl = synth.workload("prefill")
+    bias = synth.gen_bias(wl)
+    # pre-activations carry about 2^-9 / sqrt(3) of their rms as rounding
+    # noise; SiTU-GLU's steep parts lift single H and Y elements to a few
+    # percent of the rms
+    err = _full_check(mx, k3, wl, bias, "prefill bf16", _lib.MOE_OPND_BF16, inter_tol=8e-2, tol=3e-2)
+    assert err <= 3e-2
 
 
 def test_prefill_T4096_mx8x3(mx, k3):
