@@ -60,6 +60,26 @@ MOE_DEV void lds_wait16(u32x4_t &v) {
 
 constexpr int pl_gcd(int a, int b) { return b == 0 ? a : pl_gcd(b, a % b); }
 
+// Weights issued in pairs of K steps: every even step issues the codes of
+// steps s + L and s + L + 1 (the two halves of each row's 128-byte line,
+// back to back) and their scales, odd steps no weights.  Memory operations
+// a wave issues in step i: kq LDS loads, plus wp weight operations when i is
+// even.  After step s (of parity sp), LDS stage s + 1 (issued first in step
+// s + 2 - S) and weight step s + 1 (issued last in the even step e whose pair
+// holds s + 1) must have landed; returns how many operations issued after the
+// later of the two may stay in flight.
+constexpr int pl_pair_ops(int i, int kq, int wp) { return kq + ((i & 1) == 0 ? wp : 0); }
+constexpr int pl_pair_vm_left(int sp, int S, int L, int kq, int wp) {
+  const int s = 64 + sp;  // any step of this parity far from the start
+  const int e = ((s + 1 - L) & 1) == 0 ? s + 1 - L : s - L;
+  int left_w = 0;
+  for (int i = e + 1; i <= s; ++i) left_w += pl_pair_ops(i, kq, wp);
+  const int a = s + 2 - S;
+  int left_a = (a & 1) == 0 ? wp : 0;
+  for (int i = a + 1; i <= s; ++i) left_a += pl_pair_ops(i, kq, wp);
+  return left_w < left_a ? left_w : left_a;
+}
+
 // Eight affine 2-bit codes (a 16-bit run, code i in bits 2i .. 2i+1) as
 // exact bf16 integers in element order: the codes are spread one per nibble
 // (the low two bits of nibble i), where code q reads as the e2m1 value q / 2,
@@ -73,8 +93,9 @@ MOE_DEV bf16x8_t aff2x8_ordered(uint32_t x) {
 }
 
 // WF: MXFP4 or affine 2-bit weights; RW weight-ring slots, S LDS stages, LDS
-// reads D fragments ahead
-template <int WF, bool PAIR, int NPL, int NTA, int MT, int NW, int RW, int S, int D>
+// reads D fragments ahead; PW = 2: MXFP4 weights issued in pairs of K steps
+// (pl_pair_vm_left), RW - 2 steps ahead of the even step of a pair
+template <int WF, bool PAIR, int NPL, int NTA, int MT, int NW, int RW, int S, int D, int PW>
 __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int expert, int row0, int nrows,
                                           int nb) {
   constexpr bool AFF = WF == W_AFF2;
@@ -88,6 +109,8 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
   constexpr int KQ = (QI + NW - 1) / NW;  // per wave (the last round may leave waves idle)
   static_assert(pl_stage_bytes(NPL, NTA) == QI * 1024, "whole wave loads");
   static_assert(RW >= 2 && RW <= 8 && S >= 2 && S <= 4, "ring shapes");
+  static_assert(PW == 1 || (PW == 2 && !AFF && RW % 2 == 0 && RW >= 4), "paired weights: MXFP4, even ring");
+  constexpr int L = RW - 2;  // paired weights: the even step s issues steps s + L, s + L + 1
   // stage b of the LDS ring
   auto stage = [&](int b) { return lds + b * pl_stage_bytes(NPL, NTA); };
   constexpr int U = RW * S / pl_gcd(RW, S);  // steps per unrolled round: slot and stage repeat
@@ -152,6 +175,31 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
   constexpr int KQ_MIN = QI / NW;
   constexpr int WI = (AFF ? 3 : 2) * NTILE;
   constexpr uint32_t STEP_BYTES = AFF ? 32u : 64u;
+  // paired weights: an even step's operations are [KQ LDS loads][codes of
+  // step sw0 into slot wb0][codes of step sw1 into slot wb1][the two steps'
+  // scale dwords, one 8-byte load per tile]; an odd step's the LDS loads
+  constexpr int NOPS_E = KQ + 3 * NTILE, NOPS_O = KQ;
+  auto issue_pair_op = [&](int o, int sb, int wb0, int wb1, int sa, int sw0, int sw1) {
+    if (o < KQ) {
+      const int ii = wave + NW * o;  // uniform
+      if (ii < QI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(stage(sb) + ii * 1024), 16, qoff[o],
+                                                 (uint32_t)sa * 256u, 0, 0);
+    } else if (o < KQ + NTILE) {
+      const int t = o - KQ;
+      if constexpr (!AFF) wq[wb0][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)sw0 * STEP_BYTES);
+    } else if (o < KQ + 2 * NTILE) {
+      const int t = o - KQ - NTILE;
+      if constexpr (!AFF) wq[wb1][t] = buf_load16(wr[t / MT], woff[t], (uint32_t)sw1 * STEP_BYTES);
+    } else {
+      // scales of steps sw0 and sw0 + 1 (past the row's last step the second
+      // dword belongs to no computed step)
+      const int t = o - KQ - 2 * NTILE;
+      const u32x2_t v = buf_load8(sr[t / MT], scale_row(t), (uint32_t)sw0 * 4u);
+      wsc[wb0][t] = v[0];
+      wsc[wb1][t] = v[1];
+    }
+  };
   auto issue_op = [&](int o, int sb, int wb, int sa, int sw) {
     if (o < KQ) {
       const int ii = wave + NW * o;  // uniform
@@ -199,11 +247,21 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
     constexpr int SB = decltype(sbc)::value, WB = decltype(wbc)::value;
     constexpr int WN = (WB + RW - 1) % RW, SN = (SB + S - 1) % S;
     const int sa = min(s + S - 1, nks - 1), sw = min(s + RW - 1, nks - 1);
+    // paired weights (WB = s mod RW, RW even, so WB has the parity of s)
+    constexpr bool EVEN = (WB & 1) == 0;
+    constexpr int WP0 = (WB + L) % RW, WP1 = (WB + L + 1) % RW;
+    const int sw0 = min(s + L, nks - 1), sw1 = min(s + L + 1, nks - 1);
+    constexpr int NOPS_S = PW == 1 ? NOPS : EVEN ? NOPS_E : NOPS_O;
     constexpr int FJ = NPL * NTA;  // fragments per sub-step
     constexpr int F = 4 * FJ;
-    constexpr int J = (NOPS + F / 2 - 1) / (F / 2);  // loads issued per fragment
+    constexpr int J = (NOPS_S + F / 2 - 1) / (F / 2);  // loads issued per fragment
     u32x4_t bq[D + 1];
-    bf16x8_t wa[2][NTILE];
+    // converted weights: sub-step j + 1 is converted over sub-step j's
+    // fragments into the other buffer; items of five or six token tiles with
+    // paired weights (whose ring takes the registers) convert each sub-step's
+    // tiles at its start into one buffer
+    constexpr int WAB = (PW == 2 && NTA >= 5) ? 1 : 2;
+    bf16x8_t wa[WAB][NTILE];
     // MXFP4: the scale of the lane's scale group; affine: the two groups'
     // scales of the lane's four output rows 4 kg + r (from the lanes that
     // loaded those rows), with a temporary sum per group
@@ -239,17 +297,21 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
       constexpr int f = decltype(fc)::value;
       constexpr int j = f / FJ, i = f % FJ, n = f % NTA;
       if constexpr (f + D < F) issue(std::integral_constant<int, f + D>{});
-      if constexpr (j + 1 < 4) {
+      if constexpr (WAB == 2 && j + 1 < 4) {
         // tiles [i NTILE / FJ, (i + 1) NTILE / FJ) of sub-step j + 1
 #pragma unroll
         for (int t = (i * NTILE) / FJ; t < ((i + 1) * NTILE) / FJ; ++t) wa[(j + 1) & 1][t] = convert(j + 1, t);
+      }
+      if constexpr (WAB == 1 && i == 0 && j > 0) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) wa[0][t] = convert(j, t);
       }
       constexpr int behind = (f + D < F) ? D : F - 1 - f;  // reads issued after f
       lds_wait16<behind>(bq[f % (D + 1)]);
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bq[f % (D + 1)]);
       if constexpr (AFF) {
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) tmp[t][n] = mfma_16x16x32(wa[j & 1][t], bv, tmp[t][n]);
+        for (int t = 0; t < NTILE; ++t) tmp[t][n] = mfma_16x16x32(wa[(j & 1) % WAB][t], bv, tmp[t][n]);
         if constexpr ((f + 1) % (2 * FJ) == 0) {
           // group h of the step is complete: add it times its scales
           constexpr int h = f / (2 * FJ);
@@ -266,10 +328,13 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[j & 1][t], bv, acc[t][n]);
+        for (int t = 0; t < NTILE; ++t) acc[t][n] = mfma_16x16x32(wa[(j & 1) % WAB][t], bv, acc[t][n]);
       }
 #pragma unroll
-      for (int o = f * J; o < (f + 1) * J && o < NOPS; ++o) issue_op(o, SN, WN, sa, sw);
+      for (int o = f * J; o < (f + 1) * J && o < NOPS_S; ++o) {
+        if constexpr (PW == 1) issue_op(o, SN, WN, sa, sw);
+        else issue_pair_op(o, SN, WP0, WP1, sa, sw0, sw1);
+      }
     });
   };
   // After step s, stage s + 1 must be in LDS for every wave and weight step
@@ -279,28 +344,43 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
   constexpr int PER_STEP = KQ_MIN + WI;
   constexpr int AFTER_A = WI + (S - 2) * PER_STEP, AFTER_W = (RW - 2) * PER_STEP;
   constexpr int VM_LEFT = AFTER_A < AFTER_W ? AFTER_A : AFTER_W;
-  static_assert(VM_LEFT < 64, "vmcnt range");
-  auto wait_and_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_LEFT));
+  // paired weights: by the parity of the step just computed
+  constexpr int VM_LEFT_E = pl_pair_vm_left(0, S, L, KQ_MIN, 3 * NTILE);
+  constexpr int VM_LEFT_O = pl_pair_vm_left(1, S, L, KQ_MIN, 3 * NTILE);
+  static_assert(VM_LEFT < 64 && VM_LEFT_E < 64 && VM_LEFT_O < 64, "vmcnt range");
+  auto wait_and_sync = [&](auto oddc) {
+    constexpr int V = PW == 1 ? VM_LEFT : decltype(oddc)::value ? VM_LEFT_O : VM_LEFT_E;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);  // keep the next step's register work behind the wait
   };
+  static_assert(PW == 1 || U % 2 == 0, "paired weights: rounds of whole pairs");
   auto step = [&](auto ic, int s) {
     constexpr int I = decltype(ic)::value;
     compute(std::integral_constant<int, I % S>{}, std::integral_constant<int, I % RW>{}, s);
-    wait_and_sync();
+    wait_and_sync(std::integral_constant<bool, (I & 1) == 1>{});
   };
 
   // prologue: the loads of steps -M .. -1, in the same pattern as every step
-  constexpr int M = (RW > S ? RW : S) - 1;
+  // (paired weights: M covers the pairs of steps 0 .. L - 1 and no earlier pair)
+  constexpr int M = PW == 1 ? (RW > S ? RW : S) - 1 : (L > S - 1 ? L : S - 1);
+  static_assert(PW == 1 || M < L + 2, "no pair before step 0");
   static_for<M>([&](auto ic) {
     constexpr int r = decltype(ic)::value - M;  // -M .. -1
     constexpr int SN = ((r + S - 1) % S + S) % S, WN = ((r + RW - 1) % RW + RW) % RW;
     const int sa = max(min(r + S - 1, nks - 1), 0), sw = max(min(r + RW - 1, nks - 1), 0);
+    if constexpr (PW == 1) {
 #pragma unroll
-    for (int o = 0; o < NOPS; ++o) issue_op(o, SN, WN, sa, sw);
+      for (int o = 0; o < NOPS; ++o) issue_op(o, SN, WN, sa, sw);
+    } else {
+      constexpr bool EVEN = (r & 1) == 0;
+      constexpr int WP0 = ((r + L) % RW + RW) % RW, WP1 = ((r + L + 1) % RW + RW) % RW;
+      const int sw0 = max(min(r + L, nks - 1), 0), sw1 = max(min(r + L + 1, nks - 1), 0);
+#pragma unroll
+      for (int o = 0; o < (EVEN ? NOPS_E : NOPS_O); ++o) issue_pair_op(o, SN, WP0, WP1, sa, sw0, sw1);
+    }
   });
-  wait_and_sync();
+  wait_and_sync(std::true_type{});  // the virtual step -1 is odd
   int s = 0;
   for (; s + U - 1 < nks; s += U) static_for<U>([&](auto ic) { step(ic, s + decltype(ic)::value); });
   // tail: s is a multiple of U, so step i keeps stage i % S and slot i % RW
@@ -398,7 +478,17 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
 // and their activation stages (small, so four fit) three steps ahead too.
 // Larger items: three and three; affine weights (more registers per tile),
 // two and two.
-constexpr int pl_ring(int wf, int nta) { return nta <= 2 ? 4 : wf == W_AFF2 ? 2 : 3; }
+// MXFP4 weights are issued in pairs of K steps (both halves of each row's
+// 128-byte line back to back: one step apart, most second halves missed the
+// L2 and the weight lines crossed the memory bus about 1.75 times); their ring
+// holds the step pair computed and one pair in flight (two for items of one
+// or two token tiles, whose steps are short).  Items of six token
+// tiles keep single steps and a ring of three: the accumulators leave no
+// registers for a fourth slot.
+constexpr int pl_pw(int wf, int nta) { return wf == W_AFF2 || nta == 6 ? 1 : 2; }
+constexpr int pl_ring(int wf, int nta) {
+  return wf == W_AFF2 ? (nta <= 2 ? 4 : 2) : nta == 6 ? 3 : nta <= 2 ? 6 : 4;
+}
 constexpr int pl_stages(int wf, int nta) { return nta <= 2 ? 4 : wf == W_AFF2 ? 2 : 3; }
 // fragment reads ahead of their MFMAs (affine weights: one, for registers)
 constexpr int pl_d(int wf) { return wf == W_AFF2 ? 1 : 2; }
@@ -424,7 +514,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_pl_kernel(GemmArgs g) {
   const int4 c = reinterpret_cast<const int4 *>(g.chunks)[chunk];
   const int nta = min((c.z + 15) >> 4, NT);
 #define MOE_PL_ITEM(A) \
-  pfpl_item<WF, PAIR, NPL, A, MT, NW, pl_ring(WF, A), pl_stages(WF, A), pl_d(WF)>(g, lds, c.x, c.y, c.z, nb)
+  pfpl_item<WF, PAIR, NPL, A, MT, NW, pl_ring(WF, A), pl_stages(WF, A), pl_d(WF), pl_pw(WF, A)>(g, lds, c.x, c.y, c.z, nb)
   if (nta == NT) {
     MOE_PL_ITEM(NT);
     return;
