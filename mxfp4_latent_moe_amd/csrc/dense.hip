@@ -5,9 +5,12 @@
 //
 // Work item: 256 tokens x 256 weight rows (a pair: 128 gate rows and the 128
 // up rows of the same output columns), optionally one of `splits` K ranges.
-// Four waves, one per SIMD, each own 128 weight rows x 128 tokens as 4 x 4
+// Eight waves, two per SIMD, each own 128 weight rows x 64 tokens as 4 x 2
 // tiles of v_mfma_f32_32x32x16_bf16 (weights on the MFMA's M side, tokens
-// on its N side); the accumulators fill the 256 AGPRs.
+// on its N side; 128 accumulator registers).  With one wave per SIMD (4 x 4
+// tiles each) the MFMA pipe idled through every step's barrier and LDS waits;
+// the second wave of a SIMD fills them (the layer-0 FFN at T = 4096: 7.78 to
+// 7.20 ms).
 //
 // Both operands reach LDS through direct-to-LDS buffer loads in which eight
 // consecutive lanes fetch one 128-byte line, so every L1 request is a whole
@@ -27,7 +30,8 @@ namespace {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int DT = 256;  // tokens and weight rows per work-group
-constexpr int DNW = 4;   // waves
+constexpr int DNW = 8;   // waves: two halves of the weight rows x DNW / 2 slices of the tokens
+constexpr int DNB = DT / (DNW / 2) / 32;  // 32-token tiles per wave
 
 
 MOE_DEV f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -154,11 +158,12 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
     for (int k = 0; k < KL; ++k) load_one(stg, k, s);
   };
 
-  // ---- operand reads: wave (wm, wn) = (wave & 1, wave >> 1) owns tokens
-  // 128 wm .. +127 and weight rows 128 wn .. +127 of the tile (a pair: gate
-  // rows 64 wn .. +63 and the up rows 128 + 64 wn .. +63).  Lane l reads row
-  // l % 32 of each 32-row tile, chunk 2 j + l / 32 of MFMA step j.
-  const int wm = wave & 1, wn = wave >> 1;
+  // ---- operand reads: wave (wm, wn) = (wave % (DNW / 2), wave / (DNW / 2))
+  // owns tokens 32 DNB wm .. + 32 DNB - 1 and weight rows 128 wn .. +127 of
+  // the tile (a pair: gate rows 64 wn .. +63 and the up rows 128 + 64 wn ..
+  // +63).  Lane l reads row l % 32 of each 32-row tile, chunk 2 j + l / 32 of
+  // MFMA step j.
+  const int wm = wave % (DNW / 2), wn = wave / (DNW / 2);
   const int l32 = lane & 31, lh = lane >> 5;
   // per-lane offsets within a region of row l32 (+32 a for tile a), chunk 2 j + lh;
   // 32 rows are a whole number of 8-line swizzle periods, so the tile offset is a constant
@@ -174,17 +179,17 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
   const uint32_t ring_base = lds_addr(ring);
   // weight rows and token rows of the wave as region offsets
   const int wrow0 = wrow_tile(0);
-  const int tokrow0 = 128 * wm;
+  const int tokrow0 = 32 * DNB * wm;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][DNB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16_t{};
+    for (int b = 0; b < DNB; ++b) acc[a][b] = f32x16_t{};
 
-  constexpr int R = 4 + 4 * NPL;  // fragment reads per MFMA step
+  constexpr int R = 4 + DNB * NPL;  // fragment reads per MFMA step
   static_assert(J % 2 == 0, "fragment buffers alternate with the MFMA step");
-  u32x4_t fw[2][4], ft[2][NPL][4];
+  u32x4_t fw[2][4], ft[2][NPL][DNB];
   // reads of MFMA step j of the stage at `base` into fragment buffer j % 2
   auto issue = [&](uint32_t base, auto jc) {
     constexpr int j = decltype(jc)::value;
@@ -203,10 +208,10 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
     }
     static_for<NPL>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      dread<(1 + p) * REG>(at, ft[j & 1][p][0]);
-      dread<(1 + p) * REG + TILE_OFF>(at, ft[j & 1][p][1]);
-      dread<(1 + p) * REG + 2 * TILE_OFF>(at, ft[j & 1][p][2]);
-      dread<(1 + p) * REG + 3 * TILE_OFF>(at, ft[j & 1][p][3]);
+      static_for<DNB>([&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        dread<(1 + p) * REG + b * TILE_OFF>(at, ft[j & 1][p][b]);
+      });
     });
   };
   auto tie = [&](int q) {
@@ -215,7 +220,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
 #pragma unroll
     for (int p = 0; p < NPL; ++p)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) dtie(ft[q][p][b]);
+      for (int b = 0; b < DNB; ++b) dtie(ft[q][p][b]);
   };
   auto mfmas = [&](int q) {
 #pragma unroll
@@ -223,7 +228,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fw[q][a], ft[q][p][b], acc[a][b]);
+        for (int b = 0; b < DNB; ++b) acc[a][b] = mfma32(fw[q][a], ft[q][p][b], acc[a][b]);
   };
   auto slot_base = [&](int s) { return ring_base + (uint32_t)((s % NST) * STAGE); };
 
@@ -274,7 +279,7 @@ MOE_DEV void dense_tile_body(const GemmArgs &g, uint8_t *ring) {
   // 16-byte stores need every row to start 16-byte aligned
   const bool vec_ok = (ldc & 3) == 0;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < DNB; ++b) {
     const int t = t0 + tokrow0 + 32 * b + l32;
     if (t >= rows) continue;
     float *crow = C + (long long)t * ldc;
