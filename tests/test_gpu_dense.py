@@ -59,10 +59,11 @@ def test_shared_expert_ffn_tiled(mx, mode, tol):
     assert err <= tol
 
 
-@pytest.mark.parametrize("E,T", [(64, 1100), (62, 1100), (242, 1100), (62, 300), (242, 40)])
+@pytest.mark.parametrize("E,T", [(64, 1100), (62, 1100), (242, 1100), (62, 300), (62, 100), (242, 40)])
 def test_route_tiled(mx, E, T):
-    """Router logits + top-k and the latent projection z: at T = 1100 on the
-    tiled kernel, at T = 300 and 40 on the mid-size and streaming kernels.
+    """Router logits + top-k and the latent projection z: at T = 1100 and 300
+    on the tiled kernel (at 300 one ragged token tile, K split), at T = 100
+    and 40 on the mid-size and streaming kernels.
     Expert counts that are not a multiple of 4 leave a ragged group of logit
     columns at the end of every row."""
     from mxfp4_latent_moe_amd import _lib, ops
