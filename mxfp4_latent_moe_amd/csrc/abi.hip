@@ -567,7 +567,8 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
       GemmArgs as = a;
       as.chunks = chunks2;
       as.chunk_count = count2;
-      as.n_blocks = (N + grouped_stream_rows_per_wg(gateup) - 1) / grouped_stream_rows_per_wg(gateup);
+      as.n_blocks = (N + grouped_stream_rows_per_wg(gateup, PERSIST_ROWS_WIDE) - 1) /
+                    grouped_stream_rows_per_wg(gateup, PERSIST_ROWS_WIDE);
       as.splits = 1;
       as.grid_logical = s->n_experts * as.n_blocks;
       if (launch_grouped_stream(W_MXFP4, afmt, gateup, as, st, PERSIST_ROWS_WIDE) != hipSuccess) return MOE_EHIP;

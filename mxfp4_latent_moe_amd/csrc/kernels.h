@@ -107,7 +107,7 @@ GemmPlan plan_dense(int rows, int N, int K, bool pair);
 GemmPlan plan_grouped(int P, int E, int N, int K, bool pair);
 
 int stream_rows_per_wg(int wfmt, bool pair);
-int grouped_stream_rows_per_wg(bool pair);
+int grouped_stream_rows_per_wg(bool pair, int rows = PERSIST_ROWS);
 bool grouped_stream_fits(int K);
 // rows: chunk rows the kernel stages (PERSIST_ROWS, or PERSIST_ROWS_WIDE for MXFP4)
 hipError_t launch_grouped_stream(int wfmt, int afmt, bool pair, const GemmArgs &a, hipStream_t st,
