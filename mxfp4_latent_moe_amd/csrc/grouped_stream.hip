@@ -38,6 +38,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   constexpr int ROWS_WG = 16 * NW * MT;
   constexpr int NPL = (AF == A_F32_SPLIT) ? 2 : 1;
   constexpr int STEP = 16 * R * 8;  // bf16 elements per K step per plane: [octet][row][8]
+  constexpr bool FOLD = NPL == 2 && 2 * R <= 16;
   __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
 
   const int tid = threadIdx.x;
@@ -193,6 +194,18 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   };
 
   auto finish_item = [&]() {
+    // hi + lo per output: the lo column R lanes up (folded), or the second accumulator
+    f32x4_t af[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      af[t] = acc[t];
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) af[t][r] += __shfl_down(af[t][r], R, 64);
+      } else if constexpr (NPL == 2) {
+        af[t] += accl[t];
+      }
+    }
     const int tok = r16;
     if (tok < nrows) {
       const long long orow = row0 + tok;
@@ -200,14 +213,12 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int col0 = wrow_base + m * 16 + 4 * kg;
-        f32x4_t a = acc[m];
-        if constexpr (NPL == 2) a += accl[m];
+        const f32x4_t a = af[m];
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (PAIR) {
-            f32x4_t u = acc[m + MT];
-            if constexpr (NPL == 2) u += accl[m + MT];
+            const f32x4_t u = af[m + MT];
             v[r] = situ_glu(a[r], u[r], g.beta, g.beta_lin);
           } else {
             v[r] = a[r];
@@ -231,8 +242,13 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
   };
 
   // Lanes whose token column is >= R read row (r16 % R): those MFMA output
-  // columns are never stored.
+  // columns are never stored.  With two activation planes and at most eight
+  // rows, one MFMA takes both planes (FOLD): columns 0..R-1 read the rows' hi
+  // plane, R..2R-1 their lo plane, and the epilogue adds column r + R to
+  // column r, the same two fp32 sums added as with a second accumulator, at
+  // half the MFMAs and B reads.
   const int brow = r16 % R;
+  const __bf16 *const bsrc = &lds[FOLD ? (r16 / R) & 1 : 0][0];
   // one K step from group slot 0
   auto compute = [&](int d, int q) {
     float scl[NTILE];
@@ -244,15 +260,15 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = q * STEP + ((4 * kg + j) * R + brow) * 8;
-      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&bsrc[off]);
       bf16x8_t bl;
-      if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
+      if constexpr (NPL == 2 && !FOLD) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
       bf16x8_t wa[NTILE];
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) wa[t] = fp4x8_to_bf16(wq[0][d][t][j], scl[t]);
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) acc[t] = mfma_16x16x32(wa[t], bh, acc[t]);
-      if constexpr (NPL == 2) {
+      if constexpr (NPL == 2 && !FOLD) {
 #pragma unroll
         for (int t = 0; t < NTILE; ++t) accl[t] = mfma_16x16x32(wa[t], bl, accl[t]);
       }
