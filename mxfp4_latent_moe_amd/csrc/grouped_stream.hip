@@ -330,6 +330,9 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g)
   constexpr int STEP = 16 * R * 8;     // bf16 elements per K step per plane: [octet][row][8]
   constexpr int SUMS = 2 * 4 * R * 8;  // per-group activation sums: [slice][octet][row][8] (64 groups)
   constexpr uint32_t STEP_BYTES = 32;  // codes of one row per K step
+  // hi and lo planes in one MFMA (columns R..2R-1 take the lo plane), as in
+  // grouped_stream_kernel; the bias part folds the group sums' hi and lo alike
+  constexpr bool FOLD = NPL == 2 && 2 * R <= 16;
   __shared__ __attribute__((aligned(16))) __bf16 lds[NPL][KSMAX * STEP];
   __shared__ __attribute__((aligned(16))) __bf16 sums[2][SUMS];
 
@@ -523,18 +526,33 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g)
   // Lanes whose token column is >= R read row (r16 % R): those MFMA output
   // columns are never stored.
   const int brow = r16 % R;
+  const int bpl = FOLD ? (r16 / R) & 1 : 0;
+  const __bf16 *const bsrc = &lds[bpl][0];
   auto finish_item = [&]() {
     // the bias part: biases of the lane's row against the staged rows' group sums
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int off = ((i * 4 + kg) * R + brow) * 8;
-      const bf16x8_t sh = *reinterpret_cast<const bf16x8_t *>(&sums[0][off]);
-      const bf16x8_t sl = *reinterpret_cast<const bf16x8_t *>(&sums[1][off]);
+      const bf16x8_t sh = *reinterpret_cast<const bf16x8_t *>(&sums[bpl][off]);
+      bf16x8_t sl;
+      if constexpr (!FOLD) sl = *reinterpret_cast<const bf16x8_t *>(&sums[1][off]);
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) {
         const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, bq[c_item & 1][t][i]);
         acc[t] = mfma_16x16x32(bw, sh, acc[t]);
-        accl[t] = mfma_16x16x32(bw, sl, accl[t]);
+        if constexpr (!FOLD) accl[t] = mfma_16x16x32(bw, sl, accl[t]);
+      }
+    }
+    // hi + lo per output: the lo column R lanes up (folded), or the second accumulator
+    f32x4_t af[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      af[t] = acc[t];
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) af[t][r] += __shfl_down(af[t][r], R, 64);
+      } else {
+        af[t] += accl[t];
       }
     }
     const int tok = r16;
@@ -544,12 +562,12 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int col0 = wrow_base + m * 16 + 4 * kg;
-        const f32x4_t a = acc[m] + accl[m];
+        const f32x4_t a = af[m];
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (PAIR) {
-            const f32x4_t u = acc[m + MT] + accl[m + MT];
+            const f32x4_t u = af[m + MT];
             v[r] = situ_glu(a[r], u[r], g.beta, g.beta_lin);
           } else {
             v[r] = a[r];
@@ -598,14 +616,14 @@ __global__ __launch_bounds__(64 * NW) void grouped_stream_aff_kernel(GemmArgs g)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int off = q * STEP + (aff2_octet(h, kg, jj) * R + brow) * 8;
-        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&lds[0][off]);
+        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&bsrc[off]);
         bf16x8_t bl;
-        if constexpr (NPL == 2) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
+        if constexpr (NPL == 2 && !FOLD) bl = *reinterpret_cast<const bf16x8_t *>(&lds[1][off]);
 #pragma unroll
         for (int t = 0; t < NTILE; ++t) {
           const bf16x8_t wa = jj ? aff2x8_to_bf16<2>(ym[t], zm[t]) : aff2x8_to_bf16<0>(ym[t], zm[t]);
           tmp[t] = mfma_16x16x32(wa, bh, tmp[t]);
-          if constexpr (NPL == 2) tmp[t] = mfma_16x16x32(wa, bl, tmp[t]);
+          if constexpr (NPL == 2 && !FOLD) tmp[t] = mfma_16x16x32(wa, bl, tmp[t]);
         }
       }
 #pragma unroll
