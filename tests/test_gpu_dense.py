@@ -1,9 +1,11 @@
-"""Parity of the dense tiled path (prefill-sized token counts) through the C ABI.
+"""Parity of the dense products through the C ABI.
 
 A mid-size layer shape keeps the oracle fast while the dense products still
 take the tiled kernel: T = 1100 tokens are four whole 256-token tiles and a
 ragged one of 76, the weight tiles leave CUs idle so K is split (partial sums
 and the finalize pass), and two shared experts check the concatenated GLU.
+At decode-sized token counts (T <= 64) the same products run on the
+persistent streaming kernel, checked at T = 1, 17 and 64.
 """
 from __future__ import annotations
 
@@ -56,6 +58,33 @@ def test_shared_expert_ffn_tiled(mx, mode, tol):
     ref = layer.shared_experts(x_bits, d["sh_gate"], d["sh_up"], d["sh_down"], s.n_shared, s.shared_inter)
     err = rel_max_err(got, ref)
     say(f"shared_expert_ffn mode {mode}: max|gpu-oracle|/rms = {err:.3e}")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("mode,tol", [(0, 1e-4), (1, 1e-2)])
+@pytest.mark.parametrize("T", [1, 17, 64])
+def test_shared_expert_ffn_decode_sizes(mx, T, mode, tol):
+    """The same product at decode-sized token counts, where it runs on the
+    persistent streaming kernel: one token, a whole 16-row chunk plus a ragged
+    one-row chunk, and four whole chunks; the K splits go through the
+    finalize pass.  Both operand modes (h split hi + lo, or rounded)."""
+    from mxfp4_latent_moe_amd import _lib, ops
+    dev = torch.device("cuda:0")
+    s = MID_SHAPE
+    x_bits = synth.gen_tokens(MID, T)
+    d = synth.gen_dense(MID)
+    out0 = np.random.default_rng(6).standard_normal((T, s.hidden)).astype(np.float32)
+    say(f"case: shared_expert_ffn T={T} mode {mode} (decode sizes)")
+    sh = _shape(mx, mode)
+    ws = torch.empty(ops.workspace_bytes(sh, _lib.MOE_FN_SHARED_FFN, T), dtype=torch.uint8, device=dev)
+    out = to_dev(out0, dev)
+    ops.shared_ffn(sh, to_dev_bf16(x_bits, dev), to_dev_bf16(d["sh_gate"], dev), to_dev_bf16(d["sh_up"], dev),
+                   to_dev_bf16(d["sh_down"], dev), out, 1, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64) - out0
+    ref = layer.shared_experts(x_bits, d["sh_gate"], d["sh_up"], d["sh_down"], s.n_shared, s.shared_inter)
+    err = rel_max_err(got, ref)
+    say(f"shared_expert_ffn T={T} mode {mode}: max|gpu-oracle|/rms = {err:.3e}")
     assert err <= tol
 
 
