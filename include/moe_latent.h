@@ -67,10 +67,12 @@ extern "C" {
 /* mxfp4_grouped_gemm operations */
 #define MOE_OP_GATEUP_SITU 0
 #define MOE_OP_DOWN 1
+#define MOE_OP_GATEUP_SITU_BF16X2 2 /* gate/up + SiTU-GLU, H written as bf16 hi + lo planes */
 
 /* activation dtypes */
 #define MOE_DT_F32 0
 #define MOE_DT_BF16 1
+#define MOE_DT_BF16X2 2 /* bf16 planes: row r holds hi[0..K) then lo[0..K) */
 
 /* moe_workspace_bytes() function selectors */
 #define MOE_FN_ROUTE 0
@@ -223,13 +225,25 @@ int moe_permute(const moe_shape *shape, int T, const int32_t *topk_ids, int32_t 
  *                  precondition), which holds for a call over an expert slice
  *                  with the full token count T; a_rows * K * (4 for fp32, 2 for
  *                  bf16) must stay below 2^31.  Otherwise a_rows >= P.
- *   a_dtype        MOE_DT_F32 (split or rounded per shape->operand_mode) or
- *                  MOE_DT_BF16 (exact, single MFMA)
+ *   a_dtype        MOE_DT_F32 (split or rounded per shape->operand_mode),
+ *                  MOE_DT_BF16 (exact, single MFMA) or, for MOE_OP_DOWN,
+ *                  MOE_DT_BF16X2 (below)
+ *   op = MOE_OP_GATEUP_SITU_BF16X2: as MOE_OP_GATEUP_SITU, with C holding H as
+ *        bf16 planes instead of fp32: row p of C (uint16 bits, [P, 2 inter])
+ *        is hi[0..inter) then lo[0..inter), where hi = bf16(h) and
+ *        lo = bf16(h - hi) (round to nearest even) of the fp32 value h the
+ *        fp32 call stores, written straight from the epilogue.  A down call
+ *        with a_dtype MOE_DT_BF16X2 then reads them with no split pass: hi and
+ *        lo in operand mode MOE_OPND_BF16X2, hi alone in MOE_OPND_BF16, with
+ *        results bitwise those of the fp32 H call.  Both forms need the tiled
+ *        path with no small-expert split (P >= 8 E with these shapes) and
+ *        operand mode MOE_OPND_BF16X2 or MOE_OPND_BF16, else MOE_ENOTSUP.
  * Experts with no rows cost nothing and nothing waits on the host: the grid
  * is sized from P and each workgroup reads its work item on the device.
- * Errors: MOE_EINVAL for bad op/dtype, P < 1, a_rows < 1 (or below P when A
- * is not gathered), null required pointers, or w3 given for MOE_OP_DOWN;
- * MOE_ENOTSUP for a gathered A of 2^31 bytes or more. */
+ * Errors: MOE_EINVAL for bad op/dtype (MOE_DT_BF16X2 with a gate/up op), P < 1,
+ * a_rows < 1 (or below P when A is not gathered), null required pointers, or
+ * w3 given for MOE_OP_DOWN; MOE_ENOTSUP for a gathered A of 2^31 bytes or
+ * more, and for the bf16-plane forms outside their limits. */
 int mxfp4_grouped_gemm(const moe_shape *shape, int op, int P, const int32_t *expert_offsets,
                        const int32_t *sorted_pair, const void *A, int a_rows, int a_dtype,
                        const uint8_t *w_packed, const uint8_t *w_scale, const uint8_t *w3_packed,

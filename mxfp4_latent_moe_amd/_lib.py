@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(PKG, "lib", "libmoe_latent.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP, MOE_EINTERNAL = 0, -1, -2, -3, -4, -5
 MOE_OPND_BF16X2, MOE_OPND_BF16, MOE_OPND_MX8X3, MOE_OPND_MX6X3 = 0, 1, 2, 3
-MOE_OP_GATEUP_SITU, MOE_OP_DOWN = 0, 1
-MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_OP_GATEUP_SITU, MOE_OP_DOWN, MOE_OP_GATEUP_SITU_BF16X2 = 0, 1, 2
+MOE_DT_F32, MOE_DT_BF16, MOE_DT_BF16X2 = 0, 1, 2
 MOE_ROUTE_NOALLOC_SCRATCH_BYTES = 8 << 20
 (MOE_FN_ROUTE, MOE_FN_PERMUTE, MOE_FN_GROUPED_GEMM, MOE_FN_COMBINE_NORM_UP, MOE_FN_SHARED_FFN,
  MOE_FN_REAP_SALIENCY, MOE_FN_COMBINE_NORM_UP_REAP, MOE_FN_GROUPED_GEMM_TWO_BANK) = range(8)

@@ -477,10 +477,13 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
   return guarded([&]() -> int {
     int rc = check_shape(s);
     if (rc) return rc;
-    if (op != MOE_OP_GATEUP_SITU && op != MOE_OP_DOWN) return MOE_EINVAL;
-    if (a_dtype != MOE_DT_F32 && a_dtype != MOE_DT_BF16) return MOE_EINVAL;
+    if (op != MOE_OP_GATEUP_SITU && op != MOE_OP_DOWN && op != MOE_OP_GATEUP_SITU_BF16X2) return MOE_EINVAL;
+    if (a_dtype != MOE_DT_F32 && a_dtype != MOE_DT_BF16 && (a_dtype != MOE_DT_BF16X2 || op != MOE_OP_DOWN))
+      return MOE_EINVAL;
     if (P <= 0 || !expert_offsets || !A || !w_packed || !w_scale || !C || !ws) return MOE_EINVAL;
-    const bool gateup = op == MOE_OP_GATEUP_SITU;
+    const bool gateup = op != MOE_OP_DOWN;
+    // H as bf16 hi + lo planes: written by the gate/up epilogue, read by down
+    const bool planes_out = op == MOE_OP_GATEUP_SITU_BF16X2, planes_in = a_dtype == MOE_DT_BF16X2;
     // gate/up with sorted_pair gathers rows of A (z [T, L]); otherwise A holds the P sorted rows
     const bool gathered = gateup && sorted_pair != nullptr;
     if (a_rows < 1 || (!gathered && a_rows < P)) return MOE_EINVAL;
@@ -504,6 +507,10 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     const int N = gateup ? s->inter : s->latent;
     const int K = gateup ? s->latent : s->inter;
     const bool hybrid = hybrid_grouped(s, w.plan, P, K);
+    if ((planes_out || planes_in) && (w.plan.variant != 3 || hybrid ||
+                                      (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16)))
+      return MOE_ENOTSUP;
+    if (planes_in && (long long)a_rows * 2 * K * 2 >= (1LL << 31)) return MOE_ENOTSUP;
     // the tiled kernel's chunks: every expert, or in a split batch the experts above the streaming kernel's rows
     if (launch_plan_chunks(expert_offsets, s->n_experts, w.plan.chunk_rows, chunks, count, st,
                            hybrid ? PERSIST_ROWS_WIDE + 1 : 1) != hipSuccess)
@@ -525,6 +532,11 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
     a.C = C;
     a.ldc = N;
     a.accumulate = 0;
+    if (planes_out) {
+      a.c_hi = reinterpret_cast<uint16_t *>(C);
+      a.c_lo = a.c_hi + N;
+      a.ldc = 2 * N;
+    }
     a.rscale = pair_weight;
     a.rscale_map = pair_weight ? sorted_pair : nullptr;
     a.chunks = chunks;
@@ -578,7 +590,11 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
       // ones are split first (hi + lo, or rounded), over the same rows as the
       // MX split above
       int npl = 1;
-      if (a_dtype == MOE_DT_F32) {
+      if (planes_in) {
+        // the caller's planes: hi and lo (or hi alone for a rounded operand), rows of 2 K
+        npl = afmt == A_F32_SPLIT ? 2 : 1;
+        a.lda = 2LL * K;
+      } else if (a_dtype == MOE_DT_F32) {
         npl = afmt == A_F32_SPLIT ? 2 : 1;
         const bool split_gathers = gathered && a_rows > P;
         const long long rows = (gathered && !split_gathers) ? (long long)a_rows : (long long)P;

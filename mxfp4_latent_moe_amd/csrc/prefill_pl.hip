@@ -457,15 +457,39 @@ __device__ __forceinline__ void pfpl_item(const GemmArgs &g, uint8_t *lds, int e
           if constexpr (PAIR) v[r] = situ_glu(acc[m][n][r], acc[m + MT][n][r], g.beta, g.beta_lin) * rs;
           else v[r] = acc[m][n][r] * rs;
         }
-        float *cp = g.C + orow * g.ldc + col0;
-        if (col0 + 3 < N) {
-          f32x4_t o = f32x4_t{v[0], v[1], v[2], v[3]};
-          if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
-          *reinterpret_cast<f32x4_t *>(cp) = o;
-        } else {
+        if (g.c_hi != nullptr) {
+          // bf16 planes: hi = bf16(v), lo = bf16(v - hi), rows of ldc elements
+          bf16x4_t h, l;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (col0 + r < N) cp[r] = g.accumulate ? cp[r] + v[r] : v[r];
+          for (int r = 0; r < 4; ++r) {
+            __bf16 hr, lr;
+            split_bf16(v[r], hr, lr);
+            h[r] = hr;
+            l[r] = lr;
+          }
+          const long long o = orow * g.ldc + col0;
+          if (col0 + 3 < N) {
+            *reinterpret_cast<bf16x4_t *>(g.c_hi + o) = h;
+            *reinterpret_cast<bf16x4_t *>(g.c_lo + o) = l;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (col0 + r < N) {
+                g.c_hi[o + r] = __builtin_bit_cast(uint16_t, h[r]);
+                g.c_lo[o + r] = __builtin_bit_cast(uint16_t, l[r]);
+              }
+          }
+        } else {
+          float *cp = g.C + orow * g.ldc + col0;
+          if (col0 + 3 < N) {
+            f32x4_t o = f32x4_t{v[0], v[1], v[2], v[3]};
+            if (g.accumulate) o += *reinterpret_cast<const f32x4_t *>(cp);
+            *reinterpret_cast<f32x4_t *>(cp) = o;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (col0 + r < N) cp[r] = g.accumulate ? cp[r] + v[r] : v[r];
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -7,9 +7,9 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (MOE_DT_BF16, MOE_DT_F32, MOE_FN_COMBINE_NORM_UP, MOE_FN_GROUPED_GEMM,
+from ._lib import (MOE_DT_BF16, MOE_DT_BF16X2, MOE_DT_F32, MOE_FN_COMBINE_NORM_UP, MOE_FN_GROUPED_GEMM,
                    MOE_FN_PERMUTE, MOE_FN_ROUTE, MOE_FN_SHARED_FFN, MOE_OP_DOWN,
-                   MOE_OP_GATEUP_SITU, MoeShape, check, load)
+                   MOE_OP_GATEUP_SITU, MOE_OP_GATEUP_SITU_BF16X2, MoeShape, check, load)
 
 
 def _p(t):
@@ -52,9 +52,11 @@ def permute(shape, topk_ids, offsets, sorted_pair, pair_pos, active, ws, stream=
 
 
 def grouped_gemm(shape, op, P, offsets, sorted_pair, A, w_packed, w_scale, w3_packed, w3_scale,
-                 pair_weight, C, ws, stream=None):
-    """mxfp4_grouped_gemm; a_rows is A's row count."""
-    a_dtype = MOE_DT_BF16 if A.dtype in (torch.bfloat16, torch.int16, torch.uint16) else MOE_DT_F32
+                 pair_weight, C, ws, stream=None, a_dtype=None):
+    """mxfp4_grouped_gemm; a_rows is A's row count.  a_dtype defaults to the
+    dtype of A (bf16 bits or fp32); MOE_DT_BF16X2 marks A as H planes."""
+    if a_dtype is None:
+        a_dtype = MOE_DT_BF16 if A.dtype in (torch.bfloat16, torch.int16, torch.uint16) else MOE_DT_F32
     check("mxfp4_grouped_gemm",
           load().mxfp4_grouped_gemm(shape, op, P, _p(offsets), _p(sorted_pair), _p(A), A.shape[0], a_dtype,
                                     _p(w_packed), _p(w_scale), _p(w3_packed), _p(w3_scale),
@@ -142,10 +144,17 @@ class LatentMoE:
     GEMMs instead (at decode sizes that puts the shared experts on the path to
     the expert GEMMs; at prefill sizes the two joins measure the same).
     overlap_shared=False runs everything on the caller's stream.
+
+    h_planes: where the expert GEMMs take the tiled path (T k >= 8 E, single
+    bank, operand mode BF16X2 or BF16) the gate/up call writes H as bf16
+    hi + lo planes (buffer "H", int16 bits [T k, 2 I]) and the down call
+    reads them, with no split pass in between; Y and the output are bitwise
+    those of the fp32 H.  h_planes=False keeps H in fp32 always.
     """
 
     def __init__(self, shape: MoeShape, weights: dict, device="cuda", overlap_shared: bool = True,
-                 latent_on_side: bool = True, late_shared_join: bool = True, bank_b: dict | None = None):
+                 latent_on_side: bool = True, late_shared_join: bool = True, bank_b: dict | None = None,
+                 h_planes: bool = True):
         missing = [k for k in WEIGHT_KEYS if k not in weights]
         if missing:
             raise ValueError(f"missing weights: {missing}")
@@ -175,6 +184,13 @@ class LatentMoE:
         self.late_shared_join = late_shared_join and overlap_shared
         # default-priority side stream for the shared experts
         self.side = torch.cuda.Stream(device=self.device) if overlap_shared else None
+        self.h_planes = h_planes
+
+    def planes_for(self, T: int) -> bool:
+        """Whether H travels as bf16 planes at T tokens (see h_planes)."""
+        s = self.shape
+        return (self.h_planes and self.bank_b is None and s.operand_mode in (_lib.MOE_OPND_BF16X2, _lib.MOE_OPND_BF16)
+                and T * s.top_k >= 8 * s.n_experts)
 
     def buffers(self, T: int) -> dict:
         if T in self._bufs:
@@ -195,7 +211,8 @@ class LatentMoE:
             "sorted_pair": torch.empty((P,), dtype=i32, device=dev),
             "pair_pos": torch.empty((P,), dtype=i32, device=dev),
             "active": torch.empty((s.n_experts + 1,), dtype=i32, device=dev),
-            "H": torch.empty((P, s.inter), dtype=f32, device=dev),
+            "H": (torch.empty((P, 2 * s.inter), dtype=torch.int16, device=dev) if self.planes_for(T)
+                  else torch.empty((P, s.inter), dtype=f32, device=dev)),
             "Y": torch.empty((P, s.latent), dtype=f32, device=dev),
             "out": torch.empty((T, s.hidden), dtype=f32, device=dev),
             "ws": torch.empty((ws,), dtype=torch.uint8, device=dev),
@@ -275,13 +292,15 @@ class LatentMoE:
                  lambda: grouped_gemm_two_bank(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], da, db,
                                                None, b["Y"], ws, st))
         else:
+            planes = self.planes_for(T)
             call("grouped_gemm_gateup", st,
-                 lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU, P, b["offsets"], b["sorted_pair"], b["z"],
-                                      w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, b["H"],
-                                      ws, st))
+                 lambda: grouped_gemm(s, MOE_OP_GATEUP_SITU_BF16X2 if planes else MOE_OP_GATEUP_SITU, P,
+                                      b["offsets"], b["sorted_pair"], b["z"], w["w1_packed"], w["w1_scale"],
+                                      w["w3_packed"], w["w3_scale"], None, b["H"], ws, st))
             call("grouped_gemm_down", st,
                  lambda: grouped_gemm(s, MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], b["H"], w["w2_packed"],
-                                      w["w2_scale"], None, None, None, b["Y"], ws, st))
+                                      w["w2_scale"], None, None, None, b["Y"], ws, st,
+                                      a_dtype=MOE_DT_BF16X2 if planes else None))
         if shared and side is not st and late:
             st.wait_event(side_done)
         call("moe_combine_norm_up", st,

@@ -48,7 +48,20 @@ def _run_layer(mx, k3, wl, bias_np=None, operand_mode=0, **schedule):
     x = upload_tokens(wl, DEV)
     bufs = moe.forward(x)
     torch.cuda.synchronize()
-    return {k: v.cpu().numpy() for k, v in bufs.items() if k not in ("ws",)}
+    g = {k: v.cpu().numpy() for k, v in bufs.items() if k not in ("ws",)}
+    if moe.planes_for(wl.tokens):
+        # H as bf16 hi + lo planes: the value compared is hi + lo
+        g["H_planes"] = g["H"]
+        g["H"] = planes_to_f64(g["H"])
+    return g
+
+
+def planes_to_f64(h):
+    """[rows, 2 I] bf16 bits (hi then lo) -> hi + lo as float64 [rows, I]."""
+    bits = h.view(np.uint16)
+    inter = bits.shape[1] // 2
+    return (synth.bf16_bits_to_f32(bits[:, :inter]).astype(np.float64) +
+            synth.bf16_bits_to_f32(bits[:, inter:]).astype(np.float64))
 
 
 # oracle results per (workload, sampled tokens): the three prefill operand
@@ -112,10 +125,17 @@ def _full_check(mx, k3, wl, bias, tag, operand_mode=0, inter_tol=1e-4, tol=TOL):
     # every pair of the compared tokens: H and Y rows at the GPU's sorted positions
     k = wl.shape.top_k
     pp = g["pair_pos"].reshape(-1, k)[sample[keep]].reshape(-1)
-    errH = rel_max_err(g["H"][pp], r["H_pair"][keep].reshape(pp.size, -1))
+    h_ref = r["H_pair"][keep].reshape(pp.size, -1)
+    errH = rel_max_err(g["H"][pp], h_ref)
     errY = rel_max_err(g["Y"][pp], r["Y_pair"][keep].reshape(pp.size, -1))
-    say(f"{tag}: {pp.size} pairs, H {errH:.3e}, Y {errY:.3e}")
-    assert errH < inter_tol and errY < inter_tol
+    # H delivered as bf16 hi + lo planes carries up to 2^-16 |h| of its own
+    # (each of the two roundings to nearest even errs by at most 2^-8 of its
+    # argument), on top of the arithmetic's
+    tol_h = inter_tol
+    if "H_planes" in g:
+        tol_h += 2.0 ** -16 * float(np.abs(h_ref).max() / np.sqrt(np.mean(h_ref ** 2)))
+    say(f"{tag}: {pp.size} pairs, H {errH:.3e} (bound {tol_h:.3e}), Y {errY:.3e}")
+    assert errH < tol_h and errY < inter_tol
     # at prefill sizes the pairs cover every count of active token tiles that
     # the layer's chunks have, and a chunk past a segment's first
     if wl.tokens * k / wl.shape.n_experts >= 2:
@@ -264,7 +284,7 @@ def test_expert_slice_partition_invariance(mx, k3, wl_name, mode, n_slice):
     wl = synth.workload(wl_name)
     sh = wl.shape
     say(f"case: {wl_name} layer (operand mode {mode}), then expert slices of {n_slice}")
-    g = _run_layer(mx, k3, wl, operand_mode=mode)
+    g = _run_layer(mx, k3, wl, operand_mode=mode, h_planes=False)
     w = k3["w"]
     offsets = g["offsets"]
     z = to_dev(g["z"], DEV)
@@ -367,6 +387,51 @@ def test_graph_capture_replays_full_shape(mx, k3, wl_name):
     del graph
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_h_planes_bitwise(mx, k3, mode):
+    """Prefill T = 4096: the gate/up call writing H as bf16 hi + lo planes
+    gives exactly the split of the fp32 H call (hi = bf16(h), lo = bf16(h - hi),
+    round to nearest even), and the down call reading those planes gives the
+    fp32 H call's Y bit for bit, in both operand modes that take planes.  At
+    decode sizes (the persistent kernel) the plane forms are refused."""
+    from mxfp4_latent_moe_amd import _lib, ops
+    wl = synth.workload("prefill")
+    sh = wl.shape
+    say(f"case: H planes at prefill, operand mode {mode}")
+    moe = mx.LatentMoE(mx.shape_of(sh, mode), k3["w"], DEV, h_planes=False)
+    b = moe.forward(upload_tokens(wl, DEV))
+    torch.cuda.synchronize()
+    s = moe.shape
+    w = k3["w"]
+    P = wl.tokens * sh.top_k
+    ws = torch.empty(ops.workspace_bytes(s, ops.MOE_FN_GROUPED_GEMM, P), dtype=torch.uint8, device=DEV)
+    Hp = torch.empty((P, 2 * sh.inter), dtype=torch.int16, device=DEV)
+    Y = torch.empty_like(b["Y"])
+    ops.grouped_gemm(s, _lib.MOE_OP_GATEUP_SITU_BF16X2, P, b["offsets"], b["sorted_pair"], b["z"], w["w1_packed"],
+                     w["w1_scale"], w["w3_packed"], w["w3_scale"], None, Hp, ws)
+    ops.grouped_gemm(s, ops.MOE_OP_DOWN, P, b["offsets"], b["sorted_pair"], Hp, w["w2_packed"], w["w2_scale"],
+                     None, None, None, Y, ws, a_dtype=_lib.MOE_DT_BF16X2)
+    torch.cuda.synchronize()
+    hi = b["H"].to(torch.bfloat16)
+    lo = (b["H"] - hi.float()).to(torch.bfloat16)
+    assert torch.equal(Hp[:, :sh.inter], hi.view(torch.int16))
+    assert torch.equal(Hp[:, sh.inter:], lo.view(torch.int16))
+    assert torch.equal(Y, b["Y"])
+    del Hp, Y, ws, b, moe
+    # decode sizes: refused
+    dwl = synth.workload("decode")
+    dmoe = mx.LatentMoE(mx.shape_of(sh, mode), w, DEV)
+    db = dmoe.forward(upload_tokens(dwl, DEV))
+    torch.cuda.synchronize()
+    dP = dwl.tokens * sh.top_k
+    dws = torch.empty(ops.workspace_bytes(s, ops.MOE_FN_GROUPED_GEMM, dP), dtype=torch.uint8, device=DEV)
+    dHp = torch.empty((dP, 2 * sh.inter), dtype=torch.int16, device=DEV)
+    with pytest.raises(_lib.MoeError) as ei:
+        ops.grouped_gemm(s, _lib.MOE_OP_GATEUP_SITU_BF16X2, dP, db["offsets"], db["sorted_pair"], db["z"],
+                         w["w1_packed"], w["w1_scale"], w["w3_packed"], w["w3_scale"], None, dHp, dws)
+    assert ei.value.code == _lib.MOE_ENOTSUP
+
+
 def _pruned_weights(w, keep_np):
     """The layer's weights renumbered to the kept experts: new expert i is old
     expert keep[i]; router rows, bias and expert stacks reordered alike."""
@@ -414,7 +479,9 @@ def test_runtime_pruning_renumbered_subset(mx, k3, wl_name):
     k = sh.top_k
     pairs = (np.nonzero(same)[0][:, None] * k + np.arange(k)).reshape(-1)
     pf, pg = full["pair_pos"][pairs], g["pair_pos"][pairs]
-    assert np.array_equal(g["H"][pg], full["H"][pf]) and np.array_equal(g["Y"][pg], full["Y"][pf])
+    # H as the layer delivers it (bf16 planes at prefill sizes): the same bits
+    assert np.array_equal(g["H"][pg], full.get("H_planes", full["H"])[pf])
+    assert np.array_equal(g["Y"][pg], full["Y"][pf])
     if same.all():
         assert np.array_equal(g["sorted_pair"], full["sorted_pair"])
         assert np.array_equal(g["offsets"], full["offsets"][np.r_[keep, E]])

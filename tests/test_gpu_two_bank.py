@@ -48,7 +48,7 @@ def _routing(mx, wl, w, x):
     from mxfp4_latent_moe_amd import ops
     s = mx.shape_of(wl.shape)
     T = x.shape[0]
-    moe = mx.LatentMoE(s, w, DEV)
+    moe = mx.LatentMoE(s, w, DEV, h_planes=False)
     b = moe.forward(x)
     torch.cuda.synchronize()
     return s, b, T * wl.shape.top_k
@@ -100,7 +100,7 @@ def test_affine_bank_on_paired_values(mx, T):
     x = upload_tokens(wl, DEV)
     s = mx.shape_of(MID)
     say(f"case: affine bank B on paired values, T={T}")
-    single = {k: v.clone() for k, v in mx.LatentMoE(s, w, DEV).forward(x).items()}
+    single = {k: v.clone() for k, v in mx.LatentMoE(s, w, DEV, h_planes=False).forward(x).items()}
     two = mx.LatentMoE(s, {k: (v[:N_A] if k[:2] in ("w1", "w3", "w2") else v) for k, v in w.items()}, DEV,
                        bank_b=bank_b).forward(x)
     torch.cuda.synchronize()
