@@ -499,18 +499,18 @@ int mxfp4_grouped_gemm(const moe_shape *s, int op, int P, const int32_t *expert_
         (w3_scale && (reinterpret_cast<uintptr_t>(w3_scale) & 3u)))
       return MOE_EINVAL;
     const GroupedWs w = grouped_ws(s, P, gateup);
+    const int N = gateup ? s->inter : s->latent;
+    const int K = gateup ? s->latent : s->inter;
+    const bool hybrid = hybrid_grouped(s, w.plan, P, K);
+    // the bf16-plane forms: the tiled path with no small-expert split, bf16 operand modes
+    if ((planes_out || planes_in) && (w.plan.variant != 3 || hybrid ||
+                                      (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16)))
+      return MOE_ENOTSUP;
     if (ws_bytes < w.total) return MOE_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t *chunks = reinterpret_cast<int32_t *>(wsp(ws, w.chunks));
     int32_t *count = reinterpret_cast<int32_t *>(wsp(ws, w.count));
-    const int N = gateup ? s->inter : s->latent;
-    const int K = gateup ? s->latent : s->inter;
-    const bool hybrid = hybrid_grouped(s, w.plan, P, K);
-    if ((planes_out || planes_in) && (w.plan.variant != 3 || hybrid ||
-                                      (s->operand_mode != MOE_OPND_BF16X2 && s->operand_mode != MOE_OPND_BF16)))
-      return MOE_ENOTSUP;
-    if (planes_in && (long long)a_rows * 2 * K * 2 >= (1LL << 31)) return MOE_ENOTSUP;
     // the tiled kernel's chunks: every expert, or in a split batch the experts above the streaming kernel's rows
     if (launch_plan_chunks(expert_offsets, s->n_experts, w.plan.chunk_rows, chunks, count, st,
                            hybrid ? PERSIST_ROWS_WIDE + 1 : 1) != hipSuccess)

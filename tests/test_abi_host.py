@@ -148,6 +148,18 @@ def test_grouped_gemm_validation(lib):
     big = -(-(1 << 31) // (lat * 4))  # smallest row count with 2^31 bytes or more
     assert call(ar=big) == _lib.MOE_ENOTSUP
     assert call(ar=big - 1, wsb=ws - 1) == _lib.MOE_EWORKSPACE
+    # H as bf16 planes: planes input only for down; both forms only on the
+    # tiled path without the small-expert split (P >= 8 E) in bf16 operand modes
+    GP, BP = _lib.MOE_OP_GATEUP_SITU_BF16X2, _lib.MOE_DT_BF16X2
+    assert call(dt=BP) == _lib.MOE_EINVAL
+    assert call(op=GP) == _lib.MOE_ENOTSUP                                   # P = 256: decode sizes
+    assert call(op=D, w3p=None, w3s=None, ar=P, dt=BP) == _lib.MOE_ENOTSUP
+    Pb = 8 * s.n_experts
+    wsb_big = lib.moe_workspace_bytes(s, _lib.MOE_FN_GROUPED_GEMM, Pb)
+    assert call(op=GP, P_=Pb, wsb=wsb_big - 1) == _lib.MOE_EWORKSPACE      # accepted up to the workspace check
+    mx6 = _shape(operand_mode=_lib.MOE_OPND_MX6X3)
+    assert lib.mxfp4_grouped_gemm(mx6, GP, Pb, FAKE, FAKE, FAKE, Pb // 16, f32, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  FAKE, wsb_big, None) == _lib.MOE_ENOTSUP
 
 
 def test_combine_and_shared_validation(lib):
