@@ -1,6 +1,10 @@
-// Streaming variant of the weight-stationary GEMM for chunks of at most 16
+// Streaming variants of the weight-stationary GEMM for chunks of at most 16
 // token rows (decode-sized work): the weights are the whole cost, so the
-// kernel is built to keep many weight bytes in flight.
+// kernels are built to keep many weight bytes in flight.
+//
+// stream_gemm_kernel (one item per work-group) serves the grouped MXFP4
+// products the persistent kernel does not take; the dense bf16 products run
+// on stream_persist_kernel below (the one-item kernel remains their fallback).
 //
 //  * A workgroup's token rows (R rows per chunk) for its K slice sit in LDS
 //    for the whole main loop: one barrier per workgroup, none per K step.
