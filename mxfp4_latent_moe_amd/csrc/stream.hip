@@ -553,8 +553,12 @@ constexpr int SP_WAVES = 4;
 
 template <int AF, bool PAIR>
 hipError_t launch_persist(const GemmArgs &a, hipStream_t st) {
-  // every split must own at least one K step (the kernel walks each item's steps)
-  if (a.K % KSTEP || a.splits < 1 || a.splits > a.K / KSTEP || a.n_blocks < 1) return hipErrorInvalidValue;
+  // every split owns at least one K step (the kernel walks each item's steps)
+  // and at most the STREAM_KSMAX steps of the slice the kernel stages
+  const int ksteps = a.K / KSTEP;
+  if (a.K % KSTEP || a.splits < 1 || a.splits > ksteps || (ksteps + a.splits - 1) / a.splits > STREAM_KSMAX ||
+      a.n_blocks < 1)
+    return hipErrorInvalidValue;
   void *fn = reinterpret_cast<void *>(&stream_persist_kernel<AF, PAIR, SP_AHEAD, SP_WAVES>);
   // one resident wave of work-groups (occupancy queried once per kernel and device)
   static std::atomic<int> cache[64];
